@@ -1,0 +1,127 @@
+"""CPU oracle for the prefix-scan primitives -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never does, and this
+package never imports the HIP library: the two share no code.
+
+Each function wraps one plain sequential C routine of ``oracle.c`` (see that
+file for the passage of the pages it follows) and works on numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def load():
+    """Load liboracle.so, compiling it with gcc first if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_scan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_int]
+    lib.oracle_scan_u32.restype = ctypes.c_uint32
+    lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
+    lib.oracle_scan_blocked_u32.restype = ctypes.c_int
+    lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
+    lib.oracle_segscan_u32.restype = ctypes.c_uint64
+    lib.oracle_compact_flags.argtypes = [i32p, i32p, ctypes.c_uint64]
+    lib.oracle_compact_flags.restype = ctypes.c_uint64
+    lib.oracle_stable_argsort_u32.argtypes = [u32p, i32p, ctypes.c_uint64]
+    lib.oracle_stable_argsort_u32.restype = ctypes.c_int
+    lib.oracle_radix_perm_u32.argtypes = [u32p, i32p, ctypes.c_uint64, ctypes.c_int]
+    lib.oracle_radix_perm_u32.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u32(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint32:
+        raise TypeError("expected a uint32 array, got %s" % a.dtype)
+    return a
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def scan_u32(a, inclusive=False):
+    """O1: (out, total) -- exclusive or inclusive scan of a, wrapping at 2^32."""
+    a = _u32(a)
+    out = np.empty_like(a)
+    total = load().oracle_scan_u32(_ptr(a, ctypes.c_uint32), _ptr(out, ctypes.c_uint32),
+                                   a.size, 1 if inclusive else 0)
+    return out, int(total)
+
+
+def scan_exclusive_u32(a):
+    return scan_u32(a, inclusive=False)
+
+
+def scan_inclusive_u32(a):
+    return scan_u32(a, inclusive=True)
+
+
+def scan_blocked_u32(a, b, inclusive=False):
+    """O1b: the three-pass scan at fork depth b; len(a) must be a power of two."""
+    out = np.array(_u32(a), copy=True)
+    total = ctypes.c_uint32(0)
+    rc = load().oracle_scan_blocked_u32(_ptr(out, ctypes.c_uint32), out.size, int(b),
+                                        1 if inclusive else 0, ctypes.byref(total))
+    if rc != 0:
+        raise ValueError("blocked scan needs a power-of-two length, got %d" % out.size)
+    return out, int(total.value)
+
+
+def segscan_u32(a, seg_len):
+    """O2: (out, sums) -- inclusive scan restarted at every multiple of seg_len."""
+    a = _u32(a)
+    if seg_len <= 0:
+        raise ValueError("seg_len must be positive")
+    nseg = (a.size + seg_len - 1) // seg_len
+    out = np.empty_like(a)
+    sums = np.empty(nseg, dtype=np.uint32)
+    got = load().oracle_segscan_u32(_ptr(a, ctypes.c_uint32), _ptr(out, ctypes.c_uint32), a.size,
+                                    int(seg_len), _ptr(sums, ctypes.c_uint32))
+    assert got == nseg
+    return out, sums
+
+
+def compact_flags(flags):
+    """O3: (indices, count) -- kept indices in order, then -1 in every other slot."""
+    flags = np.ascontiguousarray(flags, dtype=np.int32)
+    out = np.empty(flags.size, dtype=np.int32)
+    count = load().oracle_compact_flags(_ptr(flags, ctypes.c_int32), _ptr(out, ctypes.c_int32),
+                                        flags.size)
+    return out, int(count)
+
+
+def stable_argsort_u32(keys):
+    """O4 by definition: the unique stable sorting permutation (gather form)."""
+    keys = _u32(keys)
+    perm = np.empty(keys.size, dtype=np.int32)
+    rc = load().oracle_stable_argsort_u32(_ptr(keys, ctypes.c_uint32), _ptr(perm, ctypes.c_int32),
+                                          keys.size)
+    if rc != 0:
+        raise ValueError("too many keys")
+    return perm
+
+
+def radix_perm_u32(keys, bits_per_pass=1):
+    """O4 by the pages' passes: LSB-first 1-bit (32 passes) or 4-bit (8 passes)."""
+    keys = _u32(keys)
+    perm = np.empty(keys.size, dtype=np.int32)
+    rc = load().oracle_radix_perm_u32(_ptr(keys, ctypes.c_uint32), _ptr(perm, ctypes.c_int32),
+                                      keys.size, int(bits_per_pass))
+    if rc != 0:
+        raise ValueError("bits_per_pass must be 1 or 4 and n below 2^31")
+    return perm

@@ -1,0 +1,356 @@
+/*
+ * oracle.c -- plain sequential CPU oracle for the prefix-scan primitives.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no source, header, table or helper with the HIP
+ * library, and it includes nothing but the C standard library.
+ *
+ * Every function below is the plain definition of its result, written as a
+ * loop in index order, in 32-bit unsigned arithmetic (C defines unsigned
+ * overflow as wrap-around mod 2^32, which is the wrapping add the pages
+ * require).  Where a page describes a schedule (the blocked three-pass scan,
+ * the one-bit radix passes), that schedule is written out step by step as a
+ * second function, used by the tests to check that every schedule reaches the
+ * same bits as the definition.
+ *
+ * Sources (pages):
+ *   [bend]  bendlib, "scan.bend source": header comment (contract, fork depth,
+ *           three passes), "Loops (one lane)", "Pass 1", "Pass 3", "Driver",
+ *           "API".
+ *   [cairn] CAIRN, "Concurrency": sections "reduce and compact" and "scan".
+ *   [futh]  Futhark 0.7.4, Futhark.Pass.ExtractKernels.Segmented:
+ *           regularSegmentedRedomap (Large / Small), regularSegmentedScan.
+ *   [ent]   entelechy docs, package "parallel": kernel table rows
+ *           compact_blank, compact_offsets, compact_gather, compact_total,
+ *           sort_identity, sort_zeros, sort_place, sort_next_bit, and the
+ *           interface rows compact, sort, sort_pass.
+ *
+ * Parity status: every function here is pinned by CPU tests against values
+ * and properties fixed outside this file (worked examples printed on the
+ * pages, closed forms, numpy library routines, brute force); none is
+ * "parity unpinned".
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* O1 -- the scan, by its definition.                                        */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [bend] header comment and "API": exclusive makes a[j] the sum
+ * a[0] + .. + a[j-1] (a[0] becomes 0), inclusive makes a[j] the sum
+ * a[0] + .. + a[j]; both return the total a[0] + .. + a[n-1]; sums wrap at
+ * 2^32.  [cairn] "scan": the same two forms, and a scan may run in place
+ * because each step reads only its own element.
+ *
+ * out may equal a (in place): each a[j] is read before out[j] is written.
+ * Returns the total (0 for n == 0).
+ */
+uint32_t oracle_scan_u32(const uint32_t *a, uint32_t *out, uint64_t n, int inclusive)
+{
+    uint32_t running = 0;
+    for (uint64_t j = 0; j < n; ++j) {
+        uint32_t x = a[j];
+        if (inclusive) {
+            running += x;
+            out[j] = running;
+        } else {
+            out[j] = running;
+            running += x;
+        }
+    }
+    return running;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O1b -- the blocked three-pass scan of [bend], used only to check that      */
+/* every fork depth gives the same bits as O1.                                */
+/* ------------------------------------------------------------------------- */
+
+/* floor(log2 n) for n >= 1. */
+static unsigned floor_log2_u64(uint64_t n)
+{
+    unsigned lg = 0;
+    while (n > 1) {
+        n >>= 1;
+        ++lg;
+    }
+    return lg;
+}
+
+/*
+ * [bend] "Loops (one lane)": one lane walks entries [j, j + count) of a,
+ * writing the running sum before (exclusive) or through (inclusive) each
+ * entry, starting from `base`; returns the running sum past the last entry.
+ */
+static uint32_t one_lane_walk(uint32_t *a, uint64_t j, uint64_t count, uint32_t base, int inclusive)
+{
+    uint32_t s = base;
+    for (uint64_t k = j; k < j + count; ++k) {
+        uint32_t x = a[k];
+        if (inclusive) {
+            s += x;
+            a[k] = s;
+        } else {
+            a[k] = s;
+            s += x;
+        }
+    }
+    return s;
+}
+
+/*
+ * [bend] header comment ("Three passes, with no atomics") and "Driver":
+ *   lg = log2 n, d = min(b, lg), e = lg - d; the array is 2^d blocks of 2^e;
+ *   pass 1: s[i] = sum of block i;
+ *   pass 2: s becomes its exclusive scan plus the total -- on one lane when
+ *           d < 12, otherwise by this same scheme at depth floor(d/2) whose
+ *           own pass 2 is always one lane (run1.sums calls run0);
+ *   pass 3: block i is scanned in place from base s[i].
+ * The page covers arrays of 2^lg entries only, so n must be a power of two.
+ *
+ * `nested_allowed` is 1 for a top-level call and 0 for the nested pass 2.
+ * The 2^12 switch and the floor(d/2) depth are the page's.
+ */
+static uint32_t blocked_scan(uint32_t *a, uint64_t n, unsigned b, int inclusive, int nested_allowed)
+{
+    unsigned lg = floor_log2_u64(n);
+    unsigned d = b < lg ? b : lg;
+    unsigned e = lg - d;
+    uint64_t blocks = (uint64_t)1 << d;
+    uint64_t bsize = (uint64_t)1 << e;
+
+    /* "Array.new(U32, d, 0)" read as 2^d zeros: one sum per block. */
+    uint32_t *s = (uint32_t *)calloc((size_t)blocks, sizeof(uint32_t));
+    if (!s)
+        abort();
+
+    /* Pass 1: each block's sum into s[i] (sums.leaf / sum.go). */
+    for (uint64_t i = 0; i < blocks; ++i) {
+        uint32_t acc = 0;
+        for (uint64_t k = i * bsize; k < (i + 1) * bsize; ++k)
+            acc += a[k];
+        s[i] = acc;
+    }
+
+    /* Pass 2: s becomes its exclusive scan; the walk's end is the total. */
+    uint32_t total;
+    if (d < 12 || !nested_allowed)
+        total = one_lane_walk(s, 0, blocks, 0, 0);             /* run0.sums */
+    else
+        total = blocked_scan(s, blocks, d / 2, 0, 0);           /* run1.sums */
+
+    /* Pass 3: each block's scan in place from its base (puts.leaf / go). */
+    for (uint64_t i = 0; i < blocks; ++i)
+        (void)one_lane_walk(a, i * bsize, bsize, s[i], inclusive);
+
+    free(s);
+    return total;
+}
+
+/*
+ * Returns 0 and sets *total on success; -1 when n is zero or not a power of
+ * two (the page's scheme is defined on 2^lg entries only).
+ */
+int oracle_scan_blocked_u32(uint32_t *a, uint64_t n, unsigned b, int inclusive, uint32_t *total)
+{
+    if (n == 0 || (n & (n - 1)) != 0)
+        return -1;
+    *total = blocked_scan(a, n, b, inclusive, 1);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O2 -- segmented scan and segment sums over regular segments.              */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [futh] regularSegmentedScan / regularSegmentedRedomap name a scan and a
+ * reduction over regular segments: segment s is entries [s*L, s*L + L) (the
+ * last one shorter when L does not divide n).  The definition:
+ *   out[j]  = a[L*floor(j/L)] + .. + a[j]            (mod 2^32)
+ *   sums[s] = a[s*L] + .. + a[min(s*L + L, n) - 1]   (mod 2^32)
+ * The page's Large/Small strategies are schedules and do not change it.
+ * out may equal a.  sums may be NULL.  Returns the number of segments
+ * (ceil(n / L)), or 0 when L == 0.
+ */
+uint64_t oracle_segscan_u32(const uint32_t *a, uint32_t *out, uint64_t n, uint64_t L, uint32_t *sums)
+{
+    if (L == 0)
+        return 0;
+    uint32_t running = 0;
+    for (uint64_t j = 0; j < n; ++j) {
+        if (j % L == 0)
+            running = 0;                /* a segment head restarts the sum */
+        running += a[j];
+        out[j] = running;
+        if (sums && (j % L == L - 1 || j == n - 1))
+            sums[j / L] = running;
+    }
+    return (n + L - 1) / L;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O3 -- stream compaction of flagged rows.                                  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [ent] compact: a non-zero flag keeps that element's index; the kept indices
+ * are gathered to the front, and their count comes out.  The page's steps in
+ * its order:
+ *   compact_blank   -- every slot of the output starts at -1;
+ *   compact_offsets -- inclusive prefix sum of the keep bits, so a kept
+ *                      element at i belongs at offsets[i] - 1;
+ *   compact_gather  -- each kept index i is written to slot offsets[i] - 1;
+ *                      a zero flag writes nothing;
+ *   compact_total   -- the count of kept elements (offsets[n-1], 0 if n = 0).
+ * Returns the count.  out holds n entries.
+ */
+uint64_t oracle_compact_flags(const int32_t *flags, int32_t *out, uint64_t n)
+{
+    for (uint64_t k = 0; k < n; ++k)                 /* compact_blank */
+        out[k] = -1;
+    if (n == 0)
+        return 0;
+
+    uint64_t *offsets = (uint64_t *)malloc((size_t)n * sizeof(uint64_t));
+    if (!offsets)
+        abort();
+    uint64_t running = 0;                            /* compact_offsets */
+    for (uint64_t i = 0; i < n; ++i) {
+        running += (flags[i] != 0) ? 1u : 0u;
+        offsets[i] = running;
+    }
+    for (uint64_t i = 0; i < n; ++i)                 /* compact_gather */
+        if (flags[i] != 0)
+            out[offsets[i] - 1] = (int32_t)i;
+    uint64_t count = offsets[n - 1];                 /* compact_total */
+    free(offsets);
+    return count;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O4 -- the stable radix-sort permutation.                                  */
+/* ------------------------------------------------------------------------- */
+
+static int cmp_u64(const void *x, const void *y)
+{
+    uint64_t a = *(const uint64_t *)x, b = *(const uint64_t *)y;
+    return (a > b) - (a < b);
+}
+
+/*
+ * The definition: perm is the permutation, in gather form (sorted[k] =
+ * keys[perm[k]], as [ent] sort is read through: at(bodies, at(order, slot))),
+ * that puts the keys in non-decreasing unsigned order with equal keys in
+ * ascending source index -- the unique stable sorting permutation.
+ * Computed by sorting the distinct 64-bit composites (key << 32 | index);
+ * since no two composites are equal the order is total and stability is
+ * built in.  n must be below 2^32.
+ */
+int oracle_stable_argsort_u32(const uint32_t *keys, int32_t *perm, uint64_t n)
+{
+    if (n >= ((uint64_t)1 << 32))
+        return -1;
+    if (n == 0)
+        return 0;
+    uint64_t *pairs = (uint64_t *)malloc((size_t)n * sizeof(uint64_t));
+    if (!pairs)
+        abort();
+    for (uint64_t i = 0; i < n; ++i)
+        pairs[i] = ((uint64_t)keys[i] << 32) | i;
+    qsort(pairs, (size_t)n, sizeof(uint64_t), cmp_u64);
+    for (uint64_t k = 0; k < n; ++k)
+        perm[k] = (int32_t)(uint32_t)(pairs[k] & 0xFFFFFFFFu);
+    free(pairs);
+    return 0;
+}
+
+/*
+ * [ent] sort / sort_pass, least significant bit first, with the pages' steps:
+ *   sort_identity -- order[i] = i;
+ *   per bit (sort_next_bit steps bit = 0, 1, .., 31):
+ *     sort_zeros -- zeros[i] = how many places at or before i hold an element
+ *                   (read through order) with a 0 at this bit;
+ *     sort_place -- a zero lands at its rank among the zeros, zeros[i] - 1;
+ *                   a one lands behind all Z zeros at its rank among the
+ *                   ones, Z + (i + 1 - zeros[i]) - 1;
+ *                   each place is written by exactly one element.
+ * Keys are full 32-bit unsigned values, so 32 one-bit passes run (the page
+ * allows 1..31 bits of non-negative keys; the unsigned widening is this
+ * build's reading).
+ *
+ * bits_per_pass == 4 runs the same loop with a 4-bit digit per pass, 8
+ * passes: a stable counting pass in which a digit-d element lands at
+ * (count of smaller digits) + (its rank among the digit-d elements); [cairn]
+ * "scan" says the radix sort places each digit by an exclusive scan, and this
+ * is that placement for 16 digit values.
+ * Returns 0, or -1 for bits_per_pass other than 1 or 4 or n >= 2^31.
+ */
+int oracle_radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass)
+{
+    if ((bits_per_pass != 1 && bits_per_pass != 4) || n >= ((uint64_t)1 << 31))
+        return -1;
+    if (n == 0)
+        return 0;
+    uint32_t *order = (uint32_t *)malloc((size_t)n * sizeof(uint32_t));
+    uint32_t *next = (uint32_t *)malloc((size_t)n * sizeof(uint32_t));
+    uint32_t *zeros = (uint32_t *)malloc((size_t)n * sizeof(uint32_t));
+    if (!order || !next || !zeros)
+        abort();
+
+    for (uint64_t i = 0; i < n; ++i)                 /* sort_identity */
+        order[i] = (uint32_t)i;
+
+    if (bits_per_pass == 1) {
+        for (unsigned bit = 0; bit < 32; ++bit) {    /* sort_next_bit */
+            uint32_t z = 0;                          /* sort_zeros */
+            for (uint64_t i = 0; i < n; ++i) {
+                if (((keys[order[i]] >> bit) & 1u) == 0)
+                    ++z;
+                zeros[i] = z;
+            }
+            uint32_t Z = z;
+            for (uint64_t i = 0; i < n; ++i) {       /* sort_place */
+                uint64_t dest;
+                if (((keys[order[i]] >> bit) & 1u) == 0)
+                    dest = (uint64_t)zeros[i] - 1;
+                else
+                    dest = (uint64_t)Z + (i + 1 - zeros[i]) - 1;
+                next[dest] = order[i];
+            }
+            uint32_t *t = order;
+            order = next;
+            next = t;
+        }
+    } else {
+        for (unsigned shift = 0; shift < 32; shift += 4) {
+            uint64_t count[16] = {0};
+            for (uint64_t i = 0; i < n; ++i)
+                ++count[(keys[order[i]] >> shift) & 15u];
+            uint64_t base[16];
+            uint64_t acc = 0;                        /* exclusive scan of counts */
+            for (int dgt = 0; dgt < 16; ++dgt) {
+                base[dgt] = acc;
+                acc += count[dgt];
+            }
+            for (uint64_t i = 0; i < n; ++i) {       /* stable placement */
+                unsigned dgt = (keys[order[i]] >> shift) & 15u;
+                next[base[dgt]++] = order[i];
+            }
+            uint32_t *t = order;
+            order = next;
+            next = t;
+        }
+    }
+
+    for (uint64_t k = 0; k < n; ++k)
+        perm[k] = (int32_t)order[k];
+    free(order);
+    free(next);
+    free(zeros);
+    return 0;
+}

@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Nothing here needs a GPU.  The oracle is checked against: values the pages
+print (tests/golden/), closed forms, numpy library routines (cumsum,
+flatnonzero, argsort(kind="stable")), pure-Python brute force on tiny inputs,
+and the invariants the pages state (every fork depth gives the same bits,
+inclusive = exclusive + element, compaction ranks = inclusive offsets - 1,
+the permutation matches a stable sort).
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+M = 1 << 32
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# O1 scan
+# --------------------------------------------------------------------------
+
+def test_scan_worked_example_cairn_offsets():
+    g = golden("cairn_scan_offsets.json")
+    a = np.array(g["input"], dtype=np.uint32)
+    ex, tot = oracle.scan_exclusive_u32(a)
+    assert tot == g["total"]
+    for j, v in g["exclusive_at"].items():
+        assert int(ex[int(j)]) == v
+
+
+def test_scan_iota_total_cairn_tasks():
+    g = golden("cairn_tasks_total.json")
+    _, tot = oracle.scan_exclusive_u32(workloads.iota_u32(g["n"]))
+    assert tot == g["total"]
+    _, tot_in = oracle.scan_inclusive_u32(workloads.iota_u32(g["n"]))
+    assert tot_in == g["total"]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 64, 1000, 1 << 16, (1 << 16) + 3])
+def test_scan_closed_form_all_ones(n):
+    ex, t = oracle.scan_exclusive_u32(workloads.ones_u32(n))
+    inc, t2 = oracle.scan_inclusive_u32(workloads.ones_u32(n))
+    j = np.arange(n, dtype=np.uint64)
+    assert np.array_equal(ex, j.astype(np.uint32))
+    assert np.array_equal(inc, (j + 1).astype(np.uint32))
+    assert t == t2 == n % M
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 4096, (1 << 20) + 1])
+def test_scan_closed_form_all_ff_wraps(n):
+    ex, t = oracle.scan_exclusive_u32(workloads.all_ff_u32(n))
+    inc, _ = oracle.scan_inclusive_u32(workloads.all_ff_u32(n))
+    j = np.arange(n, dtype=np.int64)
+    assert np.array_equal(ex, ((-j) % M).astype(np.uint32))
+    assert np.array_equal(inc, ((-(j + 1)) % M).astype(np.uint32))
+    assert t == (-n) % M
+
+
+def test_scan_closed_form_totals_at_config_sizes():
+    # all-ones and all-0xFFFFFFFF totals at 2^24 (the 2^28 case is the same
+    # closed form; it runs in the GPU parity tests).
+    n = 1 << 24
+    _, t1 = oracle.scan_exclusive_u32(workloads.ones_u32(n))
+    _, t2 = oracle.scan_exclusive_u32(workloads.all_ff_u32(n))
+    assert t1 == 0x01000000
+    assert t2 == 0xFF000000
+
+
+@pytest.mark.parametrize("seed,n", [(1, 1), (2, 17), (3, 1000), (4, 1 << 16), (5, 123457)])
+def test_scan_matches_numpy_cumsum(seed, n):
+    a = workloads.small_random_u32(n, seed)
+    inc, t = oracle.scan_inclusive_u32(a)
+    ex, t2 = oracle.scan_exclusive_u32(a)
+    ref = np.cumsum(a, dtype=np.uint32)
+    assert np.array_equal(inc, ref)
+    assert t == t2 == int(ref[-1])
+    assert ex[0] == 0 and np.array_equal(ex[1:], ref[:-1])
+
+
+def test_scan_brute_force_exhaustive_tiny():
+    vals = [0, 1, 2, M - 1, M - 2]
+    for n in range(0, 5):
+        for tup in itertools.product(vals, repeat=n):
+            a = np.array(tup, dtype=np.uint32)
+            ex, t = oracle.scan_exclusive_u32(a)
+            inc, t2 = oracle.scan_inclusive_u32(a)
+            assert ex.tolist() == brute.exclusive(list(tup))
+            assert inc.tolist() == brute.inclusive(list(tup))
+            assert t == t2 == brute.total(list(tup))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_scan_brute_force_random_upto_64(seed):
+    n = 1 + seed * 9
+    a = workloads.small_random_u32(n, 1000 + seed)
+    ex, t = oracle.scan_exclusive_u32(a)
+    inc, _ = oracle.scan_inclusive_u32(a)
+    assert ex.tolist() == brute.exclusive(a.tolist())
+    assert inc.tolist() == brute.inclusive(a.tolist())
+    assert t == brute.total(a.tolist())
+
+
+@pytest.mark.parametrize("n", [1, 5, 4099])
+def test_scan_invariants(n):
+    a = workloads.small_random_u32(n, 77)
+    ex, t = oracle.scan_exclusive_u32(a)
+    inc, t2 = oracle.scan_inclusive_u32(a)
+    assert np.array_equal(inc, ex + a)               # wraps like the arrays do
+    assert int(inc[-1]) == t == t2 == int((np.uint64(ex[-1]) + a[-1]) % M)
+
+
+def test_scan_empty():
+    ex, t = oracle.scan_exclusive_u32(np.zeros(0, dtype=np.uint32))
+    assert ex.size == 0 and t == 0
+
+
+# --------------------------------------------------------------------------
+# O1b blocked three-pass: every fork depth gives the same bits
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lg", [0, 1, 4, 10, 13])
+def test_blocked_every_b_same_bits(lg):
+    n = 1 << lg
+    a = workloads.small_random_u32(n, 300 + lg)
+    for inclusive in (False, True):
+        ref, tref = oracle.scan_u32(a, inclusive)
+        for b in range(0, lg + 3):           # b above lg is lowered to lg
+            out, t = oracle.scan_blocked_u32(a, b, inclusive)
+            assert t == tref, (lg, b)
+            assert np.array_equal(out, ref), (lg, b, inclusive)
+
+
+def test_blocked_nested_pass2_branch():
+    # d >= 12 takes the nested pass 2 at depth floor(d/2); check d = 12..16.
+    n = 1 << 16
+    a = workloads.small_random_u32(n, 12345)
+    ref, tref = oracle.scan_exclusive_u32(a)
+    for b in range(12, 17):
+        out, t = oracle.scan_blocked_u32(a, b, False)
+        assert t == tref and np.array_equal(out, ref), b
+
+
+def test_blocked_config_small_b0_to_8():
+    a = workloads.uniform_u32(workloads.N_SCAN_SMALL, workloads.SEED_SCAN_SMALL)
+    for inclusive in (False, True):
+        ref, tref = oracle.scan_u32(a, inclusive)
+        for b in range(9):
+            out, t = oracle.scan_blocked_u32(a, b, inclusive)
+            assert t == tref and np.array_equal(out, ref)
+
+
+def test_blocked_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        oracle.scan_blocked_u32(np.ones(3, dtype=np.uint32), 1)
+
+
+# --------------------------------------------------------------------------
+# O2 segmented scan and sums
+# --------------------------------------------------------------------------
+
+def test_segscan_reduce_pin_cairn_weights():
+    g = golden("cairn_reduce_weights.json")
+    w = (np.arange(g["n"]) % g["modulus"]).astype(np.uint32)
+    out, sums = oracle.segscan_u32(w, g["n"])
+    assert sums.tolist() == [g["sum"]]
+    assert int(out[-1]) == g["sum"]
+
+
+@pytest.mark.parametrize("n,L", [(4096, 16), (5000, 16), (1 << 14, 1 << 10), (1000, 7), (64, 64), (63, 64)])
+def test_segscan_matches_numpy(n, L):
+    a = workloads.small_random_u32(n, n + L, high=1 << 16)
+    out, sums = oracle.segscan_u32(a, L)
+    pad = (-n) % L
+    ap = np.concatenate([a, np.zeros(pad, dtype=np.uint32)]).reshape(-1, L)
+    ref = np.cumsum(ap, axis=1, dtype=np.uint32).reshape(-1)[:n]
+    assert np.array_equal(out, ref)
+    assert np.array_equal(sums, np.cumsum(ap, axis=1, dtype=np.uint32)[:, -1])
+
+
+def test_segscan_special_cases():
+    a = workloads.small_random_u32(1000, 9)
+    out, sums = oracle.segscan_u32(a, 1)             # L = 1: out = a, sums = a
+    assert np.array_equal(out, a) and np.array_equal(sums, a)
+    inc, t = oracle.scan_inclusive_u32(a)
+    for L in (1000, 1001, 1 << 20):                  # L >= n: one segment
+        out, sums = oracle.segscan_u32(a, L)
+        assert np.array_equal(out, inc) and sums.tolist() == [t]
+
+
+def test_segscan_restart_equals_per_segment_scan():
+    a = workloads.small_random_u32(3 * 512 + 100, 10)
+    out, sums = oracle.segscan_u32(a, 512)
+    for s in range(0, a.size, 512):
+        inc, t = oracle.scan_inclusive_u32(a[s:s + 512])
+        assert np.array_equal(out[s:s + 512], inc)
+        assert int(sums[s // 512]) == t
+        assert int(sums[s // 512]) == int(out[min(s + 512, a.size) - 1])
+
+
+def test_segscan_wraps():
+    L = 1 << 17                                      # 2^17 * 65535 > 2^32
+    a = np.full(2 * L, 0xFFFF, dtype=np.uint32)
+    out, sums = oracle.segscan_u32(a, L)
+    assert int(sums[0]) == (L * 0xFFFF) % M and int(sums[1]) == (L * 0xFFFF) % M
+    assert int(out[L]) == 0xFFFF
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_segscan_brute_force(seed):
+    n = 5 + 9 * seed
+    L = 1 + seed * 2
+    a = workloads.small_random_u32(n, 2000 + seed)
+    out, sums = oracle.segscan_u32(a, L)
+    bo, bs = brute.segscan(a.tolist(), L)
+    assert out.tolist() == bo and sums.tolist() == bs
+
+
+# --------------------------------------------------------------------------
+# O3 compaction
+# --------------------------------------------------------------------------
+
+def test_compact_worked_example_cairn_keep_live():
+    g = golden("cairn_compact_keep_live.json")
+    flags = np.array(g["flags"], dtype=np.int32)
+    idx, count = oracle.compact_flags(flags)
+    assert count == g["count"]
+    assert flags[idx[:count]].tolist() == g["gathered_values"]
+    assert (idx[count:] == -1).all()
+
+
+@pytest.mark.parametrize("p,n", [(0.5, 10000), (0.01, 10000), (0.99, 10000), (0.5, 1), (0.3, 4097)])
+def test_compact_matches_flatnonzero_and_ranks(p, n):
+    flags = workloads.bernoulli_flags(n, p, int(p * 1000) + n)
+    idx, count = oracle.compact_flags(flags)
+    kept = np.flatnonzero(flags)
+    assert count == kept.size
+    assert np.array_equal(idx[:count], kept.astype(np.int32))
+    assert (idx[count:] == -1).all()
+    # ranks = inclusive offsets - 1 (offsets from the scan oracle)
+    inc, tot = oracle.scan_inclusive_u32((flags != 0).astype(np.uint32))
+    assert tot == count
+    assert np.array_equal(idx[inc[kept].astype(np.int64) - 1], kept.astype(np.int32))
+
+
+def test_compact_special_cases():
+    idx, c = oracle.compact_flags(np.zeros(100, dtype=np.int32))
+    assert c == 0 and (idx == -1).all()
+    idx, c = oracle.compact_flags(np.ones(100, dtype=np.int32))
+    assert c == 100 and np.array_equal(idx, np.arange(100, dtype=np.int32))
+    idx, c = oracle.compact_flags(np.array([-5, 0, 2], dtype=np.int32))   # any non-zero keeps
+    assert c == 2 and idx.tolist() == [0, 2, -1]
+    idx, c = oracle.compact_flags(np.zeros(0, dtype=np.int32))
+    assert c == 0 and idx.size == 0
+
+
+def test_compact_brute_force_exhaustive():
+    for n in range(0, 9):
+        for tup in itertools.product([0, 1, -1], repeat=min(n, 6)):
+            flags = list(tup) + [1, 0] * ((n - len(tup)) // 2) + [0] * ((n - len(tup)) % 2)
+            idx, c = oracle.compact_flags(np.array(flags, dtype=np.int32))
+            bi, bc = brute.compact(flags)
+            assert idx.tolist() == bi and c == bc
+
+
+# --------------------------------------------------------------------------
+# O4 radix permutation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,n,high", [(1, 1000, 1 << 32), (2, 1000, 8), (3, 4097, 256), (4, 1, 5),
+                                         (5, 3000, 2)])
+def test_radix_matches_numpy_stable_argsort(seed, n, high):
+    keys = workloads.small_random_u32(n, seed, high=high)
+    ref = np.argsort(keys, kind="stable").astype(np.int32)
+    assert np.array_equal(oracle.stable_argsort_u32(keys), ref)
+    assert np.array_equal(oracle.radix_perm_u32(keys, 1), ref)
+    assert np.array_equal(oracle.radix_perm_u32(keys, 4), ref)
+
+
+def test_radix_distinct_workload_shape():
+    keys = workloads.radix_keys_distinct(20000)
+    assert np.unique(keys).size == 256
+    ref = np.argsort(keys, kind="stable").astype(np.int32)
+    assert np.array_equal(oracle.radix_perm_u32(keys, 1), ref)
+    assert np.array_equal(oracle.radix_perm_u32(keys, 4), ref)
+
+
+def test_radix_special_cases():
+    n = 777
+    srt = np.arange(n, dtype=np.uint32) * 3
+    iota = np.arange(n, dtype=np.int32)
+    for bpp in (1, 4):
+        assert np.array_equal(oracle.radix_perm_u32(srt, bpp), iota)
+        assert np.array_equal(oracle.radix_perm_u32(np.full(n, 0xABCDEF01, dtype=np.uint32), bpp), iota)
+        dec = (np.uint32(0xFFFFFFFF) - np.arange(n, dtype=np.uint32))
+        assert np.array_equal(oracle.radix_perm_u32(dec, bpp), iota[::-1])
+    assert np.array_equal(oracle.stable_argsort_u32(srt), iota)
+
+
+def test_radix_brute_force_all_small_arrays():
+    for n in range(0, 6):
+        for tup in itertools.product([0, 1, 0x80000000, 0xFFFFFFFF], repeat=n):
+            keys = np.array(tup, dtype=np.uint32)
+            bp = brute.stable_perm(list(tup))
+            assert oracle.stable_argsort_u32(keys).tolist() == bp
+            assert oracle.radix_perm_u32(keys, 1).tolist() == bp
+            assert oracle.radix_perm_u32(keys, 4).tolist() == bp
+
+
+def test_radix_perm_is_bijection_and_sorts():
+    keys = workloads.radix_keys_uniform(50000, 11)
+    perm = oracle.radix_perm_u32(keys, 1)
+    seen = np.zeros(keys.size, dtype=bool)
+    seen[perm] = True
+    assert seen.all()
+    s = keys[perm]
+    assert (s[1:] >= s[:-1]).all()
+    ties = s[1:] == s[:-1]
+    assert (perm[1:][ties] > perm[:-1][ties]).all()
+
+
+def test_radix_rejects_bad_args():
+    with pytest.raises(ValueError):
+        oracle.radix_perm_u32(np.ones(4, dtype=np.uint32), 2)

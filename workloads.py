@@ -1,0 +1,96 @@
+"""Seeded synthetic inputs for the prefix-scan primitives.
+
+This module only draws random numbers and fills arrays; it holds none of the
+arithmetic of the method, so both sides of a parity check (the HIP library
+and the CPU oracle) can take their inputs from it without sharing any code of
+the computation.  Every generator is a ``numpy.random.Generator`` over
+``PCG64(seed)``, so the same seed gives the same array on every machine.
+
+The workloads (sizes, value ranges, seeds):
+
+  scan_small      n = 2^16 uniform u32 (seed 101), checked at fork depths 0..8
+  scan_mid        n = 2^24 uniform u32 (seed 201), plus all-ones / all-0xFFFFFFFF
+  scan_large      n = 2^28 uniform u32 (seed 202), plus all-ones / all-0xFFFFFFFF
+  compact_p*      n = 2^26 int32 0/1 flags, Bernoulli keep probability
+                  p = 0.5 / 0.01 / 0.99 (seeds 301 / 302 / 303)
+  segscan         n = 2^26 u32 uniform over [0, 2^16) (seed 401), regular
+                  segments of length 16 and 2^20
+  radix_uniform   n = 2^25 uniform u32 keys (seed 501)
+  radix_distinct  n = 2^25 keys drawn from 256 distinct uniform u32 values
+                  (seed 502)
+"""
+import numpy as np
+
+U32_MAX = 0xFFFFFFFF
+
+SEED_SCAN_SMALL = 101
+SEED_SCAN_MID = 201
+SEED_SCAN_LARGE = 202
+SEED_COMPACT = {0.5: 301, 0.01: 302, 0.99: 303}
+SEED_SEGSCAN = 401
+SEED_RADIX_UNIFORM = 501
+SEED_RADIX_DISTINCT = 502
+
+N_SCAN_SMALL = 1 << 16
+N_SCAN_MID = 1 << 24
+N_SCAN_LARGE = 1 << 28
+N_COMPACT = 1 << 26
+N_SEGSCAN = 1 << 26
+SEG_LENS = (16, 1 << 20)
+N_RADIX = 1 << 25
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def uniform_u32(n: int, seed: int) -> np.ndarray:
+    """n values uniform over [0, 2^32)."""
+    return rng(seed).integers(0, 1 << 32, size=n, dtype=np.uint32)
+
+
+def ones_u32(n: int) -> np.ndarray:
+    return np.ones(n, dtype=np.uint32)
+
+
+def all_ff_u32(n: int) -> np.ndarray:
+    """Every entry 0xFFFFFFFF: the sums wrap at every step."""
+    return np.full(n, U32_MAX, dtype=np.uint32)
+
+
+def iota_u32(n: int) -> np.ndarray:
+    return np.arange(n, dtype=np.uint32)
+
+
+def bernoulli_flags(n: int, p: float, seed: int) -> np.ndarray:
+    """int32 flags, 1 with probability p, else 0."""
+    return (rng(seed).random(n) < p).astype(np.int32)
+
+
+def compact_flags(p: float, n: int = N_COMPACT) -> np.ndarray:
+    return bernoulli_flags(n, p, SEED_COMPACT[p])
+
+
+def seg_values(n: int = N_SEGSCAN, seed: int = SEED_SEGSCAN) -> np.ndarray:
+    """u32 values uniform over [0, 2^16)."""
+    return rng(seed).integers(0, 1 << 16, size=n, dtype=np.uint32)
+
+
+def radix_keys_uniform(n: int = N_RADIX, seed: int = SEED_RADIX_UNIFORM) -> np.ndarray:
+    return uniform_u32(n, seed)
+
+
+def radix_keys_distinct(n: int = N_RADIX, distinct: int = 256,
+                        seed: int = SEED_RADIX_DISTINCT) -> np.ndarray:
+    """Keys drawn uniformly from `distinct` distinct uniform u32 values."""
+    g = rng(seed)
+    while True:
+        vals = g.integers(0, 1 << 32, size=distinct, dtype=np.uint32)
+        if np.unique(vals).size == distinct:
+            break
+    return vals[g.integers(0, distinct, size=n)]
+
+
+def small_random_u32(n: int, seed: int, high: int = 1 << 32) -> np.ndarray:
+    """Generic seeded u32 array for the small parity cases."""
+    return rng(seed).integers(0, high, size=n, dtype=np.uint32)
