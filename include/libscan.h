@@ -1,0 +1,229 @@
+/*
+ * libscan.h -- device-wide parallel prefix primitives over 32-bit integers
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer to memory the caller
+ *   owns (for instance a torch tensor's data); the library never allocates,
+ *   frees or keeps any of them past the call.  Arrays are dense and
+ *   contiguous, element i at byte offset 4*i, and must be 4-byte aligned.
+ *   Host pointers are named *_host and are plain host memory.
+ * Stream.  Every call is ordered on `stream` (NULL is the null stream).  It
+ *   enqueues its kernels and returns; it waits for the GPU only when the
+ *   caller asks for a result on the host (a non-NULL *_host pointer), because
+ *   only then does the host observe it.
+ * Scratch.  Calls that coordinate workgroups need device scratch memory,
+ *   sized by the matching *_scratch_bytes query.  A scratch buffer must be
+ *   zero-filled once before its first use (libscan_scratch_init does this
+ *   on the stream); after that the library keeps it consistent from call to
+ *   call by itself, with no clearing in between.  Two calls that may run at
+ *   the same time (different streams) need different scratch buffers.
+ * Errors.  Every int-returning call returns LIBSCAN_OK (0) or a negative
+ *   LIBSCAN_ERR_* code.  Argument errors are found before anything is
+ *   launched and leave every buffer untouched.  LIBSCAN_ERR_HIP means a HIP
+ *   call failed; libscan_strerror then names the HIP error.
+ * Arithmetic.  All sums are unsigned 32-bit and wrap at 2^32.  Every result
+ *   is unique and independent of tile size, workgroup count and fork depth:
+ *   the library returns the same bits as the sequential definition.
+ * Limits.  n <= LIBSCAN_MAX_N for the scans; n <= 2^31 - 1 where the output
+ *   holds int32 indices (compaction, radix permutation).
+ */
+#ifndef LIBSCAN_H
+#define LIBSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    LIBSCAN_OK = 0,
+    LIBSCAN_ERR_NULL = -1,     /* a required pointer is NULL */
+    LIBSCAN_ERR_SIZE = -2,     /* n beyond the entry point's limit */
+    LIBSCAN_ERR_ARG = -3,      /* an argument outside its documented range */
+    LIBSCAN_ERR_SCRATCH = -4,  /* scratch_bytes below the size query's answer */
+    LIBSCAN_ERR_HIP = -5,      /* a HIP runtime call failed */
+    LIBSCAN_ERR_ALIGN = -6     /* a pointer is not 4-byte aligned */
+};
+
+/* Largest n accepted by the scans and the segmented scan (2^36 elements,
+ * 256 GiB of u32). */
+#define LIBSCAN_MAX_N ((uint64_t)1 << 36)
+/* Largest n accepted where outputs are int32 indices. */
+#define LIBSCAN_MAX_N_INDEX ((uint64_t)0x7FFFFFFF)
+
+/* Scan algorithms for scan_u32_ex. */
+enum {
+    LIBSCAN_ALGO_AUTO = 0,       /* the single-pass look-back scan */
+    LIBSCAN_ALGO_LOOKBACK = 1,   /* single pass, chained carry between tiles */
+    LIBSCAN_ALGO_THREEPASS = 2   /* reduce blocks / scan the sums / rescan blocks */
+};
+
+/* Text for a status code; for LIBSCAN_ERR_HIP, the text of the HIP error the
+ * calling thread saw last.  Never NULL. */
+const char *libscan_strerror(int status);
+
+/* Library version string, e.g. "libscan 0.1 gfx950". */
+const char *libscan_version(void);
+
+/* Zero-fill `scratch_bytes` bytes of device scratch on `stream` with a fill
+ * kernel (no hipMemset node, so it can be captured in a graph).  Required
+ * once before a scratch buffer's first use. */
+int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Scan                                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Exclusive / inclusive prefix sum of n u32 values, in place.
+ *   bendlib "scan.bend source", header comment and API: exclusive makes a[j]
+ *   the sum a[0] + .. + a[j-1] (a[0] becomes 0), inclusive makes a[j] the sum
+ *   a[0] + .. + a[j]; both return the total a[0] + .. + a[n-1]; sums wrap at
+ *   2^32.  CAIRN "Concurrency", section "scan": a device scan whose total
+ *   nobody binds leaves its prefixes in device memory and nothing waits.
+ *
+ * data         device, n u32, read then overwritten in place.
+ * n            element count; 0 is a no-op with total 0.
+ * total_host   host u32 or NULL.  If set, the call copies the total there and
+ *              waits for the stream.
+ * total_dev    device u32 or NULL.  If set, the total is written there in
+ *              stream order; the call does not wait.
+ * scratch      device scratch of at least scan_scratch_bytes(n) bytes,
+ *              zero-filled once before first use.
+ * stream       HIP stream.
+ * Errors: ERR_NULL (data NULL with n > 0, or scratch NULL with n > 0),
+ * ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_SCRATCH, ERR_HIP.
+ */
+size_t scan_scratch_bytes(uint64_t n);
+int scan_exclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream);
+int scan_inclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * The scan with the algorithm and the fork depth chosen by the caller.
+ *   bendlib "scan.bend source", header comment: fork depth b cuts the array
+ *   into 2^b equal blocks (b lowered to log2 n when larger) and every b gives
+ *   the same bits; the three passes are (1) each block's sum, (2) the
+ *   exclusive scan of the sums and the total -- one lane below 2^12 sums,
+ *   else this same scan at half the depth -- and (3) each block rescanned from
+ *   its base, in place.
+ *
+ * inclusive    0 exclusive, 1 inclusive.
+ * algo         LIBSCAN_ALGO_*.
+ * fork_depth   THREEPASS: -1 picks a depth for the GPU, b >= 0 uses
+ *              d = min(b, floor(log2 n), 24) and 2^d blocks of ceil(n / 2^d)
+ *              entries (the last blocks shorter or empty when 2^d does not
+ *              divide n), one workgroup per block.  LOOKBACK: must be -1.
+ * Other arguments as scan_exclusive_u32.  scratch must hold
+ * scan_ex_scratch_bytes(n, algo, fork_depth) bytes.
+ * Errors: as scan_exclusive_u32, plus ERR_ARG for an unknown algo, a
+ * fork_depth below -1 or above 40, or a fork_depth with LOOKBACK.
+ */
+size_t scan_ex_scratch_bytes(uint64_t n, int algo, int fork_depth);
+int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_depth,
+                uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
+                hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Segmented scan and segment sums over regular segments                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Inclusive scan restarted at every segment head, and each segment's sum.
+ *   Futhark 0.7.4 Futhark.Pass.ExtractKernels.Segmented: regularSegmentedScan
+ *   and regularSegmentedRedomap over regular segments, with a Small strategy
+ *   (several segments per workgroup) and a Large one (several workgroups per
+ *   segment, their partial results combined).
+ * Segment s is entries [s*seg_len, min(s*seg_len + seg_len, n)).
+ *   out[j]  = in[h] + .. + in[j], h = seg_len * floor(j / seg_len)
+ *   sums[s] = the sum of segment s
+ *
+ * in        device, n u32.
+ * out       device, n u32; may equal in (in place); partial overlap is not
+ *           allowed.
+ * seg_len   segment length >= 1; seg_len >= n is one segment.
+ * seg_sums  device, ceil(n / seg_len) u32, or NULL to skip the sums.
+ * scratch   at least segscan_scratch_bytes(n, seg_len) bytes, zeroed once.
+ * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_ARG
+ * (seg_len == 0), ERR_SCRATCH, ERR_HIP.
+ */
+size_t segscan_scratch_bytes(uint64_t n, uint64_t seg_len);
+int segscan_u32(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
+                uint32_t *seg_sums, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stream compaction                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Indices of the non-zero flags, in order, at the front of out_idx; -1 in
+ * every other slot; the count kept.
+ *   entelechy "parallel" package, compact: a non-zero flag keeps that
+ *   element's index; compact_offsets is the inclusive prefix sum, so a kept
+ *   element at i lands at offsets[i] - 1 (compact_gather); compact_blank
+ *   leaves -1 where nothing was gathered; compact_total is the count.
+ *
+ * flags       device, n int32; any non-zero value keeps its index.
+ * out_idx     device, n int32; every slot is written exactly once.  Must not
+ *             overlap flags.
+ * count_host  host u32 or NULL (if set, the call waits for the stream).
+ * count_dev   device u32 or NULL.
+ * scratch     at least compact_scratch_bytes(n) bytes, zeroed once.
+ * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N_INDEX),
+ * ERR_SCRATCH, ERR_HIP.
+ */
+size_t compact_scratch_bytes(uint64_t n);
+int compact_flags_u32(const int32_t *flags, int32_t *out_idx, uint64_t n, uint32_t *count_host,
+                      uint32_t *count_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stable LSB radix-sort permutation                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The stable permutation that sorts n unsigned 32-bit keys, in gather form:
+ * keys[perm[0]] <= keys[perm[1]] <= ..., equal keys in ascending index.
+ *   entelechy "parallel" package, sort / sort_pass / sort_zeros / sort_place:
+ *   least significant bit first; per bit, the count of zeros at or before
+ *   each place ranks the zeros, and every one lands behind all zeros at its
+ *   rank among the ones.  CAIRN "Concurrency", section "scan": the radix sort
+ *   places each digit with an exclusive scan, which makes it stable.
+ *
+ * keys           device, n u32 (not modified).
+ * perm           device, n int32 output.  Must not overlap keys.
+ * bits_per_pass  1 (32 one-bit passes) or 4 (8 four-bit passes); both give
+ *                the same permutation.
+ * scratch        at least radix_scratch_bytes(n, bits_per_pass) bytes,
+ *                zeroed once.  It holds the key and index ping-pong rows.
+ * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N_INDEX), ERR_ARG
+ * (bits_per_pass not 1 or 4), ERR_SCRATCH, ERR_HIP.
+ */
+size_t radix_scratch_bytes(uint64_t n, int bits_per_pass);
+int radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass,
+                   void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Measurement aid                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * dst[i] = src[i] for i < n with the same 16-byte loads and stores the scans
+ * use: the practical bandwidth ceiling a streaming kernel reaches, timed
+ * beside the scans, and the known-size kernel that calibrates the HBM byte
+ * counters.  src and dst must not overlap.
+ * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_HIP.
+ */
+int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSCAN_H */

@@ -1,0 +1,289 @@
+"""Python binding of libscan, the MI355X (gfx950) prefix-scan library.
+
+Argument marshalling only: every function here checks tensors, takes their
+device pointers and the current HIP stream, and calls the C entry point of the
+same name in ``libscan.so`` (declared in ``include/libscan.h``).  All
+computation runs in the library's HIP kernels; there is no CPU fallback, and
+a missing ``libscan.so`` raises.
+
+PyTorch supplies device memory and streams.  Tensors must be on a CUDA (HIP)
+device, contiguous, with 4-byte elements (torch.int32 or torch.uint32).
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "LibscanError", "lib", "version",
+    "scan_exclusive_u32", "scan_inclusive_u32", "scan_u32_ex",
+    "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
+    "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
+    "compact_scratch_bytes", "radix_scratch_bytes",
+    "ALGO_AUTO", "ALGO_LOOKBACK", "ALGO_THREEPASS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libscan.so")
+
+OK = 0
+ERR_NULL, ERR_SIZE, ERR_ARG, ERR_SCRATCH, ERR_HIP, ERR_ALIGN = -1, -2, -3, -4, -5, -6
+ALGO_AUTO, ALGO_LOOKBACK, ALGO_THREEPASS = 0, 1, 2
+_ALGOS = {"auto": ALGO_AUTO, "lookback": ALGO_LOOKBACK, "threepass": ALGO_THREEPASS}
+
+
+class LibscanError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, lib().libscan_strerror(status).decode(),
+                                                         status))
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libscan.so (ctypes.CDLL) with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libscan.so is not built (%s); run `python -m prefix_scan_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u64, i32, sz = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_size_t
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        L.libscan_strerror.argtypes = [i32]
+        L.libscan_strerror.restype = ctypes.c_char_p
+        L.libscan_version.argtypes = []
+        L.libscan_version.restype = ctypes.c_char_p
+        L.libscan_scratch_init.argtypes = [vp, sz, vp]
+        L.libscan_scratch_init.restype = i32
+        L.scan_scratch_bytes.argtypes = [u64]
+        L.scan_scratch_bytes.restype = sz
+        L.scan_ex_scratch_bytes.argtypes = [u64, i32, i32]
+        L.scan_ex_scratch_bytes.restype = sz
+        for name in ("scan_exclusive_u32", "scan_inclusive_u32"):
+            f = getattr(L, name)
+            f.argtypes = [vp, u64, u32p, vp, vp, sz, vp]
+            f.restype = i32
+        L.scan_u32_ex.argtypes = [vp, u64, i32, i32, i32, u32p, vp, vp, sz, vp]
+        L.scan_u32_ex.restype = i32
+        L.segscan_scratch_bytes.argtypes = [u64, u64]
+        L.segscan_scratch_bytes.restype = sz
+        L.segscan_u32.argtypes = [vp, vp, u64, u64, vp, vp, sz, vp]
+        L.segscan_u32.restype = i32
+        L.compact_scratch_bytes.argtypes = [u64]
+        L.compact_scratch_bytes.restype = sz
+        L.compact_flags_u32.argtypes = [vp, vp, u64, u32p, vp, vp, sz, vp]
+        L.compact_flags_u32.restype = i32
+        L.radix_scratch_bytes.argtypes = [u64, i32]
+        L.radix_scratch_bytes.restype = sz
+        L.radix_perm_u32.argtypes = [vp, vp, u64, i32, vp, sz, vp]
+        L.radix_perm_u32.restype = i32
+        L.copy_u32.argtypes = [vp, vp, u64, vp]
+        L.copy_u32.restype = i32
+        _lib = L
+    return _lib
+
+
+def version():
+    return lib().libscan_version().decode()
+
+
+def _check(status, what):
+    if status != OK:
+        raise LibscanError(status, what)
+
+
+def _dev_u32(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("%s must be int32 or uint32, got %s" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream), s
+
+
+# --------------------------------------------------------------------------
+# Scratch: one zero-initialised buffer per (device, stream), grown on demand.
+# The library keeps a buffer consistent between calls by itself, so a buffer
+# is initialised only when it is created.
+# --------------------------------------------------------------------------
+_scratch = {}
+_scratch_lock = threading.Lock()
+
+
+def _scratch_for(device, stream_obj, nbytes):
+    key = (device.index, stream_obj.cuda_stream)
+    with _scratch_lock:
+        buf = _scratch.get(key)
+        if buf is None or buf.numel() < nbytes:
+            size = max(nbytes, 2 * buf.numel() if buf is not None else 0, 1 << 16)
+            with torch.cuda.stream(stream_obj):
+                buf = torch.empty(size, dtype=torch.uint8, device=device)
+            _check(lib().libscan_scratch_init(ctypes.c_void_p(buf.data_ptr()), size,
+                                              ctypes.c_void_p(stream_obj.cuda_stream)),
+                   "libscan_scratch_init")
+            _scratch[key] = buf
+        return buf
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _total_args(want_total, total_dev):
+    host = ctypes.c_uint32(0)
+    hp = ctypes.pointer(host) if want_total else ctypes.POINTER(ctypes.c_uint32)()
+    if total_dev is not None:
+        _dev_u32(total_dev, "total_dev")
+    return host, hp
+
+
+# --------------------------------------------------------------------------
+# Entry points
+# --------------------------------------------------------------------------
+
+def scan_scratch_bytes(n):
+    return lib().scan_scratch_bytes(n)
+
+
+def scan_ex_scratch_bytes(n, algo=ALGO_AUTO, fork_depth=-1):
+    return lib().scan_ex_scratch_bytes(n, _algo(algo), fork_depth)
+
+
+def _algo(algo):
+    return _ALGOS[algo] if isinstance(algo, str) else int(algo)
+
+
+def scan_u32_ex(data, inclusive=False, algo="auto", fork_depth=-1, want_total=True,
+                total_dev=None, stream=None):
+    """In-place scan of `data` by the chosen algorithm; returns the total
+    (an int, after waiting for the stream) when want_total, else None."""
+    _dev_u32(data, "data")
+    a = _algo(algo)
+    sh, s = _stream_handle(data.device, stream)
+    need = lib().scan_ex_scratch_bytes(data.numel(), a, fork_depth)
+    scr = _scratch_for(data.device, s, need)
+    host, hp = _total_args(want_total, total_dev)
+    _check(lib().scan_u32_ex(_ptr(data), data.numel(), 1 if inclusive else 0, a, fork_depth, hp,
+                             _ptr(total_dev), _ptr(scr), scr.numel(), sh), "scan_u32_ex")
+    return int(host.value) if want_total else None
+
+
+def _scan(name, data, want_total, total_dev, stream):
+    _dev_u32(data, "data")
+    sh, s = _stream_handle(data.device, stream)
+    scr = _scratch_for(data.device, s, lib().scan_scratch_bytes(data.numel()))
+    host, hp = _total_args(want_total, total_dev)
+    _check(getattr(lib(), name)(_ptr(data), data.numel(), hp, _ptr(total_dev), _ptr(scr),
+                                scr.numel(), sh), name)
+    return int(host.value) if want_total else None
+
+
+def scan_exclusive_u32(data, want_total=True, total_dev=None, stream=None):
+    """data[j] <- data[0] + .. + data[j-1] in place (mod 2^32); returns the total."""
+    return _scan("scan_exclusive_u32", data, want_total, total_dev, stream)
+
+
+def scan_inclusive_u32(data, want_total=True, total_dev=None, stream=None):
+    """data[j] <- data[0] + .. + data[j] in place (mod 2^32); returns the total."""
+    return _scan("scan_inclusive_u32", data, want_total, total_dev, stream)
+
+
+def segscan_scratch_bytes(n, seg_len):
+    return lib().segscan_scratch_bytes(n, seg_len)
+
+
+def segscan_u32(inp, seg_len, out=None, seg_sums=True, stream=None):
+    """Inclusive scan restarted every seg_len entries, and the segment sums.
+
+    out: output tensor (default: a new one; pass `inp` for in place).
+    seg_sums: True for a new sums tensor, a tensor to fill, or None to skip.
+    Returns (out, sums)."""
+    _dev_u32(inp, "inp")
+    n = inp.numel()
+    if out is None:
+        out = torch.empty_like(inp)
+    _dev_u32(out, "out")
+    if out.numel() != n:
+        raise ValueError("out must have as many elements as inp")
+    if seg_len <= 0:
+        raise ValueError("seg_len must be positive")
+    if seg_sums is True:
+        seg_sums = torch.empty((n + seg_len - 1) // seg_len, dtype=inp.dtype, device=inp.device)
+    if seg_sums is not None:
+        _dev_u32(seg_sums, "seg_sums")
+        if seg_sums.numel() < (n + seg_len - 1) // seg_len:
+            raise ValueError("seg_sums needs ceil(n / seg_len) entries")
+    sh, s = _stream_handle(inp.device, stream)
+    scr = _scratch_for(inp.device, s, lib().segscan_scratch_bytes(n, seg_len))
+    _check(lib().segscan_u32(_ptr(inp), _ptr(out), n, seg_len, _ptr(seg_sums), _ptr(scr),
+                             scr.numel(), sh), "segscan_u32")
+    return out, seg_sums
+
+
+def compact_scratch_bytes(n):
+    return lib().compact_scratch_bytes(n)
+
+
+def compact_flags_u32(flags, out=None, want_count=True, count_dev=None, stream=None):
+    """Kept indices (non-zero flags) in order, -1 elsewhere; returns
+    (out, count) with count an int when want_count, else None."""
+    _dev_u32(flags, "flags")
+    n = flags.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=flags.device)
+    _dev_u32(out, "out")
+    if out.numel() != n:
+        raise ValueError("out must have as many elements as flags")
+    sh, s = _stream_handle(flags.device, stream)
+    scr = _scratch_for(flags.device, s, lib().compact_scratch_bytes(n))
+    host, hp = _total_args(want_count, count_dev)
+    _check(lib().compact_flags_u32(_ptr(flags), _ptr(out), n, hp, _ptr(count_dev), _ptr(scr),
+                                   scr.numel(), sh), "compact_flags_u32")
+    return out, (int(host.value) if want_count else None)
+
+
+def radix_scratch_bytes(n, bits_per_pass=1):
+    return lib().radix_scratch_bytes(n, bits_per_pass)
+
+
+def radix_perm_u32(keys, bits_per_pass=1, perm=None, stream=None):
+    """Stable LSB-first radix-sort permutation of u32 keys (gather form)."""
+    _dev_u32(keys, "keys")
+    n = keys.numel()
+    if perm is None:
+        perm = torch.empty(n, dtype=torch.int32, device=keys.device)
+    _dev_u32(perm, "perm")
+    if perm.numel() != n:
+        raise ValueError("perm must have as many elements as keys")
+    sh, s = _stream_handle(keys.device, stream)
+    scr = _scratch_for(keys.device, s, lib().radix_scratch_bytes(n, bits_per_pass))
+    _check(lib().radix_perm_u32(_ptr(keys), _ptr(perm), n, bits_per_pass, _ptr(scr), scr.numel(),
+                                sh), "radix_perm_u32")
+    return perm
+
+
+def copy_u32(src, dst, stream=None):
+    """dst <- src with the library's streaming copy kernel."""
+    _dev_u32(src, "src")
+    _dev_u32(dst, "dst")
+    if dst.numel() != src.numel():
+        raise ValueError("src and dst differ in size")
+    sh, _ = _stream_handle(src.device, stream)
+    _check(lib().copy_u32(_ptr(src), _ptr(dst), src.numel(), sh), "copy_u32")
+    return dst

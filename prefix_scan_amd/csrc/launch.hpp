@@ -1,0 +1,76 @@
+// launch.hpp -- host-side launchers of the libscan kernels and the layout of
+// the caller's scratch buffer.  Internal to the library; the C ABI is
+// include/libscan.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace libscan {
+
+// Tile shape of the streaming kernels: BLOCK threads (4 waves), V 16-byte
+// chunks per thread, so one tile is BLOCK * V * 4 u32.
+constexpr int kBlock = 256;
+constexpr int kChunks = 8;
+constexpr uint64_t kTile = (uint64_t)kBlock * kChunks * 4;
+
+// Scratch layout.  The caller's pointer is rounded up to 256 bytes; all
+// offsets below are from that aligned base.
+//   [0, 8)      ticket word of the chained carry {epoch, next tile}
+//   [64, 68)    total / count slot, used when the caller asks for the result
+//               on the host only
+//   [256, ...)  body: per-tile descriptors, block sums, staging rows
+constexpr size_t kScratchAlign = 256;
+constexpr size_t kHeaderBytes = 256;
+constexpr size_t kTotalSlotOffset = 64;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Virtual placement of an array: head = (address / 4) mod 4.
+inline uint32_t head_of(const void *p) { return (uint32_t)(((uintptr_t)p >> 2) & 3u); }
+
+inline uint64_t tiles_for(uint64_t n, uint32_t head, uint64_t tile)
+{
+    return (n + head + tile - 1) / tile;
+}
+
+struct Scratch {
+    uint8_t *base;       // aligned base
+    size_t bytes;        // usable bytes from base
+    uint64_t *ticket() const { return reinterpret_cast<uint64_t *>(base); }
+    uint32_t *total_slot() const { return reinterpret_cast<uint32_t *>(base + kTotalSlotOffset); }
+    uint8_t *body() const { return base + kHeaderBytes; }
+};
+
+// ---- scan (scan_kernels.hip) ----
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
+                                uint32_t *total_out, hipStream_t stream);
+size_t scan_lookback_body_bytes(uint64_t n, uint32_t head);
+
+// Three-pass scan at fork depth d (2^d blocks of bsize elements).
+hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, unsigned d,
+                                 const Scratch &s, uint32_t *total_out, hipStream_t stream);
+size_t scan_threepass_body_bytes(unsigned d);
+unsigned threepass_auto_depth(uint64_t n);
+unsigned floor_log2(uint64_t n);
+
+hipError_t launch_copy(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
+
+// ---- segmented scan (segscan_kernels.hip) ----
+hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
+                          uint32_t *seg_sums, const Scratch &s, hipStream_t stream);
+size_t segscan_body_bytes(uint64_t n, uint64_t seg_len);
+
+// ---- compaction (compact_kernels.hip) ----
+hipError_t launch_compact(const int32_t *flags, int32_t *out, uint64_t n, const Scratch &s,
+                          uint32_t *count_out, hipStream_t stream);
+size_t compact_body_bytes(uint64_t n);
+
+// ---- radix permutation (radix_kernels.hip) ----
+hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass,
+                        const Scratch &s, hipStream_t stream);
+size_t radix_body_bytes(uint64_t n, int bits_per_pass);
+
+}  // namespace libscan

@@ -1,0 +1,275 @@
+// libscan_api.hip -- the C ABI of include/libscan.h: argument checks,
+// scratch carving, kernel selection, and the optional host read-back of a
+// total or count.  All GPU work is enqueued on the caller's stream.
+#include "../../include/libscan.h"
+#include "launch.hpp"
+
+#include <stdio.h>
+#include <string.h>
+
+using namespace libscan;
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return LIBSCAN_OK;
+    g_last_hip = e;
+    return LIBSCAN_ERR_HIP;
+}
+
+bool misaligned4(const void *p) { return ((uintptr_t)p & 3u) != 0; }
+
+// Carve the aligned scratch view; false if the buffer cannot hold `body`
+// bytes after the header.
+bool carve(void *scratch, size_t scratch_bytes, size_t body, Scratch *out)
+{
+    const uintptr_t p = (uintptr_t)scratch;
+    const uintptr_t a = (p + kScratchAlign - 1) & ~(uintptr_t)(kScratchAlign - 1);
+    const size_t slack = (size_t)(a - p);
+    if (scratch_bytes < slack)
+        return false;
+    const size_t usable = scratch_bytes - slack;
+    if (usable < kHeaderBytes + body)
+        return false;
+    out->base = reinterpret_cast<uint8_t *>(a);
+    out->bytes = usable;
+    return true;
+}
+
+size_t with_header(size_t body) { return (kScratchAlign - 1) + kHeaderBytes + body; }
+
+// The three-pass depth: d = min(b, floor(log2 n), kMaxForkDepth), or the
+// automatic choice for b = -1.  Every depth gives the same bits, so the cap
+// (which bounds the grid and the sums array) never changes a result.
+constexpr unsigned kMaxForkDepth = 24;
+
+unsigned threepass_depth(uint64_t n, int fork_depth)
+{
+    const unsigned lg = floor_log2(n ? n : 1);
+    unsigned d = fork_depth < 0 ? threepass_auto_depth(n) : (unsigned)fork_depth;
+    if (d > lg)
+        d = lg;
+    if (d > kMaxForkDepth)
+        d = kMaxForkDepth;
+    return d;
+}
+
+// Copies the u32 result at `dev` to `host` and waits for the stream.
+int read_back(uint32_t *host, const uint32_t *dev, hipStream_t stream)
+{
+    hipError_t e = hipMemcpyAsync(host, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return hip_status(hipStreamSynchronize(stream));
+}
+
+// A zero result to report for an empty input.
+int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
+{
+    if (dev) {
+        hipError_t e = launch_fill_zero(dev, sizeof(uint32_t), stream);
+        if (e != hipSuccess)
+            return hip_status(e);
+    }
+    if (host) {
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return hip_status(e);
+        *host = 0;
+    }
+    return LIBSCAN_OK;
+}
+
+int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_depth,
+                uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
+                hipStream_t stream)
+{
+    if (algo < LIBSCAN_ALGO_AUTO || algo > LIBSCAN_ALGO_THREEPASS)
+        return LIBSCAN_ERR_ARG;
+    if (fork_depth < -1 || fork_depth > 40)
+        return LIBSCAN_ERR_ARG;
+    if (algo != LIBSCAN_ALGO_THREEPASS && fork_depth != -1)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(data) || misaligned4(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_zero(total_host, total_dev, stream);
+    if (!data || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes,
+               scan_ex_scratch_bytes(n, algo, fork_depth) - with_header(0), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *tot = total_dev ? total_dev : s.total_slot();
+    hipError_t e;
+    if (algo == LIBSCAN_ALGO_THREEPASS) {
+        const unsigned d = threepass_depth(n, fork_depth);
+        e = launch_scan_threepass(data, n, inclusive != 0, d, s, tot, stream);
+    } else {
+        e = launch_scan_lookback(data, n, inclusive != 0, s, tot, stream);
+    }
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (total_host)
+        return read_back(total_host, tot, stream);
+    return LIBSCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *libscan_strerror(int status)
+{
+    switch (status) {
+    case LIBSCAN_OK: return "ok";
+    case LIBSCAN_ERR_NULL: return "a required pointer is NULL";
+    case LIBSCAN_ERR_SIZE: return "n is beyond this entry point's limit";
+    case LIBSCAN_ERR_ARG: return "an argument is outside its documented range";
+    case LIBSCAN_ERR_SCRATCH: return "scratch buffer is smaller than the size query's answer";
+    case LIBSCAN_ERR_HIP: return hipGetErrorString(g_last_hip);
+    case LIBSCAN_ERR_ALIGN: return "a pointer is not 4-byte aligned";
+    default: return "unknown libscan status";
+    }
+}
+
+const char *libscan_version(void) { return "libscan 0.1 gfx950"; }
+
+int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (!scratch)
+        return scratch_bytes ? LIBSCAN_ERR_NULL : LIBSCAN_OK;
+    return hip_status(launch_fill_zero(scratch, scratch_bytes, stream));
+}
+
+size_t scan_scratch_bytes(uint64_t n)
+{
+    // Any head (0..3) fits: size for the largest.
+    return with_header(scan_lookback_body_bytes(n, 3));
+}
+
+size_t scan_ex_scratch_bytes(uint64_t n, int algo, int fork_depth)
+{
+    if (algo == LIBSCAN_ALGO_THREEPASS) {
+        return with_header(scan_threepass_body_bytes(threepass_depth(n, fork_depth)));
+    }
+    return scan_scratch_bytes(n);
+}
+
+int scan_exclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    return scan_common(data, n, 0, LIBSCAN_ALGO_LOOKBACK, -1, total_host, total_dev, scratch,
+                       scratch_bytes, stream);
+}
+
+int scan_inclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    return scan_common(data, n, 1, LIBSCAN_ALGO_LOOKBACK, -1, total_host, total_dev, scratch,
+                       scratch_bytes, stream);
+}
+
+int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_depth,
+                uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
+                hipStream_t stream)
+{
+    if (inclusive != 0 && inclusive != 1)
+        return LIBSCAN_ERR_ARG;
+    return scan_common(data, n, inclusive, algo, fork_depth, total_host, total_dev, scratch,
+                       scratch_bytes, stream);
+}
+
+size_t segscan_scratch_bytes(uint64_t n, uint64_t seg_len)
+{
+    return with_header(segscan_body_bytes(n, seg_len));
+}
+
+int segscan_u32(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
+                uint32_t *seg_sums, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (seg_len == 0)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(in) || misaligned4(out) || misaligned4(seg_sums))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return LIBSCAN_OK;
+    if (!in || !out || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, segscan_body_bytes(n, seg_len), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    return hip_status(launch_segscan(in, out, n, seg_len, seg_sums, s, stream));
+}
+
+size_t compact_scratch_bytes(uint64_t n) { return with_header(compact_body_bytes(n)); }
+
+int compact_flags_u32(const int32_t *flags, int32_t *out_idx, uint64_t n, uint32_t *count_host,
+                      uint32_t *count_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (n > LIBSCAN_MAX_N_INDEX)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(flags) || misaligned4(out_idx) || misaligned4(count_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_zero(count_host, count_dev, stream);
+    if (!flags || !out_idx || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, compact_body_bytes(n), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *cnt = count_dev ? count_dev : s.total_slot();
+    hipError_t e = launch_compact(flags, out_idx, n, s, cnt, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (count_host)
+        return read_back(count_host, cnt, stream);
+    return LIBSCAN_OK;
+}
+
+size_t radix_scratch_bytes(uint64_t n, int bits_per_pass)
+{
+    return with_header(radix_body_bytes(n, bits_per_pass));
+}
+
+int radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass,
+                   void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (bits_per_pass != 1 && bits_per_pass != 4)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N_INDEX)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(keys) || misaligned4(perm))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return LIBSCAN_OK;
+    if (!keys || !perm || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, radix_body_bytes(n, bits_per_pass), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    return hip_status(launch_radix(keys, perm, n, bits_per_pass, s, stream));
+}
+
+int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream)
+{
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(src) || misaligned4(dst))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return LIBSCAN_OK;
+    if (!src || !dst)
+        return LIBSCAN_ERR_NULL;
+    return hip_status(launch_copy(src, dst, n, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+// scan_kernels.hip -- device-wide U32 prefix sums for gfx950.
+//
+//  * scan_lookback_kernel: one pass over the array.  Each tile is loaded once
+//    into registers, scanned locally (thread, DPP wave, LDS across waves),
+//    gets its carry from the tiles before it through the chained-carry
+//    descriptors, and is stored in place: 4 bytes read and 4 written per
+//    element, the floor for an in-place scan.  The carry handoff is the
+//    ordered relay of cubecl-tile's Relay (turns taken in run order, a
+//    turn's data published at device scope before the next one reads it),
+//    with a look-back over published aggregates in place of strict turns.
+//  * reduce_blocks_kernel + scan_blocks_kernel: the three-pass scheme of
+//    bendlib "scan.bend source" (header comment, "Pass 1", "Pass 3",
+//    "Driver"): block sums, a scan of the sums (one workgroup below 2^12
+//    sums, else the same scheme at half the depth), then each block rescanned
+//    from its base.  12 bytes per element; kept as the comparison scheme and
+//    for the fork-depth knob.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+#include <stdlib.h>
+
+namespace libscan {
+
+// ---------------------------------------------------------------------------
+// Single-pass scan with chained carry.
+// ---------------------------------------------------------------------------
+template <int BLOCK, int V, bool INCL>
+__global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restrict__ abase,
+                                                              uint64_t vlo, uint64_t vhi,
+                                                              uint32_t ntiles, uint64_t *ticket,
+                                                              uint64_t *desc, uint32_t *total_out)
+{
+    constexpr int NW = BLOCK / kWave;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    __shared__ uint32_t s_wsum[NW][V];
+    __shared__ uint32_t s_tile, s_tag, s_carry;
+
+    if (threadIdx.x == 0) {
+        const TileTicket tk = draw_ticket(ticket, ntiles);
+        s_tile = tk.tile;
+        s_tag = tk.tag;
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint32_t tag = s_tag;
+    const uint64_t vstart = (uint64_t)tile * T;
+
+    u32x4 x[V];
+    load_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
+
+    uint32_t pre[V];
+    const uint32_t agg = tile_scan<BLOCK, V>(x, pre, s_wsum);
+
+    if (threadIdx.x < kWave) {
+        uint32_t excl = 0;
+        if (tile == 0) {
+            if (threadIdx.x == 0)
+                publish(desc, 0, tag, kStatusPrefix, agg);
+        } else {
+            if (threadIdx.x == 0)
+                publish(desc, tile, tag, kStatusAgg, agg);
+            excl = lookback(desc, tile, tag);
+            if (threadIdx.x == 0)
+                publish(desc, tile, tag, kStatusPrefix, excl + agg);
+        }
+        if (threadIdx.x == 0) {
+            s_carry = excl;
+            if (tile == ntiles - 1)
+                *total_out = excl + agg;
+        }
+    }
+    __syncthreads();
+    const uint32_t carry = s_carry;
+
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        x[k] = finish_chunk<INCL>(x[k], carry + pre[k]);
+    store_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
+}
+
+// ---------------------------------------------------------------------------
+// Three-pass scheme.
+// ---------------------------------------------------------------------------
+
+// Pass 1: workgroup i sums elements [i*bsize, min((i+1)*bsize, n)).
+template <int BLOCK, int V>
+__global__ __launch_bounds__(BLOCK) void reduce_blocks_kernel(const uint32_t *__restrict__ abase,
+                                                              uint32_t head, uint64_t n,
+                                                              uint64_t bsize,
+                                                              uint32_t *__restrict__ sums)
+{
+    constexpr int NW = BLOCK / kWave;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    __shared__ uint32_t s_part[NW];
+    const uint64_t i = blockIdx.x;
+    const uint64_t lo = i * bsize < n ? i * bsize : n;
+    const uint64_t hi = lo + bsize < n ? lo + bsize : n;
+    const uint64_t vlo = lo + head, vhi = hi + head;
+
+    uint32_t acc = 0;
+    for (uint64_t vs = vlo & ~3ull; vs < vhi; vs += T) {
+        u32x4 x[V];
+        load_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            acc += (x[k].x + x[k].y) + (x[k].z + x[k].w);
+    }
+    acc = wave_sum(acc);
+    if (lane_id() == 0)
+        s_part[threadIdx.x / kWave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            t += s_part[w];
+        sums[i] = t;
+    }
+}
+
+// Pass 2 (grid of one) and pass 3: workgroup i scans its block in place,
+// tile after tile, from base bases[i] (0 when bases is null).  When
+// total_out is set, workgroup 0 writes its final running sum there (the grid
+// is one workgroup in that case, so that is the total).
+template <int BLOCK, int V, bool INCL>
+__global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict__ abase,
+                                                            uint32_t head, uint64_t n,
+                                                            uint64_t bsize,
+                                                            const uint32_t *__restrict__ bases,
+                                                            uint32_t *total_out)
+{
+    constexpr int NW = BLOCK / kWave;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    __shared__ uint32_t s_wsum[2][NW][V];
+    const uint64_t i = blockIdx.x;
+    const uint64_t lo = i * bsize < n ? i * bsize : n;
+    const uint64_t hi = lo + bsize < n ? lo + bsize : n;
+    const uint64_t vlo = lo + head, vhi = hi + head;
+
+    uint32_t carry = bases ? bases[i] : 0u;
+    int buf = 0;
+    for (uint64_t vs = vlo & ~3ull; vs < vhi; vs += T) {
+        u32x4 x[V];
+        load_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
+        uint32_t pre[V];
+        const uint32_t agg = tile_scan<BLOCK, V>(x, pre, s_wsum[buf]);
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            x[k] = finish_chunk<INCL>(x[k], carry + pre[k]);
+        store_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
+        carry += agg;
+        buf ^= 1;
+    }
+    if (total_out && i == 0 && threadIdx.x == 0)
+        *total_out = carry;
+}
+
+// ---------------------------------------------------------------------------
+// Copy (bandwidth ceiling and counter calibration) and zero fill.
+// ---------------------------------------------------------------------------
+template <int BLOCK, int V>
+__global__ __launch_bounds__(BLOCK) void copy_kernel(const uint32_t *__restrict__ src,
+                                                     uint32_t *__restrict__ dst, uint64_t n)
+{
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    const uint64_t vstart = (uint64_t)blockIdx.x * T;
+    u32x4 x[V];
+    load_tile<BLOCK, V>(src, vstart, 0, n, x);
+    store_tile<BLOCK, V>(dst, vstart, 0, n, x);
+}
+
+__global__ void copy_scalar_kernel(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                   uint64_t n)
+{
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+__global__ void fill_zero_kernel(uint8_t *p, size_t bytes)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+// ---------------------------------------------------------------------------
+
+unsigned floor_log2(uint64_t n)
+{
+    unsigned lg = 0;
+    while (n > 1) {
+        n >>= 1;
+        ++lg;
+    }
+    return lg;
+}
+
+// Tile chunks per thread for the look-back scan: kChunks unless the
+// LIBSCAN_SCAN_CHUNKS environment variable picks 4 or 16 (a tuning knob; it
+// never changes a result).
+static int scan_chunks()
+{
+    static int v = [] {
+        const char *e = getenv("LIBSCAN_SCAN_CHUNKS");
+        int c = e ? atoi(e) : kChunks;
+        return (c == 4 || c == 8 || c == 16) ? c : kChunks;
+    }();
+    return v;
+}
+
+size_t scan_lookback_body_bytes(uint64_t n, uint32_t head)
+{
+    // Sized for the smallest tile (4 chunks per thread), the most tiles.
+    return (size_t)tiles_for(n, head, (uint64_t)kBlock * 4 * 4) * sizeof(uint64_t);
+}
+
+template <int V>
+static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
+                                  uint32_t *total_out, hipStream_t stream)
+{
+    constexpr uint64_t T = (uint64_t)kBlock * V * 4;
+    const uint32_t head = head_of(data);
+    const uint64_t ntiles = tiles_for(n, head, T);
+    uint32_t *abase = data - head;
+    uint64_t *desc = reinterpret_cast<uint64_t *>(s.body());
+    if (inclusive)
+        hipLaunchKernelGGL((scan_lookback_kernel<kBlock, V, true>), dim3((uint32_t)ntiles),
+                           dim3(kBlock), 0, stream, abase, (uint64_t)head, n + head,
+                           (uint32_t)ntiles, s.ticket(), desc, total_out);
+    else
+        hipLaunchKernelGGL((scan_lookback_kernel<kBlock, V, false>), dim3((uint32_t)ntiles),
+                           dim3(kBlock), 0, stream, abase, (uint64_t)head, n + head,
+                           (uint32_t)ntiles, s.ticket(), desc, total_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
+                                uint32_t *total_out, hipStream_t stream)
+{
+    switch (scan_chunks()) {
+    case 4: return scan_lookback_v<4>(data, n, inclusive, s, total_out, stream);
+    case 16: return scan_lookback_v<16>(data, n, inclusive, s, total_out, stream);
+    default: return scan_lookback_v<8>(data, n, inclusive, s, total_out, stream);
+    }
+}
+
+// The three-pass scheme's own tile: 256 threads x 4 chunks.
+constexpr int kTpChunks = 4;
+
+unsigned threepass_auto_depth(uint64_t n)
+{
+    // About 2048 blocks (8 per CU), each at least one tile.
+    const unsigned lg = floor_log2(n);
+    return lg > 12 ? (lg - 12 < 11 ? lg - 12 : 11) : 0;
+}
+
+size_t scan_threepass_body_bytes(unsigned d)
+{
+    const size_t s1 = round_up(((size_t)1 << d) * sizeof(uint32_t), kScratchAlign);
+    const size_t s2 = round_up(((size_t)1 << (d / 2)) * sizeof(uint32_t), kScratchAlign);
+    return s1 + s2;
+}
+
+static void launch_reduce(const uint32_t *data, uint64_t n, uint64_t blocks, uint64_t bsize,
+                          uint32_t *sums, hipStream_t stream)
+{
+    const uint32_t head = head_of(data);
+    hipLaunchKernelGGL((reduce_blocks_kernel<kBlock, kTpChunks>), dim3((uint32_t)blocks),
+                       dim3(kBlock), 0, stream, data - head, head, n, bsize, sums);
+}
+
+static void launch_scan_blocks(uint32_t *data, uint64_t n, uint64_t blocks, uint64_t bsize,
+                               const uint32_t *bases, uint32_t *total_out, bool inclusive,
+                               hipStream_t stream)
+{
+    const uint32_t head = head_of(data);
+    if (inclusive)
+        hipLaunchKernelGGL((scan_blocks_kernel<kBlock, kTpChunks, true>), dim3((uint32_t)blocks),
+                           dim3(kBlock), 0, stream, data - head, head, n, bsize, bases, total_out);
+    else
+        hipLaunchKernelGGL((scan_blocks_kernel<kBlock, kTpChunks, false>), dim3((uint32_t)blocks),
+                           dim3(kBlock), 0, stream, data - head, head, n, bsize, bases, total_out);
+}
+
+hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, unsigned d,
+                                 const Scratch &s, uint32_t *total_out, hipStream_t stream)
+{
+    const uint64_t blocks = 1ull << d;
+    const uint64_t bsize = (n + blocks - 1) / blocks;
+    uint32_t *sums = reinterpret_cast<uint32_t *>(s.body());
+    uint32_t *sums2 = reinterpret_cast<uint32_t *>(
+        s.body() + round_up(blocks * sizeof(uint32_t), kScratchAlign));
+
+    // Pass 1: each block's sum.
+    launch_reduce(data, n, blocks, bsize, sums, stream);
+    // Pass 2: the sums become their exclusive scan, and the total.
+    if (d < 12) {
+        launch_scan_blocks(sums, blocks, 1, blocks, nullptr, total_out, false, stream);
+    } else {
+        const uint64_t b2 = 1ull << (d / 2);
+        const uint64_t bs2 = blocks / b2;
+        launch_reduce(sums, blocks, b2, bs2, sums2, stream);
+        launch_scan_blocks(sums2, b2, 1, b2, nullptr, total_out, false, stream);
+        launch_scan_blocks(sums, blocks, b2, bs2, sums2, nullptr, false, stream);
+    }
+    // Pass 3: each block rescanned in place from its base.
+    launch_scan_blocks(data, n, blocks, bsize, sums, nullptr, inclusive, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream)
+{
+    constexpr int V = 8;
+    constexpr uint64_t T = (uint64_t)kBlock * V * 4;
+    if (head_of(src) == 0 && head_of(dst) == 0) {
+        const uint64_t grid = (n + T - 1) / T;
+        hipLaunchKernelGGL((copy_kernel<kBlock, V>), dim3((uint32_t)grid), dim3(kBlock), 0, stream,
+                           src, dst, n);
+    } else {
+        hipLaunchKernelGGL(copy_scalar_kernel, dim3(4096), dim3(256), 0, stream, src, dst, n);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream)
+{
+    uint64_t grid = (bytes + 255) / 256;
+    if (grid > 4096)
+        grid = 4096;
+    if (grid == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((uint32_t)grid), dim3(256), 0, stream,
+                       static_cast<uint8_t *>(p), bytes);
+    return hipGetLastError();
+}
+
+}  // namespace libscan
