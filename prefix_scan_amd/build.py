@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall",
     # No packed fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep single-lane atomics as written: the wave-aggregating rewrite makes
+    # the ticket draw wait for every load issued before it.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

@@ -152,17 +152,64 @@ __device__ __forceinline__ void store4_guarded(uint32_t *abase, uint64_t q, u32x
     if (v0 + 3 >= vlo && v0 + 3 < vhi) abase[v0 + 3] = v.w;
 }
 
+// A tile's first chunk as a wave-uniform pointer (an SGPR pair): each lane
+// then adds only a 32-bit offset, so all V loads or stores of a tile share
+// one address register instead of holding V 64-bit addresses.
+__device__ __forceinline__ u32x4 *uniform_tile_ptr(const uint32_t *abase, uint64_t vstart)
+{
+    const uint64_t q = vstart / 4;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)q);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(q >> 32));
+    return const_cast<u32x4 *>(reinterpret_cast<const u32x4 *>(abase)) + (((uint64_t)hi << 32) | lo);
+}
+
+// A tile known to lie wholly inside the valid range.
+template <int BLOCK, int V>
+__device__ __forceinline__ void load_tile_full(const uint32_t *abase, uint64_t vstart,
+                                               u32x4 (&x)[V])
+{
+    const u32x4 *t = uniform_tile_ptr(abase, vstart);
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        x[k] = __builtin_nontemporal_load(t + (k * BLOCK + threadIdx.x));
+}
+
+template <int BLOCK, int V>
+__device__ __forceinline__ void store_tile_full(uint32_t *abase, uint64_t vstart,
+                                                const u32x4 (&x)[V])
+{
+    u32x4 *t = uniform_tile_ptr(abase, vstart);
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        __builtin_nontemporal_store(x[k], t + (k * BLOCK + threadIdx.x));
+}
+
+// The loads of a whole tile at vstart, or -- when `real` is false -- the
+// same number of loads of one 16-byte stand-in line.  The address is
+// selected per load, so the instruction stream is the same either way: the
+// compiler's count of outstanding loads then never depends on a branch.
+template <int BLOCK, int V>
+__device__ __forceinline__ void load_tile_full_or(const uint32_t *abase, uint64_t vstart,
+                                                  const uint32_t *line, bool real,
+                                                  u32x4 (&x)[V])
+{
+    const u32x4 *tile = uniform_tile_ptr(abase, vstart);
+    const u32x4 *alt = reinterpret_cast<const u32x4 *>(line);
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        x[k] = __builtin_nontemporal_load(real ? tile + (k * BLOCK + threadIdx.x) : alt);
+}
+
+// Any tile: whole tiles take the plain path, partial ones per-element guards.
 template <int BLOCK, int V>
 __device__ __forceinline__ void load_tile(const uint32_t *abase, uint64_t vstart, uint64_t vlo,
                                           uint64_t vhi, u32x4 (&x)[V])
 {
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    const uint64_t q0 = vstart / 4 + threadIdx.x;
     if (vstart >= vlo && vstart + T <= vhi) {
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            x[k] = load4(abase, q0 + (uint64_t)k * BLOCK);
+        load_tile_full<BLOCK, V>(abase, vstart, x);
     } else {
+        const uint64_t q0 = vstart / 4 + threadIdx.x;
 #pragma unroll
         for (int k = 0; k < V; ++k)
             x[k] = load4_guarded(abase, q0 + (uint64_t)k * BLOCK, vlo, vhi);
@@ -174,12 +221,10 @@ __device__ __forceinline__ void store_tile(uint32_t *abase, uint64_t vstart, uin
                                            uint64_t vhi, const u32x4 (&x)[V])
 {
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    const uint64_t q0 = vstart / 4 + threadIdx.x;
     if (vstart >= vlo && vstart + T <= vhi) {
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            store4(abase, q0 + (uint64_t)k * BLOCK, x[k]);
+        store_tile_full<BLOCK, V>(abase, vstart, x);
     } else {
+        const uint64_t q0 = vstart / 4 + threadIdx.x;
 #pragma unroll
         for (int k = 0; k < V; ++k)
             store4_guarded(abase, q0 + (uint64_t)k * BLOCK, x[k], vlo, vhi);
@@ -187,72 +232,93 @@ __device__ __forceinline__ void store_tile(uint32_t *abase, uint64_t vstart, uin
 }
 
 // ---------------------------------------------------------------------------
-// Tile-local scan.  In: x[k] = the thread's chunks.  Out: x[k] becomes the
-// inclusive scan inside the chunk, pre[k] the sum of every element of the
-// tile before chunk k of this thread, and the return value the tile's sum.
-// s_wsum is LDS of NW x V words; the function ends with the barrier that
-// makes it readable, so a caller reusing s_wsum for the next tile must place
-// a barrier (or use a second buffer) before the next call.
+// Tile-local scan, in three phases around the caller's two barriers.
+//
+// Element order in a tile is (chunk k, thread, element), so the tile is V
+// runs of BLOCK chunks.  Phase 1 scans each chunk in the thread and each
+// run across the wave (DPP); lane 63 leaves the wave's total for run k in
+// cell k*NW + wave of s_cell -- the cells in tile order.  After a barrier,
+// phase 2 (one wave) turns the NW*V cells into their exclusive scan and
+// returns the tile's sum.  After a second barrier, phase 3 adds to every
+// element its cell's prefix, its lane's prefix inside the wave, and the
+// carry from the tiles before.  Each thread reads only V cells, so the LDS
+// values never crowd the registers that hold the tile.
 // ---------------------------------------------------------------------------
 template <int BLOCK, int V>
-__device__ __forceinline__ uint32_t tile_scan(u32x4 (&x)[V], uint32_t (&pre)[V],
-                                              uint32_t (*s_wsum)[V])
-{
-    constexpr int NW = BLOCK / kWave;
-    const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / kWave;
-    uint32_t c[V], w[V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        x[k].y += x[k].x;
-        x[k].z += x[k].y;
-        x[k].w += x[k].z;
-        c[k] = x[k].w;
-    }
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-        w[k] = wave_incl_add(c[k]);
-    if (lane == kWave - 1) {
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            s_wsum[wave][k] = w[k];
-    }
-    __syncthreads();
-    uint32_t acc = 0;
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        uint32_t before = 0, tot = 0;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const uint32_t s = s_wsum[ww][k];
-            before += (ww < (int)wave) ? s : 0u;
-            tot += s;
-        }
-        pre[k] = acc + before + (w[k] - c[k]);
-        acc += tot;
-    }
-    return acc;
-}
+struct TileScan {
+    static constexpr int NW = BLOCK / kWave;
+    static constexpr int NCELL = NW * V;
+    static constexpr int CELLS_PER_LANE = (NCELL + kWave - 1) / kWave;
 
-// Out chunk from the chunk-inclusive scan `xi` and the sum `base` of every
-// element before the chunk.
-template <bool INCL>
-__device__ __forceinline__ u32x4 finish_chunk(u32x4 xi, uint32_t base)
-{
-    u32x4 r;
-    if (INCL) {
-        r.x = base + xi.x;
-        r.y = base + xi.y;
-        r.z = base + xi.z;
-        r.w = base + xi.w;
-    } else {
-        r.x = base;
-        r.y = base + xi.x;
-        r.z = base + xi.y;
-        r.w = base + xi.z;
+    // Phase 1.  x[k] becomes the inclusive scan inside its chunk; w[k] the
+    // inclusive wave scan of the chunk sums.
+    __device__ static __forceinline__ void local(u32x4 (&x)[V], uint32_t (&w)[V],
+                                                 uint32_t *s_cell)
+    {
+        const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            x[k].y += x[k].x;
+            x[k].z += x[k].y;
+            x[k].w += x[k].z;
+            w[k] = wave_incl_add(x[k].w);
+        }
+        if (lane_id() == kWave - 1) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                s_cell[k * NW + wave] = w[k];
+        }
     }
-    return r;
-}
+
+    // Phase 2, called by one whole wave after a barrier: the cells become
+    // their exclusive scan; returns the tile's sum in every lane.
+    __device__ static __forceinline__ uint32_t cells(uint32_t *s_cell)
+    {
+        const uint32_t lane = lane_id();
+        uint32_t v[CELLS_PER_LANE];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < CELLS_PER_LANE; ++j) {
+            const uint32_t c = lane * CELLS_PER_LANE + j;
+            v[j] = c < (uint32_t)NCELL ? s_cell[c] : 0u;
+            mine += v[j];
+        }
+        const uint32_t incl = wave_incl_add(mine);
+        uint32_t run = incl - mine;
+#pragma unroll
+        for (int j = 0; j < CELLS_PER_LANE; ++j) {
+            const uint32_t c = lane * CELLS_PER_LANE + j;
+            if (c < (uint32_t)NCELL)
+                s_cell[c] = run;
+            run += v[j];
+        }
+        return wave_bcast_last(incl);
+    }
+
+    // Phase 3, after the barrier that follows phase 2: the tile's outputs
+    // (exclusive or inclusive) plus `carry`.
+    template <bool INCL>
+    __device__ static __forceinline__ void apply(u32x4 (&x)[V], const uint32_t (&w)[V],
+                                                 const uint32_t *s_cell, uint32_t carry)
+    {
+        const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t base = carry + s_cell[k * NW + wave] + (w[k] - x[k].w);
+            if (INCL) {
+                x[k].x += base;
+                x[k].y += base;
+                x[k].z += base;
+                x[k].w += base;
+            } else {
+                x[k].w = base + x[k].z;
+                x[k].z = base + x[k].y;
+                x[k].y = base + x[k].x;
+                x[k].x = base;
+            }
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Chained carry between tiles (decoupled look-back).
@@ -300,38 +366,70 @@ __device__ __forceinline__ void publish(uint64_t *desc, uint32_t tile, uint32_t 
     __hip_atomic_store(desc + tile, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One look-back window: lane l holds the raw descriptor of tile base - l.
+// Lanes before tile 0 read descriptor 0 and count as PREFIX 0.  The word is
+// decoded only where it is used, so a caller can issue the load early and
+// wait for it late.
+struct LookbackWindow {
+    uint64_t d;
+    bool before_start;
+};
+
+__device__ __forceinline__ LookbackWindow lookback_load(const uint64_t *desc, int64_t base)
+{
+    const int64_t pi = base - (int64_t)lane_id();
+    LookbackWindow w;
+    w.before_start = pi < 0;
+    w.d = __hip_atomic_load(desc + (pi < 0 ? 0 : pi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return w;
+}
+
+// Folds one window into `excl`.  Returns 2 when a PREFIX was reached (excl
+// is the carry), 1 when all 64 tiles held aggregates (excl grew; look
+// further back), 0 when a tile before the nearest PREFIX is not ready yet
+// (nothing folded; read the same window again).
+__device__ __forceinline__ int lookback_fold(const LookbackWindow &w, uint32_t tag,
+                                             uint32_t &excl)
+{
+    const uint32_t hi = (uint32_t)(w.d >> 32);
+    const uint32_t st = w.before_start ? kStatusPrefix : (((hi & ~3u) == tag) ? (hi & 3u) : 0u);
+    const uint32_t val = w.before_start ? 0u : (uint32_t)w.d;
+    const uint64_t pref = ballot(st == kStatusPrefix);
+    const uint64_t wait = ballot(st == 0);
+    const uint32_t p = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
+    const uint64_t upto = (p >= 63) ? ~0ull : ((2ull << p) - 1);
+    if (wait & upto)
+        return 0;
+    excl += wave_sum(lane_id() <= p ? val : 0u);
+    return pref ? 2 : 1;
+}
+
 // Called by one whole wave.  Returns, in every lane, the sum of the values
-// of tiles tile-1, tile-2, ... back to and including the nearest PREFIX
-// (tiles before 0 count as PREFIX 0): the tile's exclusive carry.  Each step
-// inspects 64 predecessors at once, lane l looking at tile base - l.
+// of tiles tile-1, tile-2, ... back to and including the nearest PREFIX: the
+// tile's exclusive carry.  Each step inspects 64 predecessors at once; `w` is
+// the window for base = tile - 1, which a caller may have loaded early.  The
+// first window is folded outside the retry loop, so waiting for it does not
+// wait for loads the caller issued after it.
+__device__ __forceinline__ uint32_t lookback_from(const uint64_t *desc, uint32_t tile,
+                                                  uint32_t tag, LookbackWindow w)
+{
+    uint32_t excl = 0;
+    int r = lookback_fold(w, tag, excl);
+    int64_t base = (int64_t)tile - 1;
+    while (r != 2) {
+        if (r == 1)
+            base -= kWave;
+        else
+            __builtin_amdgcn_s_sleep(1);
+        w = lookback_load(desc, base);
+        r = lookback_fold(w, tag, excl);
+    }
+    return excl;
+}
+
 __device__ __forceinline__ uint32_t lookback(const uint64_t *desc, uint32_t tile, uint32_t tag)
 {
-    const uint32_t lane = lane_id();
-    uint32_t excl = 0;
-    int64_t base = (int64_t)tile - 1;
-    for (;;) {
-        const int64_t pi = base - (int64_t)lane;
-        uint32_t st = kStatusPrefix, val = 0;
-        if (pi >= 0) {
-            const uint64_t d = __hip_atomic_load(desc + pi, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t hi = (uint32_t)(d >> 32);
-            st = ((hi & ~3u) == tag) ? (hi & 3u) : 0u;
-            val = (uint32_t)d;
-        }
-        const uint64_t pref = ballot(st == kStatusPrefix);
-        const uint64_t wait = ballot(st == 0);
-        const uint32_t p = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
-        const uint64_t upto = (p >= 63) ? ~0ull : ((2ull << p) - 1);
-        if (wait & upto) {
-            __builtin_amdgcn_s_sleep(1);
-            continue;
-        }
-        excl += wave_sum(lane <= p ? val : 0u);
-        if (pref)
-            return excl;
-        base -= kWave;
-    }
+    return lookback_from(desc, tile, tag, lookback_load(desc, (int64_t)tile - 1));
 }
 
 }  // namespace libscan

@@ -9,17 +9,22 @@
 
 namespace libscan {
 
-// Tile shape of the streaming kernels: BLOCK threads (4 waves), V 16-byte
-// chunks per thread, so one tile is BLOCK * V * 4 u32.
+// Tile shape of the single-pass scan: BLOCK threads (4 waves), V 16-byte
+// chunks per thread, so one tile is BLOCK * V * 4 u32 (128 KiB at V = 32).
+// Large tiles keep the number of carry hand-offs, each a wait on the
+// slowest of the tiles before, small against the bytes each moves.
 constexpr int kBlock = 256;
-constexpr int kChunks = 8;
+constexpr int kChunks = 32;
 constexpr uint64_t kTile = (uint64_t)kBlock * kChunks * 4;
 
 // Scratch layout.  The caller's pointer is rounded up to 256 bytes; all
 // offsets below are from that aligned base.
 //   [0, 8)      ticket word of the chained carry {epoch, next tile}
+//   [8, 12)     exit counter of the persistent kernels
 //   [64, 68)    total / count slot, used when the caller asks for the result
 //               on the host only
+//   [128, 144)  a line the persistent kernels read in place of a tile when
+//               they have nothing to prefetch (its contents are never used)
 //   [256, ...)  body: per-tile descriptors, block sums, staging rows
 constexpr size_t kScratchAlign = 256;
 constexpr size_t kHeaderBytes = 256;
@@ -39,13 +44,17 @@ struct Scratch {
     uint8_t *base;       // aligned base
     size_t bytes;        // usable bytes from base
     uint64_t *ticket() const { return reinterpret_cast<uint64_t *>(base); }
+    uint32_t *exits() const { return reinterpret_cast<uint32_t *>(base + 8); }
     uint32_t *total_slot() const { return reinterpret_cast<uint32_t *>(base + kTotalSlotOffset); }
     uint8_t *body() const { return base + kHeaderBytes; }
+    const uint32_t *dummy_line() const { return reinterpret_cast<const uint32_t *>(base + 128); }
 };
 
 // ---- scan (scan_kernels.hip) ----
-hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
-                                uint32_t *total_out, hipStream_t stream);
+// persistent: the pipelined grid-filling kernel; else one workgroup per tile.
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+                                const Scratch &s, uint32_t *total_out, hipStream_t stream);
+int resident_grid(const void *kernel, int block);
 size_t scan_lookback_body_bytes(uint64_t n, uint32_t head);
 
 // Three-pass scan at fork depth d (2^d blocks of bsize elements).

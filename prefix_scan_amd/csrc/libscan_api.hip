@@ -88,7 +88,7 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
                 uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
                 hipStream_t stream)
 {
-    if (algo < LIBSCAN_ALGO_AUTO || algo > LIBSCAN_ALGO_THREEPASS)
+    if (algo < LIBSCAN_ALGO_AUTO || algo > LIBSCAN_ALGO_LOOKBACK_PIPELINED)
         return LIBSCAN_ERR_ARG;
     if (fork_depth < -1 || fork_depth > 40)
         return LIBSCAN_ERR_ARG;
@@ -112,7 +112,8 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
         const unsigned d = threepass_depth(n, fork_depth);
         e = launch_scan_threepass(data, n, inclusive != 0, d, s, tot, stream);
     } else {
-        e = launch_scan_lookback(data, n, inclusive != 0, s, tot, stream);
+        e = launch_scan_lookback(data, n, inclusive != 0, algo == LIBSCAN_ALGO_LOOKBACK_PIPELINED,
+                                 s, tot, stream);
     }
     if (e != hipSuccess)
         return hip_status(e);

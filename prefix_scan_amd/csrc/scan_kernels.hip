@@ -19,6 +19,11 @@
 
 #include <stdlib.h>
 
+#include <map>
+#include <type_traits>
+#include <mutex>
+#include <utility>
+
 namespace libscan {
 
 // ---------------------------------------------------------------------------
@@ -30,9 +35,9 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
                                                               uint32_t ntiles, uint64_t *ticket,
                                                               uint64_t *desc, uint32_t *total_out)
 {
-    constexpr int NW = BLOCK / kWave;
+    using TS = TileScan<BLOCK, V>;
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    __shared__ uint32_t s_wsum[NW][V];
+    __shared__ uint32_t s_cell[TS::NCELL];
     __shared__ uint32_t s_tile, s_tag, s_carry;
 
     if (threadIdx.x == 0) {
@@ -46,12 +51,13 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
     const uint64_t vstart = (uint64_t)tile * T;
 
     u32x4 x[V];
+    uint32_t w[V];
     load_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
-
-    uint32_t pre[V];
-    const uint32_t agg = tile_scan<BLOCK, V>(x, pre, s_wsum);
+    TS::local(x, w, s_cell);
+    __syncthreads();
 
     if (threadIdx.x < kWave) {
+        const uint32_t agg = TS::cells(s_cell);
         uint32_t excl = 0;
         if (tile == 0) {
             if (threadIdx.x == 0)
@@ -70,12 +76,213 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
         }
     }
     __syncthreads();
-    const uint32_t carry = s_carry;
-
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-        x[k] = finish_chunk<INCL>(x[k], carry + pre[k]);
+    TS::template apply<INCL>(x, w, s_cell, s_carry);
     store_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent, software-pipelined variant of the same single-pass scan.
+//
+// A grid sized to fill the GPU once; every workgroup draws tile numbers from
+// the ticket and processes its tiles in increasing order.  While tile `cur`
+// is scanned and waits for its carry, the loads of the workgroup's next tile
+// are already in flight and the ticket for the one after is being drawn, so
+// the carry latency overlaps HBM traffic instead of idling the CU.
+//
+// Termination: a workgroup stops drawing at its first number >= ntiles and
+// then counts itself out on the exit counter; the last one out resets the
+// ticket (counter 0, epoch + 1) and the exit counter for the next launch.
+// Progress: a workgroup holds at most three tiles (cur < nxt < nn) and
+// publishes them in that order; every tile waits only on smaller tiles, so
+// the smallest unpublished tile can always advance.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+
+template <int BLOCK, int V, bool INCL>
+__global__ __launch_bounds__(BLOCK) void scan_persistent_kernel(uint32_t *__restrict__ abase,
+                                                                uint64_t vlo, uint64_t vhi,
+                                                                uint32_t ntiles, uint64_t *ticket,
+                                                                uint32_t *exits, uint64_t *desc,
+                                                                const uint32_t *dummy,
+                                                                uint32_t *total_out)
+{
+    using TS = TileScan<BLOCK, V>;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    constexpr int kDrawer = BLOCK - kWave;       // lane 0 of the last wave
+    // Two cell buffers, alternating tile by tile: a wave may start the next
+    // tile's phase 1 while a slower one still reads this tile's cells.
+    __shared__ uint32_t s_cell[2][TS::NCELL];
+    __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag, s_carry;
+    int buf = 0;
+
+    auto draw_raw = [&]() -> uint64_t {
+        return __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // Draws after the first need only the counter: a 32-bit add on the low
+    // half of the ticket word (it never carries into the epoch, since a
+    // launch draws fewer than 2^32 numbers).
+    auto draw_num = [&]() -> uint32_t {
+        return __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(ticket), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto tile_of = [&](uint64_t raw) -> uint32_t {
+        return (uint32_t)raw < ntiles ? (uint32_t)raw : kNoTile;
+    };
+    uint32_t epoch = 0;
+    // Called by kDrawer once the workgroup has drawn its last number.
+    auto check_out = [&]() {
+        const uint32_t before =
+            __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before == gridDim.x - 1) {
+            __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ticket, (uint64_t)(epoch + 1) << 32, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    if (threadIdx.x == kDrawer) {
+        const uint64_t o1 = draw_raw();
+        epoch = (uint32_t)(o1 >> 32);
+        const uint32_t c = tile_of(o1);
+        const uint32_t x = (c != kNoTile) ? tile_of(draw_num()) : kNoTile;
+        s_cur = c;
+        s_nxt = x;
+        s_tag = (epoch & 0x3FFFFFFFu) << 2;
+        if (x == kNoTile)
+            check_out();
+    }
+    __syncthreads();
+    uint32_t cur = s_cur, nxt = s_nxt;
+    const uint32_t tag = s_tag;
+    if (cur == kNoTile)
+        return;
+
+    auto whole = [&](uint32_t t) -> bool {
+        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    };
+
+    // Wave 0, after the first barrier: the tile's sum, published as an
+    // aggregate (or as the prefix, for tile 0), and the first look-back
+    // window requested.
+    auto publish_first = [&](uint32_t agg) -> LookbackWindow {
+        LookbackWindow w0{0ull, true};
+        if (cur == 0) {
+            if (threadIdx.x == 0)
+                publish(desc, 0, tag, kStatusPrefix, agg);
+        } else {
+            if (threadIdx.x == 0)
+                publish(desc, cur, tag, kStatusAgg, agg);
+            w0 = lookback_load(desc, (int64_t)cur - 1);
+        }
+        return w0;
+    };
+    // Wave 0: folds `cur`'s carry and records it (and, on the last tile, the
+    // total) for the workgroup.
+    auto carry_of = [&](uint32_t agg, const LookbackWindow &w0) {
+        uint32_t excl = 0;
+        if (cur != 0) {
+            excl = lookback_from(desc, cur, tag, w0);
+            if (threadIdx.x == 0)
+                publish(desc, cur, tag, kStatusPrefix, excl + agg);
+        }
+        if (threadIdx.x == 0) {
+            s_carry = excl;
+            if (cur == ntiles - 1)
+                *total_out = excl + agg;
+        }
+    };
+    auto settle_draw = [&](bool drawing, uint32_t nn_raw) {
+        if (threadIdx.x == kDrawer) {
+            const uint32_t nn = drawing ? tile_of(nn_raw) : kNoTile;
+            s_nn = nn;
+            if (drawing && nn == kNoTile)
+                check_out();
+        }
+    };
+
+    // A partial tile (the first or the last of the array): guarded loads and
+    // stores, no prefetch.
+    auto slow_step = [&](u32x4 (&xa)[V]) {
+        uint32_t w[V];
+        load_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, xa);
+        TS::local(xa, w, s_cell[buf]);
+        const bool drawing = (threadIdx.x == kDrawer) && nxt != kNoTile;
+        const uint32_t nn_raw = drawing ? draw_num() : 0u;
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const uint32_t agg = TS::cells(s_cell[buf]);
+            carry_of(agg, publish_first(agg));
+        }
+        settle_draw(drawing, nn_raw);
+        __syncthreads();
+        const uint32_t nn = s_nn;
+        TS::template apply<INCL>(xa, w, s_cell[buf], s_carry);
+        store_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, xa);
+        buf ^= 1;
+        cur = nxt;
+        nxt = nn;
+    };
+
+    // One pipeline step over a whole tile: finish `cur` from registers xa
+    // while the loads of `nxt` land in yb.
+    //
+    // Order of issue, chosen so that every wait leaves the prefetch in
+    // flight: the tile is scanned first (its only wait is for xa); the
+    // aggregate is published and the first look-back window requested; the
+    // ticket draw goes out; then the prefetch.  Waiting for the window or
+    // the draw then needs only the operations issued before the prefetch.
+    // The prefetch is issued unconditionally -- when there is no whole next
+    // tile it reads a 16-byte line of scratch into yb instead -- so the
+    // number of operations between a load and its first use never depends on
+    // a branch.  Returns whether yb holds the next tile; `cur` and `nxt`
+    // advance.
+    auto step = [&](u32x4 (&xa)[V], u32x4 (&yb)[V]) -> bool {
+        uint32_t w[V];
+        TS::local(xa, w, s_cell[buf]);
+        __syncthreads();
+        uint32_t agg = 0;
+        LookbackWindow w0{0ull, true};
+        if (threadIdx.x < kWave) {
+            agg = TS::cells(s_cell[buf]);
+            w0 = publish_first(agg);
+        }
+        const bool drawing = (threadIdx.x == kDrawer) && nxt != kNoTile;
+        const uint32_t nn_raw = drawing ? draw_num() : 0u;
+        const bool prefetch = nxt != kNoTile && whole(nxt);
+        load_tile_full_or<BLOCK, V>(abase, prefetch ? (uint64_t)nxt * T : 0, dummy, prefetch, yb);
+
+        if (threadIdx.x < kWave)
+            carry_of(agg, w0);
+        settle_draw(drawing, nn_raw);
+        __syncthreads();
+        const uint32_t nn = s_nn;
+        TS::template apply<INCL>(xa, w, s_cell[buf], s_carry);
+        store_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, xa);
+        buf ^= 1;
+        cur = nxt;
+        nxt = nn;
+        return prefetch;
+    };
+
+    u32x4 a[V], b[V];
+    for (;;) {
+        while (cur != kNoTile && !whole(cur))
+            slow_step(a);
+        if (cur == kNoTile)
+            break;
+        load_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, a);
+        // The first step is peeled so that every step inside the loop is
+        // entered with the same operations outstanding; two steps per trip
+        // swap the buffers' roles without register copies.
+        if (step(a, b)) {
+            for (;;) {
+                if (!step(b, a))
+                    break;
+                if (!step(a, b))
+                    break;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -129,9 +336,10 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict
                                                             const uint32_t *__restrict__ bases,
                                                             uint32_t *total_out)
 {
-    constexpr int NW = BLOCK / kWave;
+    using TS = TileScan<BLOCK, V>;
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    __shared__ uint32_t s_wsum[2][NW][V];
+    __shared__ uint32_t s_cell[2][TS::NCELL];
+    __shared__ uint32_t s_agg;
     const uint64_t i = blockIdx.x;
     const uint64_t lo = i * bsize < n ? i * bsize : n;
     const uint64_t hi = lo + bsize < n ? lo + bsize : n;
@@ -141,14 +349,19 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict
     int buf = 0;
     for (uint64_t vs = vlo & ~3ull; vs < vhi; vs += T) {
         u32x4 x[V];
+        uint32_t w[V];
         load_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
-        uint32_t pre[V];
-        const uint32_t agg = tile_scan<BLOCK, V>(x, pre, s_wsum[buf]);
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            x[k] = finish_chunk<INCL>(x[k], carry + pre[k]);
+        TS::local(x, w, s_cell[buf]);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const uint32_t agg = TS::cells(s_cell[buf]);
+            if (threadIdx.x == 0)
+                s_agg = agg;
+        }
+        __syncthreads();
+        TS::template apply<INCL>(x, w, s_cell[buf], carry);
         store_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
-        carry += agg;
+        carry += s_agg;
         buf ^= 1;
     }
     if (total_out && i == 0 && threadIdx.x == 0)
@@ -198,6 +411,32 @@ unsigned floor_log2(uint64_t n)
     return lg;
 }
 
+// Workgroups of `block` threads of `kernel` that the current device holds at
+// once: its CU count times the occupancy per CU.  Cached per device and
+// kernel.
+int resident_grid(const void *kernel, int block)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end())
+        return it->second;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, block, 0) != hipSuccess ||
+        per <= 0)
+        per = 1;
+    const int grid = cus * per;
+    cache[{dev, kernel}] = grid;
+    return grid;
+}
+
 // Tile chunks per thread for the look-back scan: kChunks unless the
 // LIBSCAN_SCAN_CHUNKS environment variable picks 4 or 16 (a tuning knob; it
 // never changes a result).
@@ -206,7 +445,7 @@ static int scan_chunks()
     static int v = [] {
         const char *e = getenv("LIBSCAN_SCAN_CHUNKS");
         int c = e ? atoi(e) : kChunks;
-        return (c == 4 || c == 8 || c == 16) ? c : kChunks;
+        return (c == 4 || c == 8 || c == 16 || c == 32) ? c : kChunks;
     }();
     return v;
 }
@@ -218,32 +457,48 @@ size_t scan_lookback_body_bytes(uint64_t n, uint32_t head)
 }
 
 template <int V>
-static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
-                                  uint32_t *total_out, hipStream_t stream)
+static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+                                  const Scratch &s, uint32_t *total_out, hipStream_t stream)
 {
     constexpr uint64_t T = (uint64_t)kBlock * V * 4;
     const uint32_t head = head_of(data);
     const uint64_t ntiles = tiles_for(n, head, T);
     uint32_t *abase = data - head;
     uint64_t *desc = reinterpret_cast<uint64_t *>(s.body());
-    if (inclusive)
-        hipLaunchKernelGGL((scan_lookback_kernel<kBlock, V, true>), dim3((uint32_t)ntiles),
-                           dim3(kBlock), 0, stream, abase, (uint64_t)head, n + head,
-                           (uint32_t)ntiles, s.ticket(), desc, total_out);
-    else
-        hipLaunchKernelGGL((scan_lookback_kernel<kBlock, V, false>), dim3((uint32_t)ntiles),
-                           dim3(kBlock), 0, stream, abase, (uint64_t)head, n + head,
-                           (uint32_t)ntiles, s.ticket(), desc, total_out);
+    if constexpr (V <= 16) {
+        if (persistent) {
+        auto kern = inclusive ? scan_persistent_kernel<kBlock, V, true>
+                              : scan_persistent_kernel<kBlock, V, false>;
+        uint64_t grid = (uint64_t)resident_grid((const void *)kern, kBlock);
+        if (grid > ntiles)
+            grid = ntiles;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kBlock), 0, stream, abase,
+                           (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(), s.exits(), desc,
+                           s.dummy_line(), total_out);
+        return hipGetLastError();
+        }
+    }
+    {
+        auto kern = inclusive ? scan_lookback_kernel<kBlock, V, true>
+                              : scan_lookback_kernel<kBlock, V, false>;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)ntiles), dim3(kBlock), 0, stream, abase,
+                           (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(), desc, total_out);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
-                                uint32_t *total_out, hipStream_t stream)
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+                                const Scratch &s, uint32_t *total_out, hipStream_t stream)
 {
     switch (scan_chunks()) {
-    case 4: return scan_lookback_v<4>(data, n, inclusive, s, total_out, stream);
-    case 16: return scan_lookback_v<16>(data, n, inclusive, s, total_out, stream);
-    default: return scan_lookback_v<8>(data, n, inclusive, s, total_out, stream);
+    case 4: return scan_lookback_v<4>(data, n, inclusive, persistent, s, total_out, stream);
+    case 16: return scan_lookback_v<16>(data, n, inclusive, persistent, s, total_out, stream);
+    case 32:
+        // Two 32-chunk buffers do not fit a wave's registers: the pipelined
+        // kernel stays at 16.
+        return persistent ? scan_lookback_v<16>(data, n, inclusive, true, s, total_out, stream)
+                          : scan_lookback_v<32>(data, n, inclusive, false, s, total_out, stream);
+    default: return scan_lookback_v<8>(data, n, inclusive, persistent, s, total_out, stream);
     }
 }
 

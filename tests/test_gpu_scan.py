@@ -60,12 +60,13 @@ def test_threepass_deep_fork_depths(b):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 63, 64, 65, 255, 1023, 1024, 1025, 4095, 4096, 4097,
-                               8191, 8192, 8193, 16383, 16385, 65537, 100003, (1 << 20) + 7,
-                               3 * (1 << 20) + 1])
+                               8191, 8192, 8193, 16383, 16384, 16385, 24577, 65537, 100003,
+                               (1 << 20) + 7, 3 * (1 << 20) + 1, 5 * (1 << 21) - 3])
 def test_ragged_sizes(n):
     a = workloads.small_random_u32(n, n)
     for inclusive in (False, True):
         check(a, inclusive)
+        check(a, inclusive, algo="lookback_pipelined")
         check(a, inclusive, algo="threepass")
         check(a, inclusive, algo="threepass", fork_depth=3)
 
@@ -76,6 +77,7 @@ def test_unaligned_pointers(n, offset):
     a = workloads.small_random_u32(n, 31 * n + offset)
     for inclusive in (False, True):
         check(a, inclusive, offset=offset)
+        check(a, inclusive, algo="lookback_pipelined", offset=offset)
         check(a, inclusive, algo="threepass", offset=offset)
         check(a, inclusive, algo="threepass", fork_depth=2, offset=offset)
 
@@ -132,11 +134,32 @@ def test_total_on_device_and_host_agree():
 
 
 def test_repeated_calls_reuse_scratch():
-    # The chained carry's epoch advances every launch; calls of shrinking and
-    # growing size on one stream must each be exact.
-    for rep, n in enumerate([1 << 20, 5000, 1 << 18, 1 << 20, 77, (1 << 20) + 3]):
+    # The chained carry's ticket and exit counter are reset by each launch
+    # for the next; calls of shrinking and growing size, of both single-pass
+    # kernels, interleaved on one stream and one scratch buffer, must each be
+    # exact.
+    sizes = [1 << 20, 5000, 1 << 18, 1 << 22, 77, (1 << 20) + 3, 1, 8192, 3 << 20, 12345]
+    for rep, n in enumerate(sizes * 2):
         a = workloads.small_random_u32(n, 900 + rep)
-        check(a, rep % 2 == 1)
+        algo = "lookback" if rep % 3 else "lookback_pipelined"
+        check(a, rep % 2 == 1, algo=algo)
+
+
+def test_back_to_back_without_sync():
+    # Many launches queued on one stream with no host sync in between; each
+    # must see the scratch state its predecessor left.
+    n = (1 << 21) + 5
+    a = workloads.small_random_u32(n, 4242)
+    t = to_dev(a)
+    tot = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ref = a.copy()
+    for rep in range(12):
+        inclusive = rep % 2 == 1
+        f = ps.scan_inclusive_u32 if inclusive else ps.scan_exclusive_u32
+        f(t, want_total=False, total_dev=tot)
+        ref, _ = oracle.scan_u32(ref, inclusive)
+    got = to_host_u32(t)
+    assert first_mismatch(got, ref) is None
 
 
 def test_empty():
