@@ -14,11 +14,16 @@
  *   caller asks for a result on the host (a non-NULL *_host pointer), because
  *   only then does the host observe it.
  * Scratch.  Calls that coordinate workgroups need device scratch memory,
- *   sized by the matching *_scratch_bytes query.  A scratch buffer must be
- *   zero-filled once before its first use (libscan_scratch_init does this
- *   on the stream); after that the library keeps it consistent from call to
- *   call by itself, with no clearing in between.  Two calls that may run at
- *   the same time (different streams) need different scratch buffers.
+ *   sized by the matching *_scratch_bytes query.  One buffer may serve every
+ *   entry point.  The library remembers, per buffer, what its last call left
+ *   there and clears (with a small fill kernel on the stream) whatever state
+ *   the next call cannot trust -- a buffer it has not seen, or one whose last
+ *   call used another layout; calls of the same kind reuse the state without
+ *   any clearing.  If anything other than libscan writes to a scratch buffer
+ *   between calls (or it is freed and another allocation lands at the same
+ *   address), call libscan_scratch_init on it before its next use.  Two calls
+ *   that may run at the same time (different streams) need different scratch
+ *   buffers.
  * Errors.  Every int-returning call returns LIBSCAN_OK (0) or a negative
  *   LIBSCAN_ERR_* code.  Argument errors are found before anything is
  *   launched and leave every buffer untouched.  LIBSCAN_ERR_HIP means a HIP
@@ -78,8 +83,9 @@ const char *libscan_strerror(int status);
 const char *libscan_version(void);
 
 /* Zero-fill `scratch_bytes` bytes of device scratch on `stream` with a fill
- * kernel (no hipMemset node, so it can be captured in a graph).  Required
- * once before a scratch buffer's first use. */
+ * kernel (no hipMemset node, so it can be captured in a graph), and record the
+ * buffer as clean, so the next call on it clears nothing.  Needed only after
+ * something other than libscan has written to the buffer. */
 int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
@@ -100,8 +106,7 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
  *              waits for the stream.
  * total_dev    device u32 or NULL.  If set, the total is written there in
  *              stream order; the call does not wait.
- * scratch      device scratch of at least scan_scratch_bytes(n) bytes,
- *              zero-filled once before first use.
+ * scratch      device scratch of at least scan_scratch_bytes(n) bytes.
  * stream       HIP stream.
  * Errors: ERR_NULL (data NULL with n > 0, or scratch NULL with n > 0),
  * ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_SCRATCH, ERR_HIP.
@@ -156,7 +161,7 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
  *           allowed.
  * seg_len   segment length >= 1; seg_len >= n is one segment.
  * seg_sums  device, ceil(n / seg_len) u32, or NULL to skip the sums.
- * scratch   at least segscan_scratch_bytes(n, seg_len) bytes, zeroed once.
+ * scratch   at least segscan_scratch_bytes(n, seg_len) bytes.
  * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_ARG
  * (seg_len == 0), ERR_SCRATCH, ERR_HIP.
  */
@@ -181,7 +186,7 @@ int segscan_u32(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
  *             overlap flags.
  * count_host  host u32 or NULL (if set, the call waits for the stream).
  * count_dev   device u32 or NULL.
- * scratch     at least compact_scratch_bytes(n) bytes, zeroed once.
+ * scratch     at least compact_scratch_bytes(n) bytes.
  * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N_INDEX),
  * ERR_SCRATCH, ERR_HIP.
  */
@@ -206,8 +211,8 @@ int compact_flags_u32(const int32_t *flags, int32_t *out_idx, uint64_t n, uint32
  * perm           device, n int32 output.  Must not overlap keys.
  * bits_per_pass  1 (32 one-bit passes) or 4 (8 four-bit passes); both give
  *                the same permutation.
- * scratch        at least radix_scratch_bytes(n, bits_per_pass) bytes,
- *                zeroed once.  It holds the key and index ping-pong rows.
+ * scratch        at least radix_scratch_bytes(n, bits_per_pass) bytes.  It
+ *                holds the key and index ping-pong rows.
  * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N_INDEX), ERR_ARG
  * (bits_per_pass not 1 or 4), ERR_SCRATCH, ERR_HIP.
  */

@@ -19,16 +19,27 @@ constexpr uint64_t kTile = (uint64_t)kBlock * kChunks * 4;
 
 // Scratch layout.  The caller's pointer is rounded up to 256 bytes; all
 // offsets below are from that aligned base.
-//   [0, 8)      ticket word of the chained carry {epoch, next tile}
-//   [8, 12)     exit counter of the persistent kernels
+//
+// Header, the same for every entry point, never overwritten with data:
+//   [0, 8)      ticket A of the chained carry {epoch, next tile}
+//   [8, 12)     exit counter A (persistent kernels)
+//   [16, 24)    ticket B (the radix histogram scan)
+//   [24, 28)    exit counter B
 //   [64, 68)    total / count slot, used when the caller asks for the result
 //               on the host only
 //   [128, 144)  a line the persistent kernels read in place of a tile when
 //               they have nothing to prefetch (its contents are never used)
-//   [256, ...)  body: per-tile descriptors, block sums, staging rows
+// Body, from 256: each entry point's state (tile descriptors) first, then its
+// data (block sums, radix ping-pong rows).  Tickets and descriptors carry the
+// epoch of the launch that wrote them, so they stay valid from launch to
+// launch without clearing -- as long as no data of another layout has been
+// written over them.  The C ABI tracks that (state.cpp) and clears a state
+// region before a call whenever the buffer's previous layout could have
+// overwritten it.
 constexpr size_t kScratchAlign = 256;
 constexpr size_t kHeaderBytes = 256;
 constexpr size_t kTotalSlotOffset = 64;
+constexpr size_t kTicketBOffset = 16;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -41,10 +52,13 @@ inline uint64_t tiles_for(uint64_t n, uint32_t head, uint64_t tile)
 }
 
 struct Scratch {
-    uint8_t *base;       // aligned base
-    size_t bytes;        // usable bytes from base
-    uint64_t *ticket() const { return reinterpret_cast<uint64_t *>(base); }
-    uint32_t *exits() const { return reinterpret_cast<uint32_t *>(base + 8); }
+    uint8_t *base;          // aligned base: the header
+    size_t bytes;           // usable bytes from base
+    uint64_t *ticket_ptr;   // the ticket this launcher's kernels draw from
+    uint64_t *desc_ptr;     // the descriptor array they publish into
+    uint64_t *ticket() const { return ticket_ptr; }
+    uint32_t *exits() const { return reinterpret_cast<uint32_t *>(ticket_ptr + 1); }
+    uint64_t *desc() const { return desc_ptr; }
     uint32_t *total_slot() const { return reinterpret_cast<uint32_t *>(base + kTotalSlotOffset); }
     uint8_t *body() const { return base + kHeaderBytes; }
     const uint32_t *dummy_line() const { return reinterpret_cast<const uint32_t *>(base + 128); }
@@ -81,5 +95,7 @@ size_t compact_body_bytes(uint64_t n);
 hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass,
                         const Scratch &s, hipStream_t stream);
 size_t radix_body_bytes(uint64_t n, int bits_per_pass);
+// Bytes at the front of the radix body that hold descriptors (the state).
+size_t radix_state_bytes(uint64_t n, int bits_per_pass);
 
 }  // namespace libscan

@@ -7,6 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <unordered_map>
+
 using namespace libscan;
 
 namespace {
@@ -37,7 +40,90 @@ bool carve(void *scratch, size_t scratch_bytes, size_t body, Scratch *out)
         return false;
     out->base = reinterpret_cast<uint8_t *>(a);
     out->bytes = usable;
+    out->ticket_ptr = reinterpret_cast<uint64_t *>(out->base);
+    out->desc_ptr = reinterpret_cast<uint64_t *>(out->base + kHeaderBytes);
     return true;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch state tracking.
+//
+// Tickets (header) and tile descriptors (front of the body) stay valid from
+// launch to launch because every word carries the epoch of the launch that
+// wrote it.  Two things break that: data of another layout written over a
+// descriptor region (the three-pass sums, the radix rows), and a buffer whose
+// contents the library has never seen.  The library therefore remembers,
+// per scratch buffer, what its last call left there, and before each call
+// clears (with a fill kernel on the call's stream) whatever state the call
+// will read that it cannot vouch for:
+//   ZERO  -- libscan_scratch_init zeroed the buffer: every state is valid.
+//   DESC  -- descriptors of the look-back scan, segmented scan or
+//            compaction in the first `state` body bytes: valid for any of
+//            those three, a larger call clears only the extra range.
+//   RADIX -- the radix layout for one (n, bits_per_pass): valid only for the
+//            same pair.
+//   DATA  -- the three-pass scan's block sums over the body: nothing valid.
+// An unknown buffer is cleared.  Forgetting a buffer is therefore always
+// safe, so the table is simply emptied if it grows large.  After 2^29
+// launches on one buffer the state is cleared too, long before the 30-bit
+// epoch in the descriptors could repeat.
+// ---------------------------------------------------------------------------
+enum StateKind { kKindZero = 1, kKindDesc = 2, kKindRadix = 3, kKindData = 4 };
+
+struct StateRecord {
+    int kind;
+    uint64_t sig;
+    size_t state;          // body bytes of valid state from the front
+    uint64_t launches;     // launches since the last full clear
+};
+
+std::mutex g_state_mu;
+std::unordered_map<uintptr_t, StateRecord> g_state;
+constexpr uint64_t kMaxLaunchesBetweenClears = 1ull << 29;
+constexpr size_t kMaxTrackedBuffers = 4096;
+
+hipError_t prepare_state(const Scratch &s, int kind, uint64_t sig, size_t state,
+                         uint64_t launches, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lock(g_state_mu);
+    if (g_state.size() > kMaxTrackedBuffers)
+        g_state.clear();
+    const uintptr_t key = (uintptr_t)s.base;
+    StateRecord prev{0, 0, 0, 0};
+    auto it = g_state.find(key);
+    if (it != g_state.end())
+        prev = it->second;
+    if (kind == kKindData) {
+        g_state[key] = StateRecord{kKindData, 0, 0, prev.launches};
+        return hipSuccess;
+    }
+    const bool fresh_epochs = prev.kind != 0 && prev.launches + launches < kMaxLaunchesBetweenClears;
+    size_t valid = 0;              // body bytes this call may trust as they are
+    bool header_ok = false;
+    if (fresh_epochs) {
+        if (prev.kind == kKindZero || (prev.kind == kKindDesc && kind == kKindDesc)) {
+            header_ok = true;
+            valid = prev.state;
+        } else if (prev.kind == kKindRadix && kind == kKindRadix && prev.sig == sig) {
+            header_ok = true;
+            valid = state;
+        }
+    }
+    hipError_t e = hipSuccess;
+    StateRecord next{kind, sig, state, prev.launches + launches};
+    if (!header_ok) {
+        e = launch_fill_zero(s.base, kHeaderBytes + state, stream);
+        next.launches = launches;
+    } else if (valid < state) {
+        e = launch_fill_zero(s.body() + valid, state - valid, stream);
+    } else if (kind == kKindDesc) {
+        next.state = valid;        // the larger valid range stays valid
+    }
+    if (e == hipSuccess)
+        g_state[key] = next;
+    else
+        g_state.erase(key);
+    return e;
 }
 
 size_t with_header(size_t body) { return (kScratchAlign - 1) + kHeaderBytes + body; }
@@ -110,8 +196,13 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
     hipError_t e;
     if (algo == LIBSCAN_ALGO_THREEPASS) {
         const unsigned d = threepass_depth(n, fork_depth);
-        e = launch_scan_threepass(data, n, inclusive != 0, d, s, tot, stream);
+        e = prepare_state(s, kKindData, 0, 0, 0, stream);
+        if (e == hipSuccess)
+            e = launch_scan_threepass(data, n, inclusive != 0, d, s, tot, stream);
     } else {
+        e = prepare_state(s, kKindDesc, 0, scan_lookback_body_bytes(n, 3), 1, stream);
+        if (e != hipSuccess)
+            return hip_status(e);
         e = launch_scan_lookback(data, n, inclusive != 0, algo == LIBSCAN_ALGO_LOOKBACK_PIPELINED,
                                  s, tot, stream);
     }
@@ -146,7 +237,14 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
 {
     if (!scratch)
         return scratch_bytes ? LIBSCAN_ERR_NULL : LIBSCAN_OK;
-    return hip_status(launch_fill_zero(scratch, scratch_bytes, stream));
+    hipError_t e = launch_fill_zero(scratch, scratch_bytes, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    Scratch s;
+    std::lock_guard<std::mutex> lock(g_state_mu);
+    if (carve(scratch, scratch_bytes, 0, &s))
+        g_state[(uintptr_t)s.base] = StateRecord{kKindZero, 0, s.bytes - kHeaderBytes, 0};
+    return LIBSCAN_OK;
 }
 
 size_t scan_scratch_bytes(uint64_t n)
@@ -208,6 +306,9 @@ int segscan_u32(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
     Scratch s;
     if (!carve(scratch, scratch_bytes, segscan_body_bytes(n, seg_len), &s))
         return LIBSCAN_ERR_SCRATCH;
+    hipError_t e = prepare_state(s, kKindDesc, 0, segscan_body_bytes(n, seg_len), 1, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
     return hip_status(launch_segscan(in, out, n, seg_len, seg_sums, s, stream));
 }
 
@@ -228,7 +329,10 @@ int compact_flags_u32(const int32_t *flags, int32_t *out_idx, uint64_t n, uint32
     if (!carve(scratch, scratch_bytes, compact_body_bytes(n), &s))
         return LIBSCAN_ERR_SCRATCH;
     uint32_t *cnt = count_dev ? count_dev : s.total_slot();
-    hipError_t e = launch_compact(flags, out_idx, n, s, cnt, stream);
+    hipError_t e = prepare_state(s, kKindDesc, 0, compact_body_bytes(n), 1, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    e = launch_compact(flags, out_idx, n, s, cnt, stream);
     if (e != hipSuccess)
         return hip_status(e);
     if (count_host)
@@ -257,6 +361,11 @@ int radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per
     Scratch s;
     if (!carve(scratch, scratch_bytes, radix_body_bytes(n, bits_per_pass), &s))
         return LIBSCAN_ERR_SCRATCH;
+    hipError_t e = prepare_state(s, kKindRadix, (n << 3) | (uint64_t)bits_per_pass,
+                                 radix_state_bytes(n, bits_per_pass), bits_per_pass == 1 ? 32 : 8,
+                                 stream);
+    if (e != hipSuccess)
+        return hip_status(e);
     return hip_status(launch_radix(keys, perm, n, bits_per_pass, s, stream));
 }
 

@@ -1,6 +1,504 @@
+// radix_kernels.hip -- the stable LSB radix-sort permutation of u32 keys on
+// gfx950.
+//
+// entelechy "parallel" package, sort / sort_pass / sort_zeros / sort_place:
+// least significant bit first; per bit, the count of zeros at or before each
+// place ranks the zeros, and every one lands behind all zeros at its rank
+// among the ones.  CAIRN "Concurrency", section "scan": a radix sort that
+// places each digit with an exclusive scan is stable.
+//
+// The page's passes gather the keys through the permutation on every bit
+// (at(keys, at(order, i))).  Here each pass streams (key, index) pairs
+// instead, so no pass gathers: pass b reads the pairs in the order pass b-1
+// left them and writes them in the order of bit b.
+//
+// One-bit passes (32): one kernel each.  A tile counts its zeros, takes the
+// zeros before it from the chained carry, and splits its pairs stably in LDS
+// (zeros first); zeros then go to [zeros_before, +Kz) and ones to
+// [Z + ones_before, +Ko), two contiguous ranges.  Z, the array's zero count
+// for the bit, does not depend on the order, so one read of the keys before
+// the first pass counts it for all 32 bits.
+//
+// Four-bit passes (8): each digit pass is histogram -> scan -> scatter.  The
+// histogram kernel counts the 16 digits of every tile into a digit-major
+// table; the library's own single-pass scan turns the table into every
+// (digit, tile) base; the scatter kernel sorts its tile by digit in LDS
+// (four stable one-bit splits) and writes each digit's run to its base.
 #include "device_common.hpp"
 #include "launch.hpp"
+
 namespace libscan {
-size_t radix_body_bytes(uint64_t, int) { return 0; }
-hipError_t launch_radix(const uint32_t *, int32_t *, uint64_t, int, const Scratch &, hipStream_t) { return hipErrorNotSupported; }
+
+constexpr int kRadixChunks = 4;     // 256 threads x 4 chunks: 4096 keys per tile
+constexpr uint64_t kRadixTile = (uint64_t)kBlock * kRadixChunks * 4;
+
+// ---------------------------------------------------------------------------
+// Ones per bit over the whole array (for the one-bit passes' Z).
+// ---------------------------------------------------------------------------
+template <int BLOCK, int V>
+__global__ __launch_bounds__(BLOCK) void bit_ones_kernel(const uint32_t *__restrict__ kbase,
+                                                         uint64_t vlo, uint64_t vhi,
+                                                         uint32_t *ones)
+{
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    constexpr int NW = BLOCK / kWave;
+    __shared__ uint32_t s_part[NW][32];
+    uint32_t c[32];
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+        c[b] = 0;
+    for (uint64_t vs = (uint64_t)blockIdx.x * T; vs < vhi; vs += (uint64_t)gridDim.x * T) {
+        u32x4 x[V];
+        load_tile<BLOCK, V>(kbase, vs, vlo, vhi, x);    // outside the array: key 0
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+#pragma unroll
+            for (int b = 0; b < 32; ++b)
+                c[b] += ((x[k].x >> b) & 1u) + ((x[k].y >> b) & 1u) + ((x[k].z >> b) & 1u) +
+                        ((x[k].w >> b) & 1u);
+        }
+    }
+    const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+        const uint32_t t = wave_sum(c[b]);
+        if (lane_id() == 0)
+            s_part[wave][b] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            t += s_part[w][threadIdx.x];
+        atomicAdd(ones + threadIdx.x, t);
+    }
 }
+
+// ---------------------------------------------------------------------------
+// One stable split of (key, index) pairs on bit `bit`.
+//   FIRST: keys come from the caller's array (virtual range [vlo, vhi)), and
+//          the index of each key is its position.
+//   LAST:  only the indices are written (into the caller's permutation).
+// ---------------------------------------------------------------------------
+template <int BLOCK, int V, bool FIRST, bool LAST>
+__global__ __launch_bounds__(BLOCK) void radix1_pass_kernel(
+    const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,
+    const uint32_t *__restrict__ iin, uint32_t *__restrict__ kout, uint32_t *__restrict__ iout,
+    uint32_t bit, const uint32_t *__restrict__ ones, uint32_t ntiles, uint64_t *ticket,
+    uint64_t *desc)
+{
+    using TS = TileScan<BLOCK, V>;
+    constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
+    __shared__ uint32_t s_cell[TS::NCELL];
+    __shared__ uint32_t s_key[T], s_idx[T];
+    __shared__ uint32_t s_tile, s_tag, s_carry, s_zeros;
+
+    if (threadIdx.x == 0) {
+        const TileTicket tk = draw_ticket(ticket, ntiles);
+        s_tile = tk.tile;
+        s_tag = tk.tag;
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint32_t tag = s_tag;
+    const uint64_t vstart = (uint64_t)tile * T;
+    const uint64_t n = vhi - vlo;
+    const uint64_t lo = vstart > vlo ? vstart : vlo;     // first valid slot
+    const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
+    const uint32_t skip = (uint32_t)(lo - vstart);        // invalid slots before it
+
+    u32x4 key[V], idx[V], z[V];
+    uint32_t w[V];
+    load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, key);
+    if (!FIRST)
+        load_tile<BLOCK, V>(iin, vstart, vlo, vhi, idx);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
+        if (FIRST) {
+            idx[k].x = (uint32_t)(v0 + 0 - vlo);
+            idx[k].y = (uint32_t)(v0 + 1 - vlo);
+            idx[k].z = (uint32_t)(v0 + 2 - vlo);
+            idx[k].w = (uint32_t)(v0 + 3 - vlo);
+        }
+        z[k].x = (v0 + 0 >= vlo && v0 + 0 < vhi) && !((key[k].x >> bit) & 1u);
+        z[k].y = (v0 + 1 >= vlo && v0 + 1 < vhi) && !((key[k].y >> bit) & 1u);
+        z[k].z = (v0 + 2 >= vlo && v0 + 2 < vhi) && !((key[k].z >> bit) & 1u);
+        z[k].w = (v0 + 3 >= vlo && v0 + 3 < vhi) && !((key[k].w >> bit) & 1u);
+    }
+    TS::local(z, w, s_cell);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t kz = TS::cells(s_cell);
+        uint32_t excl = 0;
+        if (tile == 0) {
+            if (threadIdx.x == 0)
+                publish(desc, 0, tag, kStatusPrefix, kz);
+        } else {
+            if (threadIdx.x == 0)
+                publish(desc, tile, tag, kStatusAgg, kz);
+            excl = lookback(desc, tile, tag);
+            if (threadIdx.x == 0)
+                publish(desc, tile, tag, kStatusPrefix, excl + kz);
+        }
+        if (threadIdx.x == 0) {
+            s_carry = excl;
+            s_zeros = kz;
+        }
+    }
+    __syncthreads();
+    const uint32_t kz = s_zeros;
+
+    // Stable split in LDS: zeros at their zero rank, ones after all zeros at
+    // their one rank (slot among valid keys minus zeros before it).
+    TS::template apply<false>(z, w, s_cell, 0u);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+        const uint64_t v0 = vstart + e0;
+        const uint32_t kk[4] = {key[k].x, key[k].y, key[k].z, key[k].w};
+        const uint32_t ii[4] = {idx[k].x, idx[k].y, idx[k].z, idx[k].w};
+        const uint32_t zr[4] = {z[k].x, z[k].y, z[k].z, z[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (v0 + j < vlo || v0 + j >= vhi)
+                continue;
+            const uint32_t slot = e0 + j - skip;
+            const uint32_t p = ((kk[j] >> bit) & 1u) ? kz + (slot - zr[j]) : zr[j];
+            s_key[p] = kk[j];
+            s_idx[p] = ii[j];
+        }
+    }
+    __syncthreads();
+
+    const uint32_t zeros_before = s_carry;
+    const uint32_t valid = (uint32_t)(hi - lo);
+    const uint32_t ones_before = (uint32_t)(lo - vlo) - zeros_before;
+    const uint32_t Z = (uint32_t)n - ones[bit];
+    for (uint32_t p = threadIdx.x; p < valid; p += BLOCK) {
+        const uint32_t dest = p < kz ? zeros_before + p : Z + ones_before + (p - kz);
+        if (!LAST)
+            kout[dest] = s_key[p];
+        iout[dest] = s_idx[p];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Four-bit digit passes.
+// ---------------------------------------------------------------------------
+
+// hist[d * ntiles + tile] = how many keys of the tile have digit d.
+template <int BLOCK, int V>
+__global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__restrict__ kbase,
+                                                           uint64_t vlo, uint64_t vhi,
+                                                           uint32_t shift, uint32_t ntiles,
+                                                           uint32_t *__restrict__ hist)
+{
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    constexpr int NW = BLOCK / kWave;
+    static_assert(V * 4 < 256, "per-thread digit counts are 8-bit fields");
+    __shared__ uint32_t s_part[NW][16];
+    const uint32_t tile = blockIdx.x;
+    const uint64_t vstart = (uint64_t)tile * T;
+    u32x4 x[V];
+    load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, x);
+    // 16 counters as four words of four 8-bit fields.
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
+        const uint32_t kk[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (v0 + j < vlo || v0 + j >= vhi)
+                continue;
+            const uint32_t d = (kk[j] >> shift) & 15u;
+            const uint32_t inc = 1u << ((d & 3u) * 8u);
+            const uint32_t sel = d >> 2;
+            c[0] += sel == 0 ? inc : 0u;
+            c[1] += sel == 1 ? inc : 0u;
+            c[2] += sel == 2 ? inc : 0u;
+            c[3] += sel == 3 ? inc : 0u;
+        }
+    }
+    const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+        const uint32_t t = wave_sum((c[d >> 2] >> ((d & 3) * 8)) & 0xFFu);
+        if (lane_id() == 0)
+            s_part[wave][d] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            t += s_part[w][threadIdx.x];
+        hist[(uint64_t)threadIdx.x * ntiles + tile] = t;
+    }
+}
+
+// Scatter one tile by its digit.  base[d * ntiles + tile] is the exclusive
+// scan of the digit-major histogram: where digit d of this tile starts.
+template <int BLOCK, int V, bool FIRST, bool LAST>
+__global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
+    const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,
+    const uint32_t *__restrict__ iin, uint32_t *__restrict__ kout, uint32_t *__restrict__ iout,
+    uint32_t shift, uint32_t ntiles, const uint32_t *__restrict__ base)
+{
+    using TS = TileScan<BLOCK, V>;
+    constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
+    __shared__ uint32_t s_cell[TS::NCELL];
+    __shared__ uint32_t s_key[T], s_idx[T];
+    __shared__ uint32_t s_zeros, s_base[16], s_start[16];
+    const uint32_t tile = blockIdx.x;
+    const uint64_t vstart = (uint64_t)tile * T;
+    const uint64_t n = vhi - vlo;
+    const uint64_t lo = vstart > vlo ? vstart : vlo;
+    const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
+    const uint32_t skip = (uint32_t)(lo - vstart);
+    const uint32_t valid = (uint32_t)(hi - lo);
+
+    // Valid pairs into LDS, in order, at slots 0 .. valid-1.
+    {
+        u32x4 key[V], idx[V];
+        load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, key);
+        if (!FIRST)
+            load_tile<BLOCK, V>(iin, vstart, vlo, vhi, idx);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            const uint64_t v0 = vstart + e0;
+            const uint32_t kk[4] = {key[k].x, key[k].y, key[k].z, key[k].w};
+            const uint32_t ii[4] = {idx[k].x, idx[k].y, idx[k].z, idx[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (v0 + j < vlo || v0 + j >= vhi)
+                    continue;
+                s_key[e0 + j - skip] = kk[j];
+                s_idx[e0 + j - skip] = FIRST ? (uint32_t)(v0 + j - vlo) : ii[j];
+            }
+        }
+    }
+    __syncthreads();
+
+    // Four stable one-bit splits, least significant digit bit first: the
+    // tile ends up sorted by digit, equal digits in their original order.
+    // Slots at or past `valid` count as ones, so they stay at the end.
+    for (uint32_t b = shift; b < shift + 4; ++b) {
+        u32x4 z[V];
+        uint32_t w[V];
+        uint32_t kk[V][4], ii[V][4];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            uint32_t zz[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = e0 + j;
+                kk[k][j] = e < valid ? s_key[e] : 0u;
+                ii[k][j] = e < valid ? s_idx[e] : 0u;
+                zz[j] = e < valid && !((kk[k][j] >> b) & 1u);
+            }
+            z[k].x = zz[0];
+            z[k].y = zz[1];
+            z[k].z = zz[2];
+            z[k].w = zz[3];
+        }
+        TS::local(z, w, s_cell);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const uint32_t kz = TS::cells(s_cell);
+            if (threadIdx.x == 0)
+                s_zeros = kz;
+        }
+        __syncthreads();
+        const uint32_t kz = s_zeros;
+        TS::template apply<false>(z, w, s_cell, 0u);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            const uint32_t zr[4] = {z[k].x, z[k].y, z[k].z, z[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = e0 + j;
+                if (e >= valid)
+                    continue;
+                const uint32_t p = ((kk[k][j] >> b) & 1u) ? kz + (e - zr[j]) : zr[j];
+                s_key[p] = kk[k][j];
+                s_idx[p] = ii[k][j];
+            }
+        }
+        __syncthreads();
+    }
+
+    // Where each digit's run starts in the tile and in the output.
+    if (threadIdx.x < kWave) {
+        const uint32_t d = lane_id();
+        uint32_t b0 = 0, cnt = 0;
+        if (d < 16) {
+            const uint64_t f = (uint64_t)d * ntiles + tile;
+            b0 = base[f];
+            const uint32_t nx = (f + 1 < 16ull * ntiles) ? base[f + 1] : (uint32_t)n;
+            cnt = nx - b0;
+        }
+        const uint32_t incl = wave_incl_add(cnt);
+        if (d < 16) {
+            s_base[d] = b0;
+            s_start[d] = incl - cnt;
+        }
+    }
+    __syncthreads();
+    for (uint32_t p = threadIdx.x; p < valid; p += BLOCK) {
+        const uint32_t kv = s_key[p];
+        const uint32_t d = (kv >> shift) & 15u;
+        const uint32_t dest = s_base[d] + (p - s_start[d]);
+        if (!LAST)
+            kout[dest] = kv;
+        iout[dest] = s_idx[p];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct RadixLayout {
+    size_t desc, spine_desc, state, ones, hist, ka, kb, ia, ib, total;
+};
+
+RadixLayout radix_layout(uint64_t n, int bits_per_pass)
+{
+    const uint64_t ntiles = tiles_for(n, 3, kRadixTile);
+    RadixLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes, kScratchAlign);
+        return at;
+    };
+    // State first (descriptors of the one-bit passes and of the histogram
+    // scan), then data.
+    L.desc = take(ntiles * sizeof(uint64_t));
+    L.spine_desc = bits_per_pass == 4 ? take(scan_lookback_body_bytes(16 * ntiles, 0)) : 0;
+    L.state = off;
+    L.ones = take(32 * sizeof(uint32_t));
+    if (bits_per_pass == 4)
+        L.hist = take(16 * ntiles * sizeof(uint32_t));
+    L.ka = take(n * sizeof(uint32_t));
+    L.kb = take(n * sizeof(uint32_t));
+    L.ia = take(n * sizeof(uint32_t));
+    L.ib = take(n * sizeof(uint32_t));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+size_t radix_state_bytes(uint64_t n, int bits_per_pass)
+{
+    if (bits_per_pass != 1 && bits_per_pass != 4)
+        return 0;
+    return radix_layout(n, bits_per_pass).state;
+}
+
+size_t radix_body_bytes(uint64_t n, int bits_per_pass)
+{
+    if (bits_per_pass != 1 && bits_per_pass != 4)
+        return 0;
+    return radix_layout(n, bits_per_pass).total;
+}
+
+hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per_pass,
+                        const Scratch &s, hipStream_t stream)
+{
+    const RadixLayout L = radix_layout(n, bits_per_pass);
+    uint8_t *body = s.body();
+    uint32_t *ka = reinterpret_cast<uint32_t *>(body + L.ka);
+    uint32_t *kb = reinterpret_cast<uint32_t *>(body + L.kb);
+    uint32_t *ia = reinterpret_cast<uint32_t *>(body + L.ia);
+    uint32_t *ib = reinterpret_cast<uint32_t *>(body + L.ib);
+    uint32_t *pb = reinterpret_cast<uint32_t *>(perm);
+    // Pass p reads the side pass p-1 wrote and writes side p % 2 (side 0 =
+    // ka, ia; side 1 = kb, ib), both in scratch, aligned for vector loads.
+    // The last pass writes only indices, straight into the caller's
+    // permutation, with 4-byte stores (any 4-byte alignment).
+    uint32_t *kside[2] = {ka, kb};
+    uint32_t *iside[2] = {ia, ib};
+    const uint32_t head = head_of(keys);
+    const uint64_t ntiles_user = tiles_for(n, head, kRadixTile);
+    const uint64_t ntiles_own = tiles_for(n, 0, kRadixTile);
+    const uint32_t *kuser = keys - head;
+    const dim3 blk(kBlock);
+
+    if (bits_per_pass == 1) {
+        uint32_t *ones = reinterpret_cast<uint32_t *>(body + L.ones);
+        uint64_t *desc = reinterpret_cast<uint64_t *>(body + L.desc);
+        hipError_t e = launch_fill_zero(ones, 32 * sizeof(uint32_t), stream);
+        if (e != hipSuccess)
+            return e;
+        uint64_t grid = (n + head + kRadixTile - 1) / kRadixTile;
+        if (grid > 2048)
+            grid = 2048;
+        hipLaunchKernelGGL((bit_ones_kernel<kBlock, kRadixChunks>), dim3((uint32_t)grid), blk, 0,
+                           stream, kuser, (uint64_t)head, n + head, ones);
+        for (uint32_t b = 0; b < 32; ++b) {
+            uint32_t *ko = kside[b & 1], *io = b == 31 ? pb : iside[b & 1];
+            if (b == 0)
+                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, true, false>),
+                                   dim3((uint32_t)ntiles_user), blk, 0, stream, kuser,
+                                   (uint64_t)head, n + head, nullptr, ko, io, b, ones,
+                                   (uint32_t)ntiles_user, s.ticket(), desc);
+            else if (b == 31)
+                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, false, true>),
+                                   dim3((uint32_t)ntiles_own), blk, 0, stream, kside[(b - 1) & 1],
+                                   0ull, n, iside[(b - 1) & 1], ko, io, b, ones,
+                                   (uint32_t)ntiles_own, s.ticket(), desc);
+            else
+                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, false, false>),
+                                   dim3((uint32_t)ntiles_own), blk, 0, stream, kside[(b - 1) & 1],
+                                   0ull, n, iside[(b - 1) & 1], ko, io, b, ones,
+                                   (uint32_t)ntiles_own, s.ticket(), desc);
+        }
+        return hipGetLastError();
+    }
+
+    uint32_t *hist = reinterpret_cast<uint32_t *>(body + L.hist);
+    // The histogram scan draws from ticket B and publishes into its own
+    // descriptors, so it never disturbs the one-bit passes' state.
+    Scratch spine = s;
+    spine.ticket_ptr = reinterpret_cast<uint64_t *>(s.base + kTicketBOffset);
+    spine.desc_ptr = reinterpret_cast<uint64_t *>(body + L.spine_desc);
+    for (uint32_t p = 0; p < 8; ++p) {
+        const uint32_t shift = 4 * p;
+        const bool first = p == 0;
+        const uint32_t *kin = first ? kuser : kside[(p - 1) & 1];
+        const uint32_t *iin = first ? nullptr : iside[(p - 1) & 1];
+        const uint64_t vlo = first ? head : 0;
+        const uint64_t nt = first ? ntiles_user : ntiles_own;
+        uint32_t *ko = kside[p & 1], *io = p == 7 ? pb : iside[p & 1];
+        hipLaunchKernelGGL((digit_hist_kernel<kBlock, kRadixChunks>), dim3((uint32_t)nt), blk, 0,
+                           stream, kin, vlo, n + vlo, shift, (uint32_t)nt, hist);
+        hipError_t e = launch_scan_lookback(hist, 16 * nt, false, false, spine,
+                                            spine.total_slot(), stream);
+        if (e != hipSuccess)
+            return e;
+        if (first)
+            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, true, false>),
+                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
+                               shift, (uint32_t)nt, hist);
+        else if (p == 7)
+            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, false, true>),
+                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
+                               shift, (uint32_t)nt, hist);
+        else
+            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, false, false>),
+                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
+                               shift, (uint32_t)nt, hist);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace libscan

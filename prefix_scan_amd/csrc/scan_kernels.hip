@@ -464,7 +464,7 @@ static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, bo
     const uint32_t head = head_of(data);
     const uint64_t ntiles = tiles_for(n, head, T);
     uint32_t *abase = data - head;
-    uint64_t *desc = reinterpret_cast<uint64_t *>(s.body());
+    uint64_t *desc = s.desc();
     if constexpr (V <= 16) {
         if (persistent) {
         auto kern = inclusive ? scan_persistent_kernel<kBlock, V, true>

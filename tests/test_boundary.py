@@ -148,5 +148,7 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros(8, dtype=torch.int32)
     with pytest.raises(ValueError):
         ps.scan_exclusive_u32(t)
-    with pytest.raises(TypeError):
+    with pytest.raises((TypeError, ValueError)):
         ps.scan_exclusive_u32(torch.zeros(8, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        ps.scan_exclusive_u32([1, 2, 3])

@@ -1,0 +1,86 @@
+"""GPU parity of the segmented scan and segment sums against the CPU oracle.
+
+The workload: n = 2^26 u32 values uniform over [0, 2^16), regular segments of
+length 16 (many per tile) and 2^20 (many tiles per segment; the sums wrap past
+2^32); plus ragged lengths that divide nothing, segment lengths 1, 2, 3 and
+>= n, in-place operation, unaligned pointers and an output whose 16-byte
+phase differs from the input's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefix_scan_amd as ps
+import workloads
+from tests.gpu_util import first_mismatch, to_dev, to_host_u32
+
+pytestmark = pytest.mark.gpu
+
+
+def check(a, L, in_place=False, offset=0, out_offset=None):
+    ref, sref = oracle.segscan_u32(a, L)
+    t = to_dev(a, offset)
+    if in_place:
+        out = t
+    elif out_offset is not None:
+        out = to_dev(np.zeros(a.size, dtype=np.uint32), out_offset)
+    else:
+        out = None
+    out, sums = ps.segscan_u32(t, L, out=out)
+    got = to_host_u32(out)
+    msg = first_mismatch(got, ref)
+    assert msg is None, "%s n=%d L=%d" % (msg, a.size, L)
+    gs = to_host_u32(sums)
+    msg = first_mismatch(gs, sref)
+    assert msg is None, "sums: %s n=%d L=%d" % (msg, a.size, L)
+
+
+@pytest.mark.parametrize("L", workloads.SEG_LENS)
+def test_workload_2p26(L):
+    check(workloads.seg_values(), L)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5, 7, 16, 100, 1000, 4096, 16384, 16385, 50000,
+                               1 << 20, (1 << 20) + 1])
+def test_lengths(L):
+    a = workloads.small_random_u32((1 << 20) + 12345, L, high=1 << 16)
+    check(a, L)
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 16383, 16384, 16385, 99999])
+def test_ragged_n(n):
+    a = workloads.small_random_u32(n, n)
+    for L in (1, 16, 1000, n, n + 7):
+        check(a, L)
+
+
+def test_in_place_and_unaligned():
+    a = workloads.small_random_u32(300001, 11, high=1 << 16)
+    check(a, 16, in_place=True)
+    check(a, 1000, in_place=True, offset=3)
+    check(a, 77, offset=1)
+    check(a, 77, offset=2, out_offset=1)     # output in a different 16-byte phase
+    check(a, 1 << 16, offset=0, out_offset=3)
+
+
+def test_wrapping_sums():
+    L = 1 << 20
+    a = np.full(3 * L, 0xFFFF, dtype=np.uint32)
+    check(a, L)
+
+
+def test_reduce_pin_cairn_weights():
+    # CAIRN "Concurrency", reduce and compact: sum of i % 7 over 10000 is 29994.
+    w = (np.arange(10000) % 7).astype(np.uint32)
+    _, sums = ps.segscan_u32(to_dev(w), 10000)
+    assert int(to_host_u32(sums)[0]) == 29994
+
+
+def test_no_sums_and_empty():
+    a = workloads.small_random_u32(5000, 2)
+    out, sums = ps.segscan_u32(to_dev(a), 64, seg_sums=None)
+    ref, _ = oracle.segscan_u32(a, 64)
+    assert sums is None and np.array_equal(to_host_u32(out), ref)
+    out, sums = ps.segscan_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), 5)
+    assert out.numel() == 0
