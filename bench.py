@@ -204,13 +204,133 @@ def suite(args, torch, ps):
         perm = torch.empty_like(k)
         row("radix 1-bit x32 %s n=2^25" % kind, k.numel(), 508,
             lambda: ps.radix_perm_u32(k, 1, perm=perm), reps=5, warm=1)
-        row("radix 4-bit x8 %s n=2^25" % kind, k.numel(), 124,
+        row("radix 4-bit x8 %s n=2^25" % kind, k.numel(), 152,
             lambda: ps.radix_perm_u32(k, 4, perm=perm), reps=5, warm=1)
         del k, perm
     return out
 
 
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (run on any host, from the result databases a GPU run
+# wrote; see the commands in PROFILE_COMMANDS).
+# --------------------------------------------------------------------------
+PROFILE_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o run -- "
+    "python3 bench.py --steps 20 --warmup 5 --no-cpu [--suite]",
+    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o run -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite]",
+    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o run -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite]",
+    "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
+    "gpurun_out/prof_write [--suite]",
+]
+COPY_KERNEL = "libscan::copy_kernel"
+SCAN_KERNEL = "libscan::scan_lookback_kernel"
+
+
+def _rocpd(path):
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "*_results.db")))
+    if not dbs:
+        raise SystemExit("no rocpd database under %s" % path)
+    return sqlite3.connect(dbs[0])
+
+
+def _short(name):
+    name = name.replace("unsigned int", "u32").replace("unsigned long", "u64")
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    tag = "suite" if suite else "scan_lookback_u32_n2p28"
+    cmds = [c.replace(" [--suite]", " --suite" if suite else "") for c in PROFILE_COMMANDS]
+
+    # Kernel trace statistics.
+    db = _rocpd(trace_dir)
+    top = db.execute("select name, total_calls, total_duration, average, percentage from top "
+                     "order by total_duration desc").fetchall()
+    lines = ["# Kernel trace: %s" % ("every primitive's workload (bench.py --suite)" if suite else
+                                     "U32 exclusive scan, n = 2^28 (bench.py headline)"), "",
+             "Commands (from the repository root on the MI355X box):", ""]
+    lines += ["    " + c for c in cmds[:1]] + ["    " + cmds[3], ""]
+    lines += ["| kernel | calls | total (us) | average (us) | % |", "|---|---|---|---|---|"]
+    for name, calls, total, avg, pct in top:
+        lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (_short(name), calls, total, avg, pct))
+    n = 1 << 28
+    scan_avg = [r for r in top if SCAN_KERNEL in r[0] and "<256, 32, false>" in r[0]]
+    copy_avg = [r for r in top if COPY_KERNEL in r[0]]
+    lines.append("")
+    if scan_avg:
+        us = scan_avg[0][3]
+        lines.append("Exclusive look-back scan of 2^28 u32: average %.2f us per launch = %.1f GB/s "
+                     "of algorithmic traffic (8 B/element), %.1f%% of the 8 TB/s HBM peak."
+                     % (us, 8.0 * n / (us * 1e-6) / 1e9, 100.0 * 8.0 * n / (us * 1e-6) / 8e12))
+    if copy_avg:
+        us = copy_avg[0][3]
+        lines.append("Copy kernel over the same 1 GiB: average %.2f us = %.1f GB/s." %
+                     (us, 8.0 * n / (us * 1e-6) / 1e9))
+    with open(os.path.join(prof, "%s_kernel_trace.md" % tag), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM byte counters, calibrated on the copy kernel (known 4n + 4n bytes).
+    def per_kernel(path, counter):
+        d = _rocpd(path)
+        rows = d.execute("select kernel_name, count(*), avg(value), avg(grid_size) from "
+                         "counters_collection where counter_name = ? group by kernel_name",
+                         (counter,)).fetchall()
+        return {r[0]: (r[1], r[2], r[3]) for r in rows}
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_name = [k for k in fetch if COPY_KERNEL in k and "<256, 8>" in k]
+    if not copy_name:
+        raise SystemExit("the copy kernel is missing from the counter runs")
+    known_kib = 4.0 * n / 1024
+    f_fetch = known_kib / fetch[copy_name[0]][1]
+    f_write = known_kib / write[copy_name[0]][1]
+    lines = ["# HBM traffic from FETCH_SIZE / WRITE_SIZE: %s" % (
+        "every primitive's workload" if suite else "U32 exclusive scan, n = 2^28"), "",
+        "Commands (each counter in a run of its own):", ""]
+    lines += ["    " + c for c in cmds[1:]] + [""]
+    lines += ["Calibration on `copy_kernel<256, 8>` over 2^28 u32 (1 GiB read and 1 GiB "
+              "written per dispatch): FETCH_SIZE reads %.1f KiB, WRITE_SIZE %.1f KiB, so the "
+              "scale factors are %.4f (fetch) and %.4f (write)." %
+              (fetch[copy_name[0]][1], write[copy_name[0]][1], f_fetch, f_write), "",
+              "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | calibrated bytes |",
+              "|---|---|---|---|---|"]
+    traffic = None
+    for k in sorted(fetch):
+        if k not in write:
+            continue
+        fk, wk = fetch[k][1], write[k][1]
+        b = (fk * f_fetch + wk * f_write) * 1024
+        lines.append("| `%s` | %d | %.1f | %.1f | %.4g |" % (_short(k), fetch[k][0], fk, wk, b))
+        if SCAN_KERNEL in k and "<256, 32, false>" in k:
+            traffic = b
+    if traffic is not None:
+        lines += ["", "Exclusive look-back scan of 2^28 u32: %.4g bytes per launch against %.4g "
+                  "algorithmic (ratio %.4f)." % (traffic, 8.0 * n, traffic / (8.0 * n))]
+    with open(os.path.join(prof, "%s_hbm_counters.md" % tag), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if traffic is not None and not suite:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump({"kernel": "scan_lookback_kernel<256, 32, false>", "n": n,
+                       "hbm_bytes_per_launch": round(traffic),
+                       "algorithmic_bytes_per_launch": 8 * n,
+                       "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),
+                       "kernel_source_hash": kernel_source_hash(),
+                       "commands": cmds}, f, indent=1)
+            f.write("\n")
+    print("wrote profiles/%s_kernel_trace.md and profiles/%s_hbm_counters.md" % (tag, tag))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        args = [a for a in sys.argv[2:] if a != "--suite"]
+        summarize_profiles(args[0], args[1], args[2], "--suite" in sys.argv)
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
