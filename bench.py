@@ -137,12 +137,13 @@ def headline(args, torch, ps):
         "data": "synthetic",
         "config": {"workload": "u32 exclusive scan in place, n=2^28 uniform over [0,2^32) seed 202, "
                                "total left on the device",
-                   "n": n, "algo": "single-pass chained carry (decoupled look-back)",
+                   "n": n, "algo": "single-pass chained carry (decoupled look-back), "
+                                       "two tiles of 512x16x4 in flight per workgroup",
                    "pct_hbm_peak": round(100.0 * n * 8 / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "scan_lookback_kernel", "avg_launch_ms": round(avg_launch, 5),
+                     "kernel": "scan_pipelined_kernel" + SCAN_SHAPE, "avg_launch_ms": round(avg_launch, 5),
                      "algorithmic_bytes_per_launch": 8 * n,
                      "copy_kernel_gbs": round(copy_gbs, 1),
                      "frac_of_copy": round(achieved / copy_gbs, 4)},
@@ -181,6 +182,8 @@ def suite(args, torch, ps):
         d = torch.from_numpy(workloads.uniform_u32(n, 202).view(np.int32)).to("cuda")
         row("scan exclusive lookback n=" + label, n, 8, lambda: ps.scan_exclusive_u32(d, want_total=False))
         row("scan inclusive lookback n=" + label, n, 8, lambda: ps.scan_inclusive_u32(d, want_total=False))
+        row("scan exclusive lookback_tile n=" + label, n, 8,
+            lambda: ps.scan_u32_ex(d, algo="lookback_tile", want_total=False))
         row("scan exclusive threepass n=" + label, n, 12,
             lambda: ps.scan_u32_ex(d, algo="threepass", want_total=False))
         dst = torch.empty_like(d)
@@ -225,7 +228,8 @@ PROFILE_COMMANDS = [
     "gpurun_out/prof_write [--suite]",
 ]
 COPY_KERNEL = "libscan::copy_kernel"
-SCAN_KERNEL = "libscan::scan_lookback_kernel"
+SCAN_KERNEL = "libscan::scan_pipelined_kernel"
+SCAN_SHAPE = "<512, 16, false>"        # the default shape of the exclusive scan
 
 
 def _rocpd(path):
@@ -260,7 +264,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
     for name, calls, total, avg, pct in top:
         lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (_short(name), calls, total, avg, pct))
     n = 1 << 28
-    scan_avg = [r for r in top if SCAN_KERNEL in r[0] and "<256, 32, false>" in r[0]]
+    scan_avg = [r for r in top if SCAN_KERNEL in r[0] and SCAN_SHAPE in r[0]]
     copy_avg = [r for r in top if COPY_KERNEL in r[0]]
     lines.append("")
     if scan_avg:
@@ -307,7 +311,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
         fk, wk = fetch[k][1], write[k][1]
         b = (fk * f_fetch + wk * f_write) * 1024
         lines.append("| `%s` | %d | %.1f | %.1f | %.4g |" % (_short(k), fetch[k][0], fk, wk, b))
-        if SCAN_KERNEL in k and "<256, 32, false>" in k:
+        if SCAN_KERNEL in k and SCAN_SHAPE in k:
             traffic = b
     if traffic is not None:
         lines += ["", "Exclusive look-back scan of 2^28 u32: %.4g bytes per launch against %.4g "
@@ -316,7 +320,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
         f.write("\n".join(lines) + "\n")
     if traffic is not None and not suite:
         with open(TRAFFIC_FILE, "w") as f:
-            json.dump({"kernel": "scan_lookback_kernel<256, 32, false>", "n": n,
+            json.dump({"kernel": "scan_pipelined_kernel" + SCAN_SHAPE, "n": n,
                        "hbm_bytes_per_launch": round(traffic),
                        "algorithmic_bytes_per_launch": 8 * n,
                        "fetch_scale": round(f_fetch, 5), "write_scale": round(f_write, 5),

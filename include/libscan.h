@@ -64,15 +64,15 @@ enum {
 
 /* Scan algorithms for scan_u32_ex. */
 enum {
-    LIBSCAN_ALGO_AUTO = 0,               /* LIBSCAN_ALGO_LOOKBACK */
-    LIBSCAN_ALGO_LOOKBACK = 1,           /* single pass: one workgroup per tile, tiles
-                                            numbered in arrival order, each tile's carry
-                                            chained from its predecessors' published sums */
-    LIBSCAN_ALGO_THREEPASS = 2,          /* reduce blocks / scan the sums / rescan blocks */
-    LIBSCAN_ALGO_LOOKBACK_PIPELINED = 3  /* the single pass on a grid-filling set of
-                                            workgroups that prefetch their next tile
-                                            while waiting for a carry (kept for
-                                            comparison) */
+    LIBSCAN_ALGO_AUTO = 0,           /* LIBSCAN_ALGO_LOOKBACK */
+    LIBSCAN_ALGO_LOOKBACK = 1,       /* single pass, chained carry between tiles, on a
+                                        grid-filling set of workgroups that hold two
+                                        tiles each and take a tile's carry only after
+                                        the next tile is loaded and published */
+    LIBSCAN_ALGO_THREEPASS = 2,      /* reduce blocks / scan the sums / rescan blocks */
+    LIBSCAN_ALGO_LOOKBACK_TILE = 3   /* single pass, one workgroup per tile that waits
+                                        for its carry right away (kept for
+                                        comparison) */
 };
 
 /* Text for a status code; for LIBSCAN_ERR_HIP, the text of the HIP error the

@@ -21,16 +21,16 @@ __all__ = [
     "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
     "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
     "compact_scratch_bytes", "radix_scratch_bytes",
-    "ALGO_AUTO", "ALGO_LOOKBACK", "ALGO_THREEPASS", "ALGO_LOOKBACK_PIPELINED",
+    "ALGO_AUTO", "ALGO_LOOKBACK", "ALGO_THREEPASS", "ALGO_LOOKBACK_TILE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libscan.so")
 
 OK = 0
 ERR_NULL, ERR_SIZE, ERR_ARG, ERR_SCRATCH, ERR_HIP, ERR_ALIGN = -1, -2, -3, -4, -5, -6
-ALGO_AUTO, ALGO_LOOKBACK, ALGO_THREEPASS, ALGO_LOOKBACK_PIPELINED = 0, 1, 2, 3
+ALGO_AUTO, ALGO_LOOKBACK, ALGO_THREEPASS, ALGO_LOOKBACK_TILE = 0, 1, 2, 3
 _ALGOS = {"auto": ALGO_AUTO, "lookback": ALGO_LOOKBACK, "threepass": ALGO_THREEPASS,
-          "lookback_pipelined": ALGO_LOOKBACK_PIPELINED}
+          "lookback_tile": ALGO_LOOKBACK_TILE}
 
 
 class LibscanError(RuntimeError):

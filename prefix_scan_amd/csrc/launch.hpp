@@ -9,26 +9,20 @@
 
 namespace libscan {
 
-// Tile shape of the single-pass scan: BLOCK threads (4 waves), V 16-byte
-// chunks per thread, so one tile is BLOCK * V * 4 u32 (128 KiB at V = 32).
-// Large tiles keep the number of carry hand-offs, each a wait on the
-// slowest of the tiles before, small against the bytes each moves.
+// Tile shape of the streaming kernels: 256 threads (4 waves); the scans
+// pick their own shapes (scan_kernels.hip).
 constexpr int kBlock = 256;
-constexpr int kChunks = 32;
-constexpr uint64_t kTile = (uint64_t)kBlock * kChunks * 4;
 
 // Scratch layout.  The caller's pointer is rounded up to 256 bytes; all
 // offsets below are from that aligned base.
 //
 // Header, the same for every entry point, never overwritten with data:
 //   [0, 8)      ticket A of the chained carry {epoch, next tile}
-//   [8, 12)     exit counter A (persistent kernels)
+//   [8, 12)     exit counter A (grid-filling kernels)
 //   [16, 24)    ticket B (the radix histogram scan)
 //   [24, 28)    exit counter B
 //   [64, 68)    total / count slot, used when the caller asks for the result
 //               on the host only
-//   [128, 144)  a line the persistent kernels read in place of a tile when
-//               they have nothing to prefetch (its contents are never used)
 // Body, from 256: each entry point's state (tile descriptors) first, then its
 // data (block sums, radix ping-pong rows).  Tickets and descriptors carry the
 // epoch of the launch that wrote them, so they stay valid from launch to
@@ -61,12 +55,11 @@ struct Scratch {
     uint64_t *desc() const { return desc_ptr; }
     uint32_t *total_slot() const { return reinterpret_cast<uint32_t *>(base + kTotalSlotOffset); }
     uint8_t *body() const { return base + kHeaderBytes; }
-    const uint32_t *dummy_line() const { return reinterpret_cast<const uint32_t *>(base + 128); }
 };
 
 // ---- scan (scan_kernels.hip) ----
-// persistent: the pipelined grid-filling kernel; else one workgroup per tile.
-hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+// pipelined: the grid-filling two-tile kernel; else one workgroup per tile.
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
                                 const Scratch &s, uint32_t *total_out, hipStream_t stream);
 int resident_grid(const void *kernel, int block);
 size_t scan_lookback_body_bytes(uint64_t n, uint32_t head);

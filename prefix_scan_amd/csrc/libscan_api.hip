@@ -174,7 +174,7 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
                 uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
                 hipStream_t stream)
 {
-    if (algo < LIBSCAN_ALGO_AUTO || algo > LIBSCAN_ALGO_LOOKBACK_PIPELINED)
+    if (algo < LIBSCAN_ALGO_AUTO || algo > LIBSCAN_ALGO_LOOKBACK_TILE)
         return LIBSCAN_ERR_ARG;
     if (fork_depth < -1 || fork_depth > 40)
         return LIBSCAN_ERR_ARG;
@@ -203,8 +203,8 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
         e = prepare_state(s, kKindDesc, 0, scan_lookback_body_bytes(n, 3), 1, stream);
         if (e != hipSuccess)
             return hip_status(e);
-        e = launch_scan_lookback(data, n, inclusive != 0, algo == LIBSCAN_ALGO_LOOKBACK_PIPELINED,
-                                 s, tot, stream);
+        e = launch_scan_lookback(data, n, inclusive != 0, algo != LIBSCAN_ALGO_LOOKBACK_TILE, s,
+                                 tot, stream);
     }
     if (e != hipSuccess)
         return hip_status(e);

@@ -81,56 +81,49 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
 }
 
 // ---------------------------------------------------------------------------
-// Persistent, software-pipelined variant of the same single-pass scan.
+// Pipelined variant of the same single-pass scan.
 //
-// A grid sized to fill the GPU once; every workgroup draws tile numbers from
-// the ticket and processes its tiles in increasing order.  While tile `cur`
-// is scanned and waits for its carry, the loads of the workgroup's next tile
-// are already in flight and the ticket for the one after is being drawn, so
-// the carry latency overlaps HBM traffic instead of idling the CU.
-//
-// Termination: a workgroup stops drawing at its first number >= ntiles and
-// then counts itself out on the exit counter; the last one out resets the
+// A chained carry makes each tile wait for the slowest of the tiles before
+// it, and under a saturated HBM their loads land microseconds apart.  Here a
+// tile's carry is taken a whole load latency after its aggregate went out,
+// so its predecessors have had the same time to publish theirs.  A grid
+// that fills the GPU once draws tile numbers from the ticket; each
+// workgroup holds two tiles in registers and, per step:
+//   1. draws the number of the tile after next and issues the loads of the
+//      next tile (the look-back window of the current tile goes out first);
+//   2. waits for the next tile, scans it locally and publishes its aggregate;
+//   3. only then folds the current tile's carry, publishes its prefix, and
+//      stores it.
+// Tiles are published in increasing order per workgroup and every tile
+// waits only on smaller ones, so the smallest tile without a prefix can
+// always advance.  A workgroup stops drawing at its first number past the
+// end and counts itself out on the exit counter; the last one out resets the
 // ticket (counter 0, epoch + 1) and the exit counter for the next launch.
-// Progress: a workgroup holds at most three tiles (cur < nxt < nn) and
-// publishes them in that order; every tile waits only on smaller tiles, so
-// the smallest unpublished tile can always advance.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 template <int BLOCK, int V, bool INCL>
-__global__ __launch_bounds__(BLOCK) void scan_persistent_kernel(uint32_t *__restrict__ abase,
-                                                                uint64_t vlo, uint64_t vhi,
-                                                                uint32_t ntiles, uint64_t *ticket,
-                                                                uint32_t *exits, uint64_t *desc,
-                                                                const uint32_t *dummy,
-                                                                uint32_t *total_out)
+__global__ __launch_bounds__(BLOCK) void scan_pipelined_kernel(uint32_t *__restrict__ abase,
+                                                               uint64_t vlo, uint64_t vhi,
+                                                               uint32_t ntiles, uint64_t *ticket,
+                                                               uint32_t *exits, uint64_t *desc,
+                                                               uint32_t *total_out)
 {
     using TS = TileScan<BLOCK, V>;
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     constexpr int kDrawer = BLOCK - kWave;       // lane 0 of the last wave
-    // Two cell buffers, alternating tile by tile: a wave may start the next
-    // tile's phase 1 while a slower one still reads this tile's cells.
-    __shared__ uint32_t s_cell[2][TS::NCELL];
+    // Three cell buffers in rotation: a tile's cells are written two steps
+    // after the buffer's previous tile was last read, with a barrier between.
+    __shared__ uint32_t s_cell[3][TS::NCELL];
     __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag, s_carry;
-    int buf = 0;
 
-    auto draw_raw = [&]() -> uint64_t {
-        return __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // Draws after the first need only the counter: a 32-bit add on the low
-    // half of the ticket word (it never carries into the epoch, since a
-    // launch draws fewer than 2^32 numbers).
+    auto tile_of = [&](uint32_t raw) -> uint32_t { return raw < ntiles ? raw : kNoTile; };
     auto draw_num = [&]() -> uint32_t {
         return __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(ticket), 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto tile_of = [&](uint64_t raw) -> uint32_t {
-        return (uint32_t)raw < ntiles ? (uint32_t)raw : kNoTile;
-    };
     uint32_t epoch = 0;
-    // Called by kDrawer once the workgroup has drawn its last number.
-    auto check_out = [&]() {
+    auto check_out = [&]() {                    // kDrawer, after its last draw
         const uint32_t before =
             __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (before == gridDim.x - 1) {
@@ -139,12 +132,16 @@ __global__ __launch_bounds__(BLOCK) void scan_persistent_kernel(uint32_t *__rest
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     };
+    auto whole = [&](uint32_t t) -> bool {
+        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    };
 
     if (threadIdx.x == kDrawer) {
-        const uint64_t o1 = draw_raw();
+        const uint64_t o1 =
+            __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         epoch = (uint32_t)(o1 >> 32);
-        const uint32_t c = tile_of(o1);
-        const uint32_t x = (c != kNoTile) ? tile_of(draw_num()) : kNoTile;
+        const uint32_t c = tile_of((uint32_t)o1);
+        const uint32_t x = c != kNoTile ? tile_of(draw_num()) : kNoTile;
         s_cur = c;
         s_nxt = x;
         s_tag = (epoch & 0x3FFFFFFFu) << 2;
@@ -157,131 +154,92 @@ __global__ __launch_bounds__(BLOCK) void scan_persistent_kernel(uint32_t *__rest
     if (cur == kNoTile)
         return;
 
-    auto whole = [&](uint32_t t) -> bool {
-        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    // Wave 0: publish a scanned tile's sum (the prefix itself for tile 0).
+    auto publish_agg = [&](uint32_t t, uint32_t agg) {
+        if (threadIdx.x == 0)
+            publish(desc, t, tag, t == 0 ? kStatusPrefix : kStatusAgg, agg);
     };
 
-    // Wave 0, after the first barrier: the tile's sum, published as an
-    // aggregate (or as the prefix, for tile 0), and the first look-back
-    // window requested.
-    auto publish_first = [&](uint32_t agg) -> LookbackWindow {
+    u32x4 a[V], b[V];
+    uint32_t wa[V], wb[V];
+    uint32_t agg_cur = 0;       // wave 0 only
+    int cb = 0;                 // cell buffer of `cur`
+
+    // Prologue: the first tile, loaded and scanned synchronously.
+    load_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, a);
+    TS::local(a, wa, s_cell[cb]);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        agg_cur = TS::cells(s_cell[cb]);
+        publish_agg(cur, agg_cur);
+    }
+
+    // One step: X holds `cur` (scanned, aggregate out), Y receives `nxt`.
+    auto step = [&](u32x4 (&X)[V], uint32_t (&wX)[V], u32x4 (&Y)[V], uint32_t (&wY)[V]) {
+        const int nb = cb == 2 ? 0 : cb + 1;
+        // 1. The current tile's first look-back window, the draw of the tile
+        //    after next, and the next tile's loads.
         LookbackWindow w0{0ull, true};
-        if (cur == 0) {
-            if (threadIdx.x == 0)
-                publish(desc, 0, tag, kStatusPrefix, agg);
-        } else {
-            if (threadIdx.x == 0)
-                publish(desc, cur, tag, kStatusAgg, agg);
+        if (threadIdx.x < kWave && cur != 0)
             w0 = lookback_load(desc, (int64_t)cur - 1);
+        const bool drawing = threadIdx.x == kDrawer && nxt != kNoTile;
+        const uint32_t nn_raw = drawing ? draw_num() : 0u;
+        const bool have_next = nxt != kNoTile;
+        if (have_next) {
+            if (whole(nxt))
+                load_tile_full<BLOCK, V>(abase, (uint64_t)nxt * T, Y);
+            else
+                load_tile<BLOCK, V>(abase, (uint64_t)nxt * T, vlo, vhi, Y);
+            // 2. Scan it and publish its sum.
+            TS::local(Y, wY, s_cell[nb]);
         }
-        return w0;
-    };
-    // Wave 0: folds `cur`'s carry and records it (and, on the last tile, the
-    // total) for the workgroup.
-    auto carry_of = [&](uint32_t agg, const LookbackWindow &w0) {
-        uint32_t excl = 0;
-        if (cur != 0) {
-            excl = lookback_from(desc, cur, tag, w0);
-            if (threadIdx.x == 0)
-                publish(desc, cur, tag, kStatusPrefix, excl + agg);
+        __syncthreads();
+        uint32_t agg_next = 0;
+        if (threadIdx.x < kWave) {
+            if (have_next) {
+                agg_next = TS::cells(s_cell[nb]);
+                publish_agg(nxt, agg_next);
+            }
+            // 3. The current tile's carry.
+            uint32_t excl = 0;
+            if (cur != 0) {
+                excl = lookback_from(desc, cur, tag, w0);
+                if (threadIdx.x == 0)
+                    publish(desc, cur, tag, kStatusPrefix, excl + agg_cur);
+            }
+            if (threadIdx.x == 0) {
+                s_carry = excl;
+                if (cur == ntiles - 1)
+                    *total_out = excl + agg_cur;
+            }
         }
-        if (threadIdx.x == 0) {
-            s_carry = excl;
-            if (cur == ntiles - 1)
-                *total_out = excl + agg;
-        }
-    };
-    auto settle_draw = [&](bool drawing, uint32_t nn_raw) {
         if (threadIdx.x == kDrawer) {
             const uint32_t nn = drawing ? tile_of(nn_raw) : kNoTile;
             s_nn = nn;
             if (drawing && nn == kNoTile)
                 check_out();
         }
-    };
-
-    // A partial tile (the first or the last of the array): guarded loads and
-    // stores, no prefetch.
-    auto slow_step = [&](u32x4 (&xa)[V]) {
-        uint32_t w[V];
-        load_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, xa);
-        TS::local(xa, w, s_cell[buf]);
-        const bool drawing = (threadIdx.x == kDrawer) && nxt != kNoTile;
-        const uint32_t nn_raw = drawing ? draw_num() : 0u;
         __syncthreads();
-        if (threadIdx.x < kWave) {
-            const uint32_t agg = TS::cells(s_cell[buf]);
-            carry_of(agg, publish_first(agg));
-        }
-        settle_draw(drawing, nn_raw);
-        __syncthreads();
+        TS::template apply<INCL>(X, wX, s_cell[cb], s_carry);
+        if (whole(cur))
+            store_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, X);
+        else
+            store_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, X);
         const uint32_t nn = s_nn;
-        TS::template apply<INCL>(xa, w, s_cell[buf], s_carry);
-        store_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, xa);
-        buf ^= 1;
         cur = nxt;
         nxt = nn;
+        agg_cur = agg_next;
+        cb = nb;
     };
 
-    // One pipeline step over a whole tile: finish `cur` from registers xa
-    // while the loads of `nxt` land in yb.
-    //
-    // Order of issue, chosen so that every wait leaves the prefetch in
-    // flight: the tile is scanned first (its only wait is for xa); the
-    // aggregate is published and the first look-back window requested; the
-    // ticket draw goes out; then the prefetch.  Waiting for the window or
-    // the draw then needs only the operations issued before the prefetch.
-    // The prefetch is issued unconditionally -- when there is no whole next
-    // tile it reads a 16-byte line of scratch into yb instead -- so the
-    // number of operations between a load and its first use never depends on
-    // a branch.  Returns whether yb holds the next tile; `cur` and `nxt`
-    // advance.
-    auto step = [&](u32x4 (&xa)[V], u32x4 (&yb)[V]) -> bool {
-        uint32_t w[V];
-        TS::local(xa, w, s_cell[buf]);
-        __syncthreads();
-        uint32_t agg = 0;
-        LookbackWindow w0{0ull, true};
-        if (threadIdx.x < kWave) {
-            agg = TS::cells(s_cell[buf]);
-            w0 = publish_first(agg);
-        }
-        const bool drawing = (threadIdx.x == kDrawer) && nxt != kNoTile;
-        const uint32_t nn_raw = drawing ? draw_num() : 0u;
-        const bool prefetch = nxt != kNoTile && whole(nxt);
-        load_tile_full_or<BLOCK, V>(abase, prefetch ? (uint64_t)nxt * T : 0, dummy, prefetch, yb);
-
-        if (threadIdx.x < kWave)
-            carry_of(agg, w0);
-        settle_draw(drawing, nn_raw);
-        __syncthreads();
-        const uint32_t nn = s_nn;
-        TS::template apply<INCL>(xa, w, s_cell[buf], s_carry);
-        store_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, xa);
-        buf ^= 1;
-        cur = nxt;
-        nxt = nn;
-        return prefetch;
-    };
-
-    u32x4 a[V], b[V];
+    // Two steps per trip so the buffers swap roles without register copies.
     for (;;) {
-        while (cur != kNoTile && !whole(cur))
-            slow_step(a);
+        step(a, wa, b, wb);
         if (cur == kNoTile)
             break;
-        load_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, a);
-        // The first step is peeled so that every step inside the loop is
-        // entered with the same operations outstanding; two steps per trip
-        // swap the buffers' roles without register copies.
-        if (step(a, b)) {
-            for (;;) {
-                if (!step(b, a))
-                    break;
-                if (!step(a, b))
-                    break;
-            }
-        }
+        step(b, wb, a, wa);
+        if (cur == kNoTile)
+            break;
     }
 }
 
@@ -437,69 +395,82 @@ int resident_grid(const void *kernel, int block)
     return grid;
 }
 
-// Tile chunks per thread for the look-back scan: kChunks unless the
-// LIBSCAN_SCAN_CHUNKS environment variable picks 4 or 16 (a tuning knob; it
+// Tile shapes of the single-pass scans, BLOCK threads x V chunks: by
+// default 512 x 16 (128 KiB) for the pipelined kernel, which holds two tiles,
+// and 512 x 32 (256 KiB) for the one-tile kernel.  LIBSCAN_SCAN_BLOCK /
+// LIBSCAN_SCAN_CHUNKS pick another instantiated shape (a tuning knob; it
 // never changes a result).
-static int scan_chunks()
+struct ScanShape {
+    int block, chunks;
+};
+
+static ScanShape scan_shape(bool pipelined)
 {
-    static int v = [] {
-        const char *e = getenv("LIBSCAN_SCAN_CHUNKS");
-        int c = e ? atoi(e) : kChunks;
-        return (c == 4 || c == 8 || c == 16 || c == 32) ? c : kChunks;
+    static ScanShape env = [] {
+        const char *eb = getenv("LIBSCAN_SCAN_BLOCK");
+        const char *ec = getenv("LIBSCAN_SCAN_CHUNKS");
+        return ScanShape{eb ? atoi(eb) : 0, ec ? atoi(ec) : 0};
     }();
-    return v;
+    if (env.block == 0 && env.chunks == 0)
+        return pipelined ? ScanShape{512, 16} : ScanShape{512, 32};
+    return env;
 }
 
 size_t scan_lookback_body_bytes(uint64_t n, uint32_t head)
 {
-    // Sized for the smallest tile (4 chunks per thread), the most tiles.
-    return (size_t)tiles_for(n, head, (uint64_t)kBlock * 4 * 4) * sizeof(uint64_t);
+    // Sized for the smallest tile shape (256 x 4 = 4096 elements), the most
+    // tiles any shape can need.
+    return (size_t)tiles_for(n, head, (uint64_t)256 * 4 * 4) * sizeof(uint64_t);
 }
 
-template <int V>
-static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+template <int BLOCK, int V>
+static hipError_t scan_lookback_v(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
                                   const Scratch &s, uint32_t *total_out, hipStream_t stream)
 {
-    constexpr uint64_t T = (uint64_t)kBlock * V * 4;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     const uint32_t head = head_of(data);
     const uint64_t ntiles = tiles_for(n, head, T);
     uint32_t *abase = data - head;
     uint64_t *desc = s.desc();
-    if constexpr (V <= 16) {
-        if (persistent) {
-        auto kern = inclusive ? scan_persistent_kernel<kBlock, V, true>
-                              : scan_persistent_kernel<kBlock, V, false>;
-        uint64_t grid = (uint64_t)resident_grid((const void *)kern, kBlock);
-        if (grid > ntiles)
-            grid = ntiles;
-        hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kBlock), 0, stream, abase,
-                           (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(), s.exits(), desc,
-                           s.dummy_line(), total_out);
-        return hipGetLastError();
+    constexpr bool kPipelined = (BLOCK == 256 || BLOCK == 512) && (V == 8 || V == 16);
+    if constexpr (kPipelined) {
+        if (pipelined) {
+            auto kern = inclusive ? scan_pipelined_kernel<BLOCK, V, true>
+                                  : scan_pipelined_kernel<BLOCK, V, false>;
+            uint64_t grid = (uint64_t)resident_grid((const void *)kern, BLOCK);
+            if (grid > ntiles)
+                grid = ntiles;
+            hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(BLOCK), 0, stream, abase,
+                               (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(), s.exits(),
+                               desc, total_out);
+            return hipGetLastError();
         }
     }
-    {
-        auto kern = inclusive ? scan_lookback_kernel<kBlock, V, true>
-                              : scan_lookback_kernel<kBlock, V, false>;
-        hipLaunchKernelGGL(kern, dim3((uint32_t)ntiles), dim3(kBlock), 0, stream, abase,
-                           (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(), desc, total_out);
-    }
+    auto kern = inclusive ? scan_lookback_kernel<BLOCK, V, true> : scan_lookback_kernel<BLOCK, V, false>;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)ntiles), dim3(BLOCK), 0, stream, abase, (uint64_t)head,
+                       n + head, (uint32_t)ntiles, s.ticket(), desc, total_out);
     return hipGetLastError();
 }
 
-hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool persistent,
+hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
                                 const Scratch &s, uint32_t *total_out, hipStream_t stream)
 {
-    switch (scan_chunks()) {
-    case 4: return scan_lookback_v<4>(data, n, inclusive, persistent, s, total_out, stream);
-    case 16: return scan_lookback_v<16>(data, n, inclusive, persistent, s, total_out, stream);
-    case 32:
-        // Two 32-chunk buffers do not fit a wave's registers: the pipelined
-        // kernel stays at 16.
-        return persistent ? scan_lookback_v<16>(data, n, inclusive, true, s, total_out, stream)
-                          : scan_lookback_v<32>(data, n, inclusive, false, s, total_out, stream);
-    default: return scan_lookback_v<8>(data, n, inclusive, persistent, s, total_out, stream);
-    }
+    const ScanShape sh = scan_shape(pipelined);
+#define LIBSCAN_SHAPE(P, B, V)                                                                    \
+    if (pipelined == P && sh.block == B && sh.chunks == V)                                        \
+        return scan_lookback_v<B, V>(data, n, inclusive, P, s, total_out, stream);
+    LIBSCAN_SHAPE(true, 512, 16)
+    LIBSCAN_SHAPE(true, 512, 8)
+    LIBSCAN_SHAPE(true, 256, 16)
+    LIBSCAN_SHAPE(true, 256, 8)
+    LIBSCAN_SHAPE(false, 512, 32)
+    LIBSCAN_SHAPE(false, 512, 16)
+    LIBSCAN_SHAPE(false, 256, 32)
+    LIBSCAN_SHAPE(false, 256, 16)
+    LIBSCAN_SHAPE(false, 1024, 16)
+#undef LIBSCAN_SHAPE
+    return pipelined ? scan_lookback_v<512, 16>(data, n, inclusive, true, s, total_out, stream)
+                     : scan_lookback_v<512, 32>(data, n, inclusive, false, s, total_out, stream);
 }
 
 // The three-pass scheme's own tile: 256 threads x 4 chunks.

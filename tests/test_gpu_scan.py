@@ -66,7 +66,7 @@ def test_ragged_sizes(n):
     a = workloads.small_random_u32(n, n)
     for inclusive in (False, True):
         check(a, inclusive)
-        check(a, inclusive, algo="lookback_pipelined")
+        check(a, inclusive, algo="lookback_tile")
         check(a, inclusive, algo="threepass")
         check(a, inclusive, algo="threepass", fork_depth=3)
 
@@ -77,7 +77,7 @@ def test_unaligned_pointers(n, offset):
     a = workloads.small_random_u32(n, 31 * n + offset)
     for inclusive in (False, True):
         check(a, inclusive, offset=offset)
-        check(a, inclusive, algo="lookback_pipelined", offset=offset)
+        check(a, inclusive, algo="lookback_tile", offset=offset)
         check(a, inclusive, algo="threepass", offset=offset)
         check(a, inclusive, algo="threepass", fork_depth=2, offset=offset)
 
@@ -141,7 +141,7 @@ def test_repeated_calls_reuse_scratch():
     sizes = [1 << 20, 5000, 1 << 18, 1 << 22, 77, (1 << 20) + 3, 1, 8192, 3 << 20, 12345]
     for rep, n in enumerate(sizes * 2):
         a = workloads.small_random_u32(n, 900 + rep)
-        algo = "lookback" if rep % 3 else "lookback_pipelined"
+        algo = "lookback" if rep % 3 else "lookback_tile"
         check(a, rep % 2 == 1, algo=algo)
 
 

@@ -72,7 +72,7 @@ def test_every_entry_point_interleaved():
         scan_ok(a, "threepass", False)
         scan_ok(a, "lookback", True)
         segscan_ok(a, 1 << 15)
-        scan_ok(a, "lookback_pipelined", False)
+        scan_ok(a, "lookback_tile", False)
         radix_ok(keys[: 1000 + rep], 4)
         scan_ok(a[: 4097 + rep], "lookback", False)
         compact_ok(f[: 100003])
