@@ -1,0 +1,183 @@
+// pipeline.hpp -- the grid-filling two-tile driver of the chained carry,
+// shared by every single-pass kernel of the library on gfx950.
+//
+// A chained carry makes each tile wait for the slowest of the tiles before
+// it, and under a saturated HBM the loads of neighbouring tiles land
+// microseconds apart.  Here a grid that fills the GPU once draws tile
+// numbers from the ticket, and each workgroup holds two tiles in registers.
+// Per step it
+//   1. issues the current tile's first look-back window, draws the number of
+//      the tile after next, and issues the loads of the next tile;
+//   2. reduces the next tile locally and publishes its descriptor;
+//   3. only then folds the current tile's carry, publishes its prefix, and
+//      finishes the current tile (outputs and stores).
+// So a tile asks for its carry one full load latency after its own
+// aggregate went out, and its predecessors had the same time to publish.
+//
+// Tile numbers are drawn one at a time, so consecutive tiles go to different
+// workgroups that run side by side.  (Drawing several consecutive numbers
+// per atomic would relieve the one contended ticket word, but it hands runs
+// of consecutive tiles to one workgroup, which then finishes them one after
+// another while the next workgroup waits on the last of them: the chain
+// becomes serial.)  The ticket's rate -- one atomic per tile on one address
+// -- is what keeps tiles large.
+//
+// Progress: every tile a workgroup holds lies above its current tile, and
+// every drawn tile publishes its descriptor in step 2, as the next tile,
+// without waiting on anything; a tile waits only on smaller ones.  So the
+// workgroup with the smallest current tile looks back only over finished
+// tiles, and always advances.  A workgroup stops at its first number past
+// the end and counts itself out on the exit counter; the last one out resets
+// the ticket (counter 0, epoch + 1) and the exit counter for the next
+// launch, so no launch clears anything.
+//
+// The per-operation part is a policy type `Op`:
+//   static constexpr int BLOCK;            threads per workgroup
+//   struct Regs;                           one tile's per-thread registers
+//   struct Cells;                          one tile's LDS between phases
+//   void load(Regs &, uint32_t tile);      issue the tile's loads
+//   void local(Regs &, Cells &, uint32_t tile);   phase 1 (all threads)
+//   TileInfo summary(Cells &, uint32_t tile);     phase 2 (wave 0 only)
+//   void finish(Regs &, Cells &, uint32_t tile, uint32_t carry);
+//                                          outputs + stores (all threads;
+//                                          may hold barriers of its own)
+//   void last(uint32_t carry, const TileInfo &);  thread 0, last tile only
+#pragma once
+
+#include "device_common.hpp"
+
+namespace libscan {
+
+// What phase 2 learned about a tile.
+struct TileInfo {
+    uint32_t value;     // published value: the tile's aggregate, or -- when
+                        // `final` -- its inclusive prefix already
+    bool final;         // the value needs no carry (publish PREFIX at once)
+    bool need_carry;    // the tile's outputs depend on the tiles before it
+};
+
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+
+template <class Op>
+__device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_t *ticket,
+                                                uint32_t *exits, uint64_t *desc)
+{
+    constexpr int BLOCK = Op::BLOCK;
+    constexpr int kDrawer = BLOCK - kWave;       // lane 0 of the last wave
+    // Three cell buffers in rotation: a tile's cells are written two steps
+    // after the buffer's previous tile was last read, with barriers between.
+    __shared__ typename Op::Cells s_cells[3];
+    __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag, s_carry;
+
+    auto tile_of = [&](uint32_t raw) -> uint32_t { return raw < ntiles ? raw : kNoTile; };
+    auto draw_num = [&]() -> uint32_t {
+        return __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(ticket), 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    };
+    uint32_t epoch = 0;
+    auto check_out = [&]() {                    // kDrawer, after its last draw
+        const uint32_t before =
+            __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before == gridDim.x - 1) {
+            __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ticket, (uint64_t)(epoch + 1) << 32, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    if (threadIdx.x == kDrawer) {
+        const uint64_t o1 =
+            __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        epoch = (uint32_t)(o1 >> 32);
+        const uint32_t c = tile_of((uint32_t)o1);
+        const uint32_t x = c != kNoTile ? tile_of(draw_num()) : kNoTile;
+        s_cur = c;
+        s_nxt = x;
+        s_tag = (epoch & 0x3FFFFFFFu) << 2;
+        if (x == kNoTile)
+            check_out();
+    }
+    __syncthreads();
+    uint32_t cur = s_cur, nxt = s_nxt;
+    const uint32_t tag = s_tag;
+    if (cur == kNoTile)
+        return;
+
+    // Wave 0: a reduced tile's descriptor (tile 0's aggregate is its prefix).
+    auto publish_info = [&](uint32_t t, const TileInfo &in) {
+        if (threadIdx.x == 0)
+            publish(desc, t, tag, (t == 0 || in.final) ? kStatusPrefix : kStatusAgg, in.value);
+    };
+
+    typename Op::Regs ra, rb;
+    TileInfo info_cur{0u, true, false};         // wave 0 only
+    int cb = 0;                                 // cell buffer of `cur`
+
+    // Prologue: the first tile, loaded and reduced synchronously.
+    op.load(ra, cur);
+    op.local(ra, s_cells[cb], cur);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        info_cur = op.summary(s_cells[cb], cur);
+        publish_info(cur, info_cur);
+    }
+
+    // One step: X holds `cur` (reduced, descriptor out), Y receives `nxt`.
+    auto step = [&](typename Op::Regs &X, typename Op::Regs &Y) {
+        const int nb = cb == 2 ? 0 : cb + 1;
+        const bool carry_needed = cur != 0 && info_cur.need_carry;     // wave 0
+        LookbackWindow w0{0ull, true};
+        if (threadIdx.x < kWave && carry_needed)
+            w0 = lookback_load(desc, (int64_t)cur - 1);
+        const bool drawing = threadIdx.x == kDrawer && nxt != kNoTile;
+        const uint32_t nn_raw = drawing ? draw_num() : 0u;
+        const bool have_next = nxt != kNoTile;
+        if (have_next) {
+            op.load(Y, nxt);
+            op.local(Y, s_cells[nb], nxt);
+        }
+        __syncthreads();
+        TileInfo info_next{0u, true, false};
+        if (threadIdx.x < kWave) {
+            if (have_next) {
+                info_next = op.summary(s_cells[nb], nxt);
+                publish_info(nxt, info_next);
+            }
+            uint32_t excl = 0;
+            if (carry_needed)
+                excl = lookback_from(desc, cur, tag, w0);
+            if (threadIdx.x == 0) {
+                if (cur != 0 && !info_cur.final)
+                    publish(desc, cur, tag, kStatusPrefix, excl + info_cur.value);
+                s_carry = excl;
+                if (cur == ntiles - 1)
+                    op.last(excl, info_cur);
+            }
+        }
+        if (threadIdx.x == kDrawer) {
+            const uint32_t nn = drawing ? tile_of(nn_raw) : kNoTile;
+            s_nn = nn;
+            if (drawing && nn == kNoTile)
+                check_out();
+        }
+        __syncthreads();
+        op.finish(X, s_cells[cb], cur, s_carry);
+        const uint32_t nn = s_nn;
+        cur = nxt;
+        nxt = nn;
+        info_cur = info_next;
+        cb = nb;
+    };
+
+    // Two steps per trip so the register sets swap roles without copies.
+    for (;;) {
+        step(ra, rb);
+        if (cur == kNoTile)
+            break;
+        step(rb, ra);
+        if (cur == kNoTile)
+            break;
+    }
+}
+
+}  // namespace libscan

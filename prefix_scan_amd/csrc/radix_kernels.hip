@@ -26,11 +26,18 @@
 // (four stable one-bit splits) and writes each digit's run to its base.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace libscan {
 
-constexpr int kRadixChunks = 4;     // 256 threads x 4 chunks: 4096 keys per tile
+// Digit passes: 256 threads x 4 chunks, 4096 keys per tile.
+constexpr int kRadixChunks = 4;
 constexpr uint64_t kRadixTile = (uint64_t)kBlock * kRadixChunks * 4;
+// One-bit passes: 512 threads x 4 chunks, 8192 keys per tile (two tiles of
+// pairs in flight per workgroup).
+constexpr int kR1Block = 512;
+constexpr int kR1Chunks = 4;
+constexpr uint64_t kR1Tile = (uint64_t)kR1Block * kR1Chunks * 4;
 
 // ---------------------------------------------------------------------------
 // Ones per bit over the whole array (for the one-bit passes' Z).
@@ -76,112 +83,167 @@ __global__ __launch_bounds__(BLOCK) void bit_ones_kernel(const uint32_t *__restr
 }
 
 // ---------------------------------------------------------------------------
-// One stable split of (key, index) pairs on bit `bit`.
+// One stable split of (key, index) pairs on bit `bit`, on the pipelined
+// chained carry (pipeline.hpp): a tile's aggregate is its zero count, its
+// carry the zeros before it.
 //   FIRST: keys come from the caller's array (virtual range [vlo, vhi)), and
 //          the index of each key is its position.
 //   LAST:  only the indices are written (into the caller's permutation).
 // ---------------------------------------------------------------------------
+template <int BLOCK_, int V, bool FIRST, bool LAST>
+struct Radix1Op {
+    static constexpr int BLOCK = BLOCK_;
+    static constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
+    using TS = TileScan<BLOCK, V>;
+    // The zero flags and their scan inside each chunk are recomputed from
+    // the keys where needed rather than held across the step.
+    struct Regs {
+        u32x4 key[V], idx[V];   // idx: not held by the first pass
+        uint32_t w[V];
+    };
+    struct Cells {
+        uint32_t c[TS::NCELL];
+        uint32_t kz;        // the tile's zero count
+    };
+
+    const uint32_t *kbase;
+    uint64_t vlo, vhi;
+    const uint32_t *iin;
+    uint32_t *kout, *iout;
+    uint32_t bit;
+    const uint32_t *ones;
+
+    __device__ __forceinline__ bool whole(uint32_t t) const
+    {
+        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    }
+
+    __device__ __forceinline__ void load(Regs &r, uint32_t t) const
+    {
+        const uint64_t vstart = (uint64_t)t * T;
+        if (whole(t)) {
+            load_tile_full<BLOCK, V>(kbase, vstart, r.key);
+            if (!FIRST)
+                load_tile_full<BLOCK, V>(iin, vstart, r.idx);
+        } else {
+            load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, r.key);
+            if (!FIRST)
+                load_tile<BLOCK, V>(iin, vstart, vlo, vhi, r.idx);
+        }
+    }
+
+    // Chunk k's zero flags, scanned inside the chunk; slots outside the
+    // array count as ones.
+    __device__ __forceinline__ u32x4 zeros_scanned(const Regs &r, int k, uint64_t vstart,
+                                                   bool all_in) const
+    {
+        u32x4 z;
+        z.x = !((r.key[k].x >> bit) & 1u);
+        z.y = !((r.key[k].y >> bit) & 1u);
+        z.z = !((r.key[k].z >> bit) & 1u);
+        z.w = !((r.key[k].w >> bit) & 1u);
+        if (!all_in) {
+            const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
+            z.x &= (uint32_t)(v0 + 0 >= vlo && v0 + 0 < vhi);
+            z.y &= (uint32_t)(v0 + 1 >= vlo && v0 + 1 < vhi);
+            z.z &= (uint32_t)(v0 + 2 >= vlo && v0 + 2 < vhi);
+            z.w &= (uint32_t)(v0 + 3 >= vlo && v0 + 3 < vhi);
+        }
+        z.y += z.x;
+        z.z += z.y;
+        z.w += z.z;
+        return z;
+    }
+
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
+    {
+        const uint64_t vstart = (uint64_t)t * T;
+        const bool all_in = whole(t);
+        const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const u32x4 z = zeros_scanned(r, k, vstart, all_in);
+            r.w[k] = wave_incl_add(z.w);
+        }
+        if (lane_id() == kWave - 1) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                c.c[k * TS::NW + wave] = r.w[k];
+        }
+    }
+
+    __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
+    {
+        const uint32_t kz = TS::cells(c.c);
+        if (threadIdx.x == 0)
+            c.kz = kz;
+        return TileInfo{kz, false, true};
+    }
+
+    __device__ __forceinline__ void last(uint32_t, const TileInfo &) const {}
+
+    // Stable split in LDS: zeros at their zero rank, ones after all zeros at
+    // their one rank (slot among valid keys minus zeros before it); then the
+    // zeros go to [zeros_before, +kz) and the ones to [Z + ones_before, +ko).
+    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t,
+                                           uint32_t zeros_before) const
+    {
+        __shared__ uint32_t s_key[LAST ? 1 : T], s_idx[T];
+        const uint64_t vstart = (uint64_t)t * T;
+        const uint64_t lo = vstart > vlo ? vstart : vlo;     // first valid slot
+        const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
+        const uint32_t skip = (uint32_t)(lo - vstart);        // invalid slots before it
+        const uint32_t kz = c.kz;
+        const bool all_in = whole(t);
+        u32x4 z[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            z[k] = zeros_scanned(r, k, vstart, all_in);
+        TS::template apply<false>(z, r.w, c.c, 0u);     // exclusive zero rank in the tile
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            const uint64_t v0 = vstart + e0;
+            const uint32_t i0 = (uint32_t)(v0 - vlo);
+            const uint32_t kk[4] = {r.key[k].x, r.key[k].y, r.key[k].z, r.key[k].w};
+            const uint32_t ii[4] = {FIRST ? i0 : r.idx[k].x, FIRST ? i0 + 1 : r.idx[k].y,
+                                    FIRST ? i0 + 2 : r.idx[k].z, FIRST ? i0 + 3 : r.idx[k].w};
+            const uint32_t zr[4] = {z[k].x, z[k].y, z[k].z, z[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!all_in && (v0 + j < vlo || v0 + j >= vhi))
+                    continue;
+                const uint32_t slot = e0 + j - skip;
+                const uint32_t p = ((kk[j] >> bit) & 1u) ? kz + (slot - zr[j]) : zr[j];
+                if (!LAST)
+                    s_key[p] = kk[j];
+                s_idx[p] = ii[j];
+            }
+        }
+        __syncthreads();
+        const uint64_t n = vhi - vlo;
+        const uint32_t valid = (uint32_t)(hi - lo);
+        const uint32_t ones_before = (uint32_t)(lo - vlo) - zeros_before;
+        const uint32_t Z = (uint32_t)n - ones[bit];
+        for (uint32_t p = threadIdx.x; p < valid; p += BLOCK) {
+            const uint32_t dest = p < kz ? zeros_before + p : Z + ones_before + (p - kz);
+            if (!LAST)
+                kout[dest] = s_key[p];
+            iout[dest] = s_idx[p];
+        }
+    }
+};
+
+// Four waves per SIMD: two 512-thread workgroups per CU (128 VGPRs each).
 template <int BLOCK, int V, bool FIRST, bool LAST>
-__global__ __launch_bounds__(BLOCK) void radix1_pass_kernel(
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void radix1_pass_kernel(
     const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,
     const uint32_t *__restrict__ iin, uint32_t *__restrict__ kout, uint32_t *__restrict__ iout,
     uint32_t bit, const uint32_t *__restrict__ ones, uint32_t ntiles, uint64_t *ticket,
-    uint64_t *desc)
+    uint32_t *exits, uint64_t *desc)
 {
-    using TS = TileScan<BLOCK, V>;
-    constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
-    __shared__ uint32_t s_cell[TS::NCELL];
-    __shared__ uint32_t s_key[T], s_idx[T];
-    __shared__ uint32_t s_tile, s_tag, s_carry, s_zeros;
-
-    if (threadIdx.x == 0) {
-        const TileTicket tk = draw_ticket(ticket, ntiles);
-        s_tile = tk.tile;
-        s_tag = tk.tag;
-    }
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint32_t tag = s_tag;
-    const uint64_t vstart = (uint64_t)tile * T;
-    const uint64_t n = vhi - vlo;
-    const uint64_t lo = vstart > vlo ? vstart : vlo;     // first valid slot
-    const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
-    const uint32_t skip = (uint32_t)(lo - vstart);        // invalid slots before it
-
-    u32x4 key[V], idx[V], z[V];
-    uint32_t w[V];
-    load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, key);
-    if (!FIRST)
-        load_tile<BLOCK, V>(iin, vstart, vlo, vhi, idx);
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
-        if (FIRST) {
-            idx[k].x = (uint32_t)(v0 + 0 - vlo);
-            idx[k].y = (uint32_t)(v0 + 1 - vlo);
-            idx[k].z = (uint32_t)(v0 + 2 - vlo);
-            idx[k].w = (uint32_t)(v0 + 3 - vlo);
-        }
-        z[k].x = (v0 + 0 >= vlo && v0 + 0 < vhi) && !((key[k].x >> bit) & 1u);
-        z[k].y = (v0 + 1 >= vlo && v0 + 1 < vhi) && !((key[k].y >> bit) & 1u);
-        z[k].z = (v0 + 2 >= vlo && v0 + 2 < vhi) && !((key[k].z >> bit) & 1u);
-        z[k].w = (v0 + 3 >= vlo && v0 + 3 < vhi) && !((key[k].w >> bit) & 1u);
-    }
-    TS::local(z, w, s_cell);
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        const uint32_t kz = TS::cells(s_cell);
-        uint32_t excl = 0;
-        if (tile == 0) {
-            if (threadIdx.x == 0)
-                publish(desc, 0, tag, kStatusPrefix, kz);
-        } else {
-            if (threadIdx.x == 0)
-                publish(desc, tile, tag, kStatusAgg, kz);
-            excl = lookback(desc, tile, tag);
-            if (threadIdx.x == 0)
-                publish(desc, tile, tag, kStatusPrefix, excl + kz);
-        }
-        if (threadIdx.x == 0) {
-            s_carry = excl;
-            s_zeros = kz;
-        }
-    }
-    __syncthreads();
-    const uint32_t kz = s_zeros;
-
-    // Stable split in LDS: zeros at their zero rank, ones after all zeros at
-    // their one rank (slot among valid keys minus zeros before it).
-    TS::template apply<false>(z, w, s_cell, 0u);
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-        const uint64_t v0 = vstart + e0;
-        const uint32_t kk[4] = {key[k].x, key[k].y, key[k].z, key[k].w};
-        const uint32_t ii[4] = {idx[k].x, idx[k].y, idx[k].z, idx[k].w};
-        const uint32_t zr[4] = {z[k].x, z[k].y, z[k].z, z[k].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (v0 + j < vlo || v0 + j >= vhi)
-                continue;
-            const uint32_t slot = e0 + j - skip;
-            const uint32_t p = ((kk[j] >> bit) & 1u) ? kz + (slot - zr[j]) : zr[j];
-            s_key[p] = kk[j];
-            s_idx[p] = ii[j];
-        }
-    }
-    __syncthreads();
-
-    const uint32_t zeros_before = s_carry;
-    const uint32_t valid = (uint32_t)(hi - lo);
-    const uint32_t ones_before = (uint32_t)(lo - vlo) - zeros_before;
-    const uint32_t Z = (uint32_t)n - ones[bit];
-    for (uint32_t p = threadIdx.x; p < valid; p += BLOCK) {
-        const uint32_t dest = p < kz ? zeros_before + p : Z + ones_before + (p - kz);
-        if (!LAST)
-            kout[dest] = s_key[p];
-        iout[dest] = s_idx[p];
-    }
+    Radix1Op<BLOCK, V, FIRST, LAST> op{kbase, vlo, vhi, iin, kout, iout, bit, ones};
+    pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
 // ---------------------------------------------------------------------------
@@ -444,23 +506,23 @@ hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bit
             grid = 2048;
         hipLaunchKernelGGL((bit_ones_kernel<kBlock, kRadixChunks>), dim3((uint32_t)grid), blk, 0,
                            stream, kuser, (uint64_t)head, n + head, ones);
+        const uint64_t nt_user = tiles_for(n, head, kR1Tile);
+        const uint64_t nt_own = tiles_for(n, 0, kR1Tile);
+        auto k_first = radix1_pass_kernel<kR1Block, kR1Chunks, true, false>;
+        auto k_mid = radix1_pass_kernel<kR1Block, kR1Chunks, false, false>;
+        auto k_last = radix1_pass_kernel<kR1Block, kR1Chunks, false, true>;
         for (uint32_t b = 0; b < 32; ++b) {
             uint32_t *ko = kside[b & 1], *io = b == 31 ? pb : iside[b & 1];
-            if (b == 0)
-                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, true, false>),
-                                   dim3((uint32_t)ntiles_user), blk, 0, stream, kuser,
-                                   (uint64_t)head, n + head, nullptr, ko, io, b, ones,
-                                   (uint32_t)ntiles_user, s.ticket(), desc);
-            else if (b == 31)
-                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, false, true>),
-                                   dim3((uint32_t)ntiles_own), blk, 0, stream, kside[(b - 1) & 1],
-                                   0ull, n, iside[(b - 1) & 1], ko, io, b, ones,
-                                   (uint32_t)ntiles_own, s.ticket(), desc);
-            else
-                hipLaunchKernelGGL((radix1_pass_kernel<kBlock, kRadixChunks, false, false>),
-                                   dim3((uint32_t)ntiles_own), blk, 0, stream, kside[(b - 1) & 1],
-                                   0ull, n, iside[(b - 1) & 1], ko, io, b, ones,
-                                   (uint32_t)ntiles_own, s.ticket(), desc);
+            const bool first = b == 0;
+            auto kern = first ? k_first : (b == 31 ? k_last : k_mid);
+            const uint64_t nt = first ? nt_user : nt_own;
+            uint64_t grid = (uint64_t)resident_grid((const void *)kern, kR1Block);
+            if (grid > nt)
+                grid = nt;
+            hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kR1Block), 0, stream,
+                               first ? kuser : kside[(b - 1) & 1], first ? (uint64_t)head : 0ull,
+                               first ? n + head : n, first ? nullptr : iside[(b - 1) & 1], ko, io,
+                               b, ones, (uint32_t)nt, s.ticket(), s.exits(), desc);
         }
         return hipGetLastError();
     }

@@ -16,6 +16,7 @@
 //    for the fork-depth knob.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pipeline.hpp"
 
 #include <stdlib.h>
 
@@ -81,26 +82,58 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined variant of the same single-pass scan.
-//
-// A chained carry makes each tile wait for the slowest of the tiles before
-// it, and under a saturated HBM their loads land microseconds apart.  Here a
-// tile's carry is taken a whole load latency after its aggregate went out,
-// so its predecessors have had the same time to publish theirs.  A grid
-// that fills the GPU once draws tile numbers from the ticket; each
-// workgroup holds two tiles in registers and, per step:
-//   1. draws the number of the tile after next and issues the loads of the
-//      next tile (the look-back window of the current tile goes out first);
-//   2. waits for the next tile, scans it locally and publishes its aggregate;
-//   3. only then folds the current tile's carry, publishes its prefix, and
-//      stores it.
-// Tiles are published in increasing order per workgroup and every tile
-// waits only on smaller ones, so the smallest tile without a prefix can
-// always advance.  A workgroup stops drawing at its first number past the
-// end and counts itself out on the exit counter; the last one out resets the
-// ticket (counter 0, epoch + 1) and the exit counter for the next launch.
+// Pipelined variant of the same single-pass scan: a grid that fills the GPU
+// once, two tiles per workgroup, a tile's carry folded only after the next
+// tile is loaded and its aggregate published (pipeline.hpp).
 // ---------------------------------------------------------------------------
-constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+template <int BLOCK_, int V, bool INCL>
+struct ScanOp {
+    static constexpr int BLOCK = BLOCK_;
+    static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    using TS = TileScan<BLOCK, V>;
+    struct Regs {
+        u32x4 x[V];
+        uint32_t w[V];
+    };
+    struct Cells {
+        uint32_t c[TS::NCELL];
+    };
+
+    uint32_t *abase;
+    uint64_t vlo, vhi;
+    uint32_t *total_out;
+
+    __device__ __forceinline__ bool whole(uint32_t t) const
+    {
+        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    }
+
+    __device__ __forceinline__ void load(Regs &r, uint32_t t) const
+    {
+        if (whole(t))
+            load_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
+        else
+            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
+    }
+
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const { TS::local(r.x, r.w, c.c); }
+
+    __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
+    {
+        return TileInfo{TS::cells(c.c), false, true};
+    }
+
+    __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const { *total_out = carry + in.value; }
+
+    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
+    {
+        TS::template apply<INCL>(r.x, r.w, c.c, carry);
+        if (whole(t))
+            store_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
+        else
+            store_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
+    }
+};
 
 template <int BLOCK, int V, bool INCL>
 __global__ __launch_bounds__(BLOCK) void scan_pipelined_kernel(uint32_t *__restrict__ abase,
@@ -109,138 +142,8 @@ __global__ __launch_bounds__(BLOCK) void scan_pipelined_kernel(uint32_t *__restr
                                                                uint32_t *exits, uint64_t *desc,
                                                                uint32_t *total_out)
 {
-    using TS = TileScan<BLOCK, V>;
-    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    constexpr int kDrawer = BLOCK - kWave;       // lane 0 of the last wave
-    // Three cell buffers in rotation: a tile's cells are written two steps
-    // after the buffer's previous tile was last read, with a barrier between.
-    __shared__ uint32_t s_cell[3][TS::NCELL];
-    __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag, s_carry;
-
-    auto tile_of = [&](uint32_t raw) -> uint32_t { return raw < ntiles ? raw : kNoTile; };
-    auto draw_num = [&]() -> uint32_t {
-        return __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(ticket), 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    };
-    uint32_t epoch = 0;
-    auto check_out = [&]() {                    // kDrawer, after its last draw
-        const uint32_t before =
-            __hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (before == gridDim.x - 1) {
-            __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ticket, (uint64_t)(epoch + 1) << 32, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-    auto whole = [&](uint32_t t) -> bool {
-        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
-    };
-
-    if (threadIdx.x == kDrawer) {
-        const uint64_t o1 =
-            __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        epoch = (uint32_t)(o1 >> 32);
-        const uint32_t c = tile_of((uint32_t)o1);
-        const uint32_t x = c != kNoTile ? tile_of(draw_num()) : kNoTile;
-        s_cur = c;
-        s_nxt = x;
-        s_tag = (epoch & 0x3FFFFFFFu) << 2;
-        if (x == kNoTile)
-            check_out();
-    }
-    __syncthreads();
-    uint32_t cur = s_cur, nxt = s_nxt;
-    const uint32_t tag = s_tag;
-    if (cur == kNoTile)
-        return;
-
-    // Wave 0: publish a scanned tile's sum (the prefix itself for tile 0).
-    auto publish_agg = [&](uint32_t t, uint32_t agg) {
-        if (threadIdx.x == 0)
-            publish(desc, t, tag, t == 0 ? kStatusPrefix : kStatusAgg, agg);
-    };
-
-    u32x4 a[V], b[V];
-    uint32_t wa[V], wb[V];
-    uint32_t agg_cur = 0;       // wave 0 only
-    int cb = 0;                 // cell buffer of `cur`
-
-    // Prologue: the first tile, loaded and scanned synchronously.
-    load_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, a);
-    TS::local(a, wa, s_cell[cb]);
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        agg_cur = TS::cells(s_cell[cb]);
-        publish_agg(cur, agg_cur);
-    }
-
-    // One step: X holds `cur` (scanned, aggregate out), Y receives `nxt`.
-    auto step = [&](u32x4 (&X)[V], uint32_t (&wX)[V], u32x4 (&Y)[V], uint32_t (&wY)[V]) {
-        const int nb = cb == 2 ? 0 : cb + 1;
-        // 1. The current tile's first look-back window, the draw of the tile
-        //    after next, and the next tile's loads.
-        LookbackWindow w0{0ull, true};
-        if (threadIdx.x < kWave && cur != 0)
-            w0 = lookback_load(desc, (int64_t)cur - 1);
-        const bool drawing = threadIdx.x == kDrawer && nxt != kNoTile;
-        const uint32_t nn_raw = drawing ? draw_num() : 0u;
-        const bool have_next = nxt != kNoTile;
-        if (have_next) {
-            if (whole(nxt))
-                load_tile_full<BLOCK, V>(abase, (uint64_t)nxt * T, Y);
-            else
-                load_tile<BLOCK, V>(abase, (uint64_t)nxt * T, vlo, vhi, Y);
-            // 2. Scan it and publish its sum.
-            TS::local(Y, wY, s_cell[nb]);
-        }
-        __syncthreads();
-        uint32_t agg_next = 0;
-        if (threadIdx.x < kWave) {
-            if (have_next) {
-                agg_next = TS::cells(s_cell[nb]);
-                publish_agg(nxt, agg_next);
-            }
-            // 3. The current tile's carry.
-            uint32_t excl = 0;
-            if (cur != 0) {
-                excl = lookback_from(desc, cur, tag, w0);
-                if (threadIdx.x == 0)
-                    publish(desc, cur, tag, kStatusPrefix, excl + agg_cur);
-            }
-            if (threadIdx.x == 0) {
-                s_carry = excl;
-                if (cur == ntiles - 1)
-                    *total_out = excl + agg_cur;
-            }
-        }
-        if (threadIdx.x == kDrawer) {
-            const uint32_t nn = drawing ? tile_of(nn_raw) : kNoTile;
-            s_nn = nn;
-            if (drawing && nn == kNoTile)
-                check_out();
-        }
-        __syncthreads();
-        TS::template apply<INCL>(X, wX, s_cell[cb], s_carry);
-        if (whole(cur))
-            store_tile_full<BLOCK, V>(abase, (uint64_t)cur * T, X);
-        else
-            store_tile<BLOCK, V>(abase, (uint64_t)cur * T, vlo, vhi, X);
-        const uint32_t nn = s_nn;
-        cur = nxt;
-        nxt = nn;
-        agg_cur = agg_next;
-        cb = nb;
-    };
-
-    // Two steps per trip so the buffers swap roles without register copies.
-    for (;;) {
-        step(a, wa, b, wb);
-        if (cur == kNoTile)
-            break;
-        step(b, wb, a, wa);
-        if (cur == kNoTile)
-            break;
-    }
+    ScanOp<BLOCK, V, INCL> op{abase, vlo, vhi, total_out};
+    pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
 // ---------------------------------------------------------------------------

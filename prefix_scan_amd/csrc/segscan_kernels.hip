@@ -3,9 +3,9 @@
 //
 // Futhark 0.7.4 Futhark.Pass.ExtractKernels.Segmented names the two regimes:
 // Small (several segments per workgroup) and Large (several workgroups per
-// segment, partial results combined).  Here one single-pass kernel covers
-// both.  Segment s is entries [s*L, s*L + L); element i is a segment head
-// when i mod L == 0.  Inside a tile the scan uses the segmented operator on
+// segment, partial results combined).  Here one single-pass kernel on the
+// pipelined chained carry (pipeline.hpp) covers both.  Segment s is entries
+// [s*L, s*L + L); element i is a segment head when i mod L == 0.  Inside a tile the scan uses the segmented operator on
 // (head flag, value) pairs,
 //     (fa, va) . (fb, vb) = (fa | fb, fb ? vb : va + vb),
 // at every level: inside a chunk, across the wave (DPP), across the tile's
@@ -22,30 +22,50 @@
 // 4 bytes read + 4 written per element, plus 4 per segment.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace libscan {
 
-// Where the segment heads fall inside one tile.  `first` is the tile offset
-// of the first head at or after the tile start (may lie beyond the tile);
-// heads follow every L elements.  `seg_first` is the segment that head opens.
+// Where the segment heads fall inside one tile, in 32-bit tile offsets.
+// `first` is the offset of the first head at or after the tile start; heads
+// follow every L elements; `seg_first` is the segment that head opens.  Two
+// clamps keep everything in 32 bits without changing any answer: `first` is
+// held at T + 8 when it lies further out (no chunk of the tile, which looks
+// at most 4 past its end, can reach it), and L at 2^31 when larger (then a
+// tile, at most 2^17 long, holds one head at most, and both values put the
+// next head beyond it).
+//
+// Tile offsets are below 2^18, so x / L is one multiply and one shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): with s = 18 + ceil(log2 L) and m = ceil(2^s / L),
+// floor(x * m / 2^s) = floor(x / L) for every x < 2^18, because 2^s >= L * x
+// keeps the error x * (m - 2^s / L) / 2^s below 1 / L.
+struct DivL {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+__device__ __forceinline__ uint32_t div_l(const DivL &d, uint32_t x)
+{
+    return (uint32_t)(((uint64_t)x * d.mul) >> d.shift);
+}
+
 struct HeadMap {
-    uint64_t L;
-    uint64_t first;
+    uint32_t first;
+    uint32_t L;
+    DivL div;
     uint64_t seg_first;
-    uint32_t lg;          // log2 L when L is a power of two, else 64
 };
 
 // 5-bit mask: bit p set when tile offset e0 + p (p = 0..4) is a head.
 __device__ __forceinline__ uint32_t head_mask5(const HeadMap &h, uint32_t e0)
 {
-    uint64_t d;                        // distance from e0 to the next head
-    if ((uint64_t)e0 <= h.first) {
+    uint32_t d;                        // distance from e0 to the next head
+    if (e0 <= h.first) {
         d = h.first - e0;
     } else {
-        const uint64_t past = (uint64_t)e0 - h.first;      // < tile size
-        const uint64_t rem = (h.lg < 64) ? (past & (h.L - 1))
-                             : (h.L > 0xFFFFFFFFull ? past % h.L
-                                                    : (uint64_t)((uint32_t)past % (uint32_t)h.L));
+        const uint32_t past = e0 - h.first;
+        const uint32_t rem = past - div_l(h.div, past) * h.L;
         d = rem == 0 ? 0 : h.L - rem;
     }
     uint32_t m = 0;
@@ -53,102 +73,132 @@ __device__ __forceinline__ uint32_t head_mask5(const HeadMap &h, uint32_t e0)
         if (d < 5)
             m = 1u << d;
     } else {
-        for (uint64_t p = d; p < 5; p += h.L)
+        for (uint32_t p = d; p < 5; p += h.L)
             m |= 1u << p;
     }
     return m;
 }
 
-// Segment index of the segment that ends at tile offset e (e + 1 is a head).
-__device__ __forceinline__ uint64_t segment_ending_at(const HeadMap &h, uint64_t e)
+// Heads at tile offsets in (e_lo, e], where e_lo, the first valid offset,
+// is at or before h.first; first_eq: h.first == e_lo.
+__device__ __forceinline__ uint32_t heads_through(const HeadMap &h, uint32_t e, bool first_eq)
 {
-    const uint64_t next_head = e + 1;             // >= h.first
-    const uint64_t k = (h.lg < 64) ? ((next_head - h.first) >> h.lg) : (next_head - h.first) / h.L;
-    return h.seg_first + k - 1;
+    if (e < h.first)
+        return 0;
+    return div_l(h.div, e - h.first) + 1 - (first_eq ? 1u : 0u);
 }
 
-template <int BLOCK, int V, bool VEC_OUT>
-__global__ __launch_bounds__(BLOCK) void segscan_kernel(const uint32_t *__restrict__ ibase,
-                                                        uint32_t *obase, uint64_t vlo, uint64_t vhi,
-                                                        uint64_t L, uint32_t lg, uint32_t ntiles,
-                                                        uint64_t *ticket, uint64_t *desc,
-                                                        uint32_t *__restrict__ sums)
+// Segment index of the segment that ends at tile offset e (e + 1 is a head).
+__device__ __forceinline__ uint64_t segment_ending_at(const HeadMap &h, uint32_t e)
 {
-    constexpr int NW = BLOCK / kWave;
-    constexpr int NCELL = NW * V;
-    constexpr int CPL = (NCELL + kWave - 1) / kWave;
-    constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
+    return h.seg_first + div_l(h.div, e + 1 - h.first) - 1;
+}
+
+// SMALL_L: segments shorter than 4, whose sums go straight to memory; longer
+// ones stage a tile's sums in LDS (at most T/4 + 1 of them) and store them as
+// one contiguous run.
+template <int BLOCK_, int V, bool VEC_OUT, bool SMALL_L>
+struct SegscanOp {
+    static constexpr int BLOCK = BLOCK_;
+    static constexpr int NW = BLOCK / kWave;
+    static constexpr int NCELL = NW * V;
+    static constexpr int CPL = (NCELL + kWave - 1) / kWave;
+    static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     static_assert(V <= 16, "head masks are packed into one 64-bit word");
-    __shared__ uint32_t s_cf[NCELL], s_cv[NCELL];
-    __shared__ uint32_t s_tile, s_tag, s_carry;
+    struct Regs {
+        u32x4 x[V];
+        uint32_t we[V];     // segmented piece of the wave before this lane's chunk
+        uint64_t hm;        // head bits of each chunk
+        uint64_t em;        // segment-end bits of each chunk (the next element is a head)
+        uint32_t fe_bits;   // bit k: a head lies in the wave before chunk k's lane
+    };
+    struct Cells {
+        uint32_t f[NCELL], v[NCELL];
+    };
 
-    if (threadIdx.x == 0) {
-        const TileTicket tk = draw_ticket(ticket, ntiles);
-        s_tile = tk.tile;
-        s_tag = tk.tag;
+    const uint32_t *ibase;
+    uint32_t *obase;
+    uint64_t vlo, vhi, L;
+    uint32_t lg;            // log2 L when L is a power of two, else 64
+    DivL div;               // division by min(L, 2^31) of tile offsets
+    uint32_t *sums;
+
+    // Heads in tile t.  Element i sits at tile offset i + vlo - vstart.
+    __device__ __forceinline__ HeadMap heads(uint32_t t) const
+    {
+        const uint64_t vstart = (uint64_t)t * T;
+        uint64_t first;
+        HeadMap h;
+        if (vstart <= vlo) {
+            first = vlo - vstart;                   // element 0 is a head
+            h.seg_first = 0;
+        } else {
+            const uint64_t i_t = vstart - vlo;      // index at tile offset 0
+            const uint64_t s_t = lg < 64 ? (i_t >> lg) : i_t / L;
+            const uint64_t r = i_t - s_t * L;
+            first = r == 0 ? 0 : L - r;
+            h.seg_first = r == 0 ? s_t : s_t + 1;
+        }
+        h.first = first > T + 8 ? (uint32_t)(T + 8) : (uint32_t)first;
+        h.L = L > (1ull << 31) ? (1u << 31) : (uint32_t)L;
+        h.div = div;
+        return h;
     }
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint32_t tag = s_tag;
-    const uint64_t vstart = (uint64_t)tile * T;
-    const uint64_t n = vhi - vlo;
 
-    // Heads in this tile.  Element i sits at tile offset i + vlo - vstart.
-    HeadMap h;
-    h.L = L;
-    h.lg = lg;
-    if (vstart <= vlo) {
-        h.first = vlo - vstart;                 // element 0 is a head
-        h.seg_first = 0;
-    } else {
-        const uint64_t i_t = vstart - vlo;      // index at tile offset 0
-        const uint64_t s_t = (lg < 64) ? (i_t >> lg) : i_t / L;
-        const uint64_t r = i_t - s_t * L;
-        h.first = r == 0 ? 0 : L - r;
-        h.seg_first = r == 0 ? s_t : s_t + 1;
+    __device__ __forceinline__ void load(Regs &r, uint32_t t) const
+    {
+        const uint64_t vstart = (uint64_t)t * T;
+        if (vstart >= vlo && vstart + T <= vhi)
+            load_tile_full<BLOCK, V>(ibase, vstart, r.x);
+        else
+            load_tile<BLOCK, V>(ibase, vstart, vlo, vhi, r.x);
     }
-
-    u32x4 x[V];
-    load_tile<BLOCK, V>(ibase, vstart, vlo, vhi, x);
 
     // Phase 1: chunk-local segmented scans and the wave-level segmented scan
-    // of the chunk pieces.  hm: head bits of each chunk; fe/we: the piece of
-    // everything before this lane's chunk inside the wave.
-    uint64_t hm = 0;
-    uint32_t fe_bits = 0;
-    uint32_t we[V];
-    const uint32_t lane = lane_id();
-    const uint32_t wave = threadIdx.x / kWave;
+    // of the chunk pieces.
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
+    {
+        const HeadMap h = heads(t);
+        const uint32_t lane = lane_id();
+        const uint32_t wave = threadIdx.x / kWave;
+        r.hm = 0;
+        r.em = 0;
+        r.fe_bits = 0;
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-        const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-        const uint32_t m = head_mask5(h, e0) & 15u;
-        hm |= (uint64_t)m << (4 * k);
-        if (m & 2u) {} else x[k].y += x[k].x;
-        if (m & 4u) {} else x[k].z += x[k].y;
-        if (m & 8u) {} else x[k].w += x[k].z;
-        uint32_t f = m != 0u, v = x[k].w;
-        wave_seg_incl(f, v);
-        const uint32_t fprev = wave_shr1(f);
-        we[k] = wave_shr1(v);
-        fe_bits |= (fprev & 1u) << k;
-        if (lane == kWave - 1) {
-            s_cf[k * NW + wave] = f;
-            s_cv[k * NW + wave] = v;
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            const uint32_t m5 = head_mask5(h, e0);
+            const uint32_t m = m5 & 15u;
+            r.hm |= (uint64_t)m << (4 * k);
+            r.em |= (uint64_t)(m5 >> 1) << (4 * k);
+            if (!(m & 2u)) r.x[k].y += r.x[k].x;
+            if (!(m & 4u)) r.x[k].z += r.x[k].y;
+            if (!(m & 8u)) r.x[k].w += r.x[k].z;
+            uint32_t f = m != 0u, v = r.x[k].w;
+            wave_seg_incl(f, v);
+            const uint32_t fprev = wave_shr1(f);
+            r.we[k] = wave_shr1(v);
+            r.fe_bits |= (fprev & 1u) << k;
+            if (lane == kWave - 1) {
+                c.f[k * NW + wave] = f;
+                c.v[k * NW + wave] = v;
+            }
         }
     }
-    __syncthreads();
 
-    // Phase 2 (wave 0): exclusive segmented scan of the cells, the tile's
-    // piece, and the carry.
-    if (threadIdx.x < kWave) {
+    // Phase 2 (wave 0): exclusive segmented scan of the cells and the tile's
+    // piece.  A tile holding a head publishes its sum since the last head as
+    // a final prefix; a tile whose first element is a head needs no carry.
+    __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t t) const
+    {
+        const uint32_t lane = lane_id();
         uint32_t cf[CPL], cv[CPL];
         uint32_t mf = 0, mv = 0;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            const uint32_t c = lane * CPL + j;
-            cf[j] = c < (uint32_t)NCELL ? s_cf[c] : 0u;
-            cv[j] = c < (uint32_t)NCELL ? s_cv[c] : 0u;
+            const uint32_t q = lane * CPL + j;
+            cf[j] = q < (uint32_t)NCELL ? c.f[q] : 0u;
+            cv[j] = q < (uint32_t)NCELL ? c.v[q] : 0u;
             mv = cf[j] ? cv[j] : mv + cv[j];
             mf |= cf[j];
         }
@@ -157,102 +207,165 @@ __global__ __launch_bounds__(BLOCK) void segscan_kernel(const uint32_t *__restri
         uint32_t rf = wave_shr1(F), rv = wave_shr1(W);
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            const uint32_t c = lane * CPL + j;
-            if (c < (uint32_t)NCELL) {
-                s_cf[c] = rf;
-                s_cv[c] = rv;
+            const uint32_t q = lane * CPL + j;
+            if (q < (uint32_t)NCELL) {
+                c.f[q] = rf;
+                c.v[q] = rv;
             }
             rv = cf[j] ? cv[j] : rv + cv[j];
             rf |= cf[j];
         }
         const uint32_t tile_f = wave_bcast_last(F);
         const uint32_t tile_v = wave_bcast_last(W);
-
-        // A tile whose first valid element is a head needs no carry.
-        const bool need_carry = tile != 0 && h.first != 0;
-        uint32_t carry = 0;
-        if (tile_f) {
-            if (threadIdx.x == 0)
-                publish(desc, tile, tag, kStatusPrefix, tile_v);
-        } else if (threadIdx.x == 0) {
-            publish(desc, tile, tag, kStatusAgg, tile_v);
-        }
-        if (need_carry)
-            carry = lookback(desc, tile, tag);
-        if (!tile_f && threadIdx.x == 0)
-            publish(desc, tile, tag, kStatusPrefix, carry + tile_v);
-        if (threadIdx.x == 0)
-            s_carry = carry;
+        return TileInfo{tile_v, tile_f != 0u, heads(t).first != 0};
     }
-    __syncthreads();
+
+    __device__ __forceinline__ void last(uint32_t, const TileInfo &) const {}
 
     // Phase 3: every element's output, and the segment sums at segment ends.
-    const uint32_t carry = s_carry;
-    const uint64_t n_off = vhi - vstart;        // tile offset one past the last element
+    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
+    {
+        const HeadMap h = heads(t);
+        const uint32_t wave = threadIdx.x / kWave;
+        const uint64_t vstart = (uint64_t)t * T;
+        const uint64_t n = vhi - vlo;
+        const uint64_t n_off = vhi - vstart;        // tile offset one past the last element
+        // Inner tiles hold neither end of the array.
+        const bool inner = vstart >= vlo && vstart + T < vhi;
+        __shared__ uint32_t s_sum[SMALL_L ? 1 : T / 4 + 4];
+        const uint32_t e_lo = vstart < vlo ? (uint32_t)(vlo - vstart) : 0u;   // first valid offset
+        const uint32_t e_hi = n_off < T ? (uint32_t)n_off : (uint32_t)T;     // one past the last
+        const bool first_eq = h.first == e_lo;      // the first valid element is a head
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-        const uint32_t m = (uint32_t)(hm >> (4 * k)) & 15u;
-        const uint32_t cf = s_cf[k * NW + wave], cv = s_cv[k * NW + wave];
-        uint32_t p = cf ? cv : carry + cv;
-        p = ((fe_bits >> k) & 1u) ? we[k] : p + we[k];
-        if (!(m & 1u)) {
-            x[k].x += p;
-            if (!(m & 2u)) {
-                x[k].y += p;
-                if (!(m & 4u)) {
-                    x[k].z += p;
-                    if (!(m & 8u))
-                        x[k].w += p;
+        for (int k = 0; k < V; ++k) {
+            const uint32_t m = (uint32_t)(r.hm >> (4 * k)) & 15u;
+            const uint32_t cf = c.f[k * NW + wave], cv = c.v[k * NW + wave];
+            uint32_t p = cf ? cv : carry + cv;
+            p = ((r.fe_bits >> k) & 1u) ? r.we[k] : p + r.we[k];
+            if (!(m & 1u)) {
+                r.x[k].x += p;
+                if (!(m & 2u)) {
+                    r.x[k].y += p;
+                    if (!(m & 4u)) {
+                        r.x[k].z += p;
+                        if (!(m & 8u))
+                            r.x[k].w += p;
+                    }
+                }
+            }
+            if (sums) {
+                const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+                const uint32_t ends = (uint32_t)(r.em >> (4 * k)) & 15u;
+                const uint32_t vals[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+                if (SMALL_L) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint64_t e = (uint64_t)e0 + j;
+                        const bool inside = vstart + e >= vlo && e < n_off;
+                        if (!inside)
+                            continue;
+                        if ((ends >> j) & 1u)
+                            sums[segment_ending_at(h, e0 + j)] = vals[j];
+                        else if (e + 1 == n_off)
+                            sums[(n - 1) / L] = vals[j];
+                    }
+                } else {
+                    // A segment ends before each head and at the array's
+                    // last element; its slot counts the heads in (e_lo, e].
+                    uint32_t last = 0;
+                    if (!inner) {
+                        const uint64_t le = n_off - 1;       // the last element's offset
+                        if (le >= e0 && le < e0 + 4)
+                            last = 1u << (uint32_t)(le - e0);
+                    }
+                    const uint32_t put = ends | last;
+                    if (put) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t e = e0 + j;
+                            if (((put >> j) & 1u) && e >= e_lo && (inner || e < e_hi))
+                                s_sum[heads_through(h, e, first_eq)] = vals[j];
+                        }
+                    }
                 }
             }
         }
-        if (sums) {
-            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-            // Ends: the element before each head, and the array's last one.
-            const uint32_t m5 = head_mask5(h, e0);
-            const uint32_t vals[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+        if (VEC_OUT) {
+            if (vstart >= vlo && vstart + T <= vhi)
+                store_tile_full<BLOCK, V>(obase, vstart, r.x);
+            else
+                store_tile<BLOCK, V>(obase, vstart, vlo, vhi, r.x);
+        } else {
+            const uint64_t q0 = vstart / 4 + threadIdx.x;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint64_t e = (uint64_t)e0 + j;
-                const bool inside = vstart + e >= vlo && e < n_off;
-                if (!inside)
-                    continue;
-                if ((m5 >> (j + 1)) & 1u)
-                    sums[segment_ending_at(h, e)] = vals[j];
-                else if (e + 1 == n_off)
-                    sums[(n - 1) / L] = vals[j];
+            for (int k = 0; k < V; ++k) {
+                const uint64_t v0 = (q0 + (uint64_t)k * BLOCK) * 4;
+                const uint32_t vals[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (v0 + j >= vlo && v0 + j < vhi)
+                        obase[v0 + j] = vals[j];
             }
         }
-    }
-    if (VEC_OUT) {
-        store_tile<BLOCK, V>(obase, vstart, vlo, vhi, x);
-    } else {
-        const uint64_t q0 = vstart / 4 + threadIdx.x;
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const uint64_t v0 = (q0 + (uint64_t)k * BLOCK) * 4;
-            const uint32_t vals[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (v0 + j >= vlo && v0 + j < vhi)
-                    obase[v0 + j] = vals[j];
+        if (!SMALL_L && sums) {
+            __syncthreads();
+            // Segments ending here: heads in (e_lo, e_hi], plus the array's
+            // last segment when n is not a multiple of L.  The first is the
+            // segment of the first valid element.
+            uint32_t count = e_hi < h.first ? 0u : heads_through(h, e_hi, first_eq);
+            if (vstart + T >= vhi && n % L != 0)
+                count += 1;
+            const uint64_t s_a = first_eq ? h.seg_first : h.seg_first - 1;
+            for (uint32_t j = threadIdx.x; j < count; j += BLOCK)
+                sums[s_a + j] = s_sum[j];
         }
     }
+};
+
+template <int BLOCK, int V, bool VEC_OUT, bool SMALL_L>
+__global__ __launch_bounds__(BLOCK) void segscan_kernel(const uint32_t *__restrict__ ibase,
+                                                        uint32_t *obase, uint64_t vlo, uint64_t vhi,
+                                                        uint64_t L, uint32_t lg, DivL div,
+                                                        uint32_t ntiles,
+                                                        uint64_t *ticket, uint32_t *exits,
+                                                        uint64_t *desc, uint32_t *__restrict__ sums)
+{
+    SegscanOp<BLOCK, V, VEC_OUT, SMALL_L> op{ibase, obase, vlo, vhi, L, lg, div, sums};
+    pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
-// 256 threads x 16 chunks: 16384 elements per tile.
-constexpr int kSegChunks = 16;
+// Tile shape: 512 threads x 4 chunks, 8192 elements per tile (two tiles of
+// segmented-scan state fit in ~110 VGPRs, so two workgroups share a CU).
+// LIBSCAN_SEGSCAN_SHAPE=BxV picks another instantiated shape (a tuning knob;
+// it never changes a result).
+struct SegShape {
+    int block, chunks;
+};
+
+static SegShape segscan_shape()
+{
+    static SegShape sh = [] {
+        SegShape r{512, 4};
+        if (const char *e = getenv("LIBSCAN_SEGSCAN_SHAPE"))
+            if (sscanf(e, "%dx%d", &r.block, &r.chunks) != 2)
+                r = SegShape{512, 4};
+        return r;
+    }();
+    return sh;
+}
 
 size_t segscan_body_bytes(uint64_t n, uint64_t seg_len)
 {
     (void)seg_len;
-    return (size_t)tiles_for(n, 3, (uint64_t)kBlock * kSegChunks * 4) * sizeof(uint64_t);
+    // Sized for the smallest instantiated tile (512 x 4 = 8192 elements).
+    return (size_t)tiles_for(n, 3, (uint64_t)512 * 4 * 4) * sizeof(uint64_t);
 }
 
-hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
-                          uint32_t *seg_sums, const Scratch &s, hipStream_t stream)
+template <int BLOCK, int V>
+static hipError_t launch_segscan_v(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
+                                   uint32_t *seg_sums, const Scratch &s, hipStream_t stream)
 {
-    constexpr uint64_t T = (uint64_t)kBlock * kSegChunks * 4;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     const uint32_t head = head_of(in);
     const uint64_t ntiles = tiles_for(n, head, T);
     const uint32_t *ibase = in - head;
@@ -263,16 +376,33 @@ hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_
     uint32_t lg = 64;
     if ((seg_len & (seg_len - 1)) == 0)
         lg = floor_log2(seg_len);
-    uint64_t *desc = s.desc();
-    if (vec_out)
-        hipLaunchKernelGGL((segscan_kernel<kBlock, kSegChunks, true>), dim3((uint32_t)ntiles),
-                           dim3(kBlock), 0, stream, ibase, obase, (uint64_t)head, n + head, seg_len,
-                           lg, (uint32_t)ntiles, s.ticket(), desc, seg_sums);
-    else
-        hipLaunchKernelGGL((segscan_kernel<kBlock, kSegChunks, false>), dim3((uint32_t)ntiles),
-                           dim3(kBlock), 0, stream, ibase, obase, (uint64_t)head, n + head, seg_len,
-                           lg, (uint32_t)ntiles, s.ticket(), desc, seg_sums);
+    static_assert(T + 8 < (1u << 18), "tile offsets must stay below 2^18");
+    const uint64_t l32 = seg_len > (1ull << 31) ? (1ull << 31) : seg_len;
+    const uint32_t cl = floor_log2(l32) + ((l32 & (l32 - 1)) ? 1u : 0u);   // ceil(log2 L)
+    DivL div;
+    div.shift = 18 + cl;
+    div.mul = (uint32_t)(((1ull << div.shift) + l32 - 1) / l32);
+    const bool small = seg_len < 4;
+    auto kern = vec_out ? (small ? segscan_kernel<BLOCK, V, true, true> : segscan_kernel<BLOCK, V, true, false>)
+                        : (small ? segscan_kernel<BLOCK, V, false, true> : segscan_kernel<BLOCK, V, false, false>);
+    uint64_t grid = (uint64_t)resident_grid((const void *)kern, BLOCK);
+    if (grid > ntiles)
+        grid = ntiles;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(BLOCK), 0, stream, ibase, obase,
+                       (uint64_t)head, n + head, seg_len, lg, div, (uint32_t)ntiles, s.ticket(),
+                       s.exits(), s.desc(), seg_sums);
     return hipGetLastError();
+}
+
+hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
+                          uint32_t *seg_sums, const Scratch &s, hipStream_t stream)
+{
+    const SegShape sh = segscan_shape();
+    if (sh.block == 256 && sh.chunks == 8)
+        return launch_segscan_v<256, 8>(in, out, n, seg_len, seg_sums, s, stream);
+    if (sh.block == 512 && sh.chunks == 8)
+        return launch_segscan_v<512, 8>(in, out, n, seg_len, seg_sums, s, stream);
+    return launch_segscan_v<512, 4>(in, out, n, seg_len, seg_sums, s, stream);
 }
 
 }  // namespace libscan

@@ -84,3 +84,21 @@ def test_no_sums_and_empty():
     assert sums is None and np.array_equal(to_host_u32(out), ref)
     out, sums = ps.segscan_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), 5)
     assert out.numel() == 0
+
+
+@pytest.mark.parametrize("L", [(1 << 31) + 5, 1 << 33])
+def test_lengths_beyond_32_bits(L):
+    # One segment: the whole array, whatever the tile size.
+    a = workloads.small_random_u32(70001, 31, high=1 << 16)
+    check(a, L)
+    check(a, L, offset=2)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+@pytest.mark.parametrize("L", [4, 5, 16, 17, 4096, 8192, 16384])
+def test_tile_boundaries_every_phase(offset, L):
+    # n around whole multiples of the 8192- and 16384-element tiles, with the
+    # input in every 16-byte phase (tile 0 then starts inside the tile).
+    for n in (2 * 16384 - 1, 2 * 16384, 2 * 16384 + 3, 3 * 8192 + 1):
+        a = workloads.small_random_u32(n, 41 + L + offset, high=1 << 16)
+        check(a, L, offset=offset)
