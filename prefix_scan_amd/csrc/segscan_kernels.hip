@@ -334,6 +334,30 @@ __global__ __launch_bounds__(BLOCK) void segscan_kernel(const uint32_t *__restri
     pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
+// Independent tiles: when L divides the tile and the array's first element
+// sits at a multiple of L in its granule, every tile starts on a segment
+// head, so no carry crosses a tile.  One workgroup per tile then scans it
+// on its own (no ticket, no look-back), and several small workgroups share
+// each CU.
+template <int BLOCK, int V, bool VEC_OUT>
+__global__ __launch_bounds__(BLOCK) void segscan_independent_kernel(
+    const uint32_t *__restrict__ ibase, uint32_t *obase, uint64_t vlo, uint64_t vhi, uint64_t L,
+    uint32_t lg, DivL div, uint32_t *__restrict__ sums)
+{
+    using Op = SegscanOp<BLOCK, V, VEC_OUT, false>;
+    Op op{ibase, obase, vlo, vhi, L, lg, div, sums};
+    __shared__ typename Op::Cells s_cells;
+    typename Op::Regs r;
+    const uint32_t t = blockIdx.x;
+    op.load(r, t);
+    op.local(r, s_cells, t);
+    __syncthreads();
+    if (threadIdx.x < kWave)
+        (void)op.summary(s_cells, t);
+    __syncthreads();
+    op.finish(r, s_cells, t, 0u);
+}
+
 // Tile shape: 512 threads x 4 chunks, 8192 elements per tile (two tiles of
 // segmented-scan state fit in ~110 VGPRs, so two workgroups share a CU).
 // LIBSCAN_SEGSCAN_SHAPE=BxV picks another instantiated shape (a tuning knob;
@@ -383,6 +407,16 @@ static hipError_t launch_segscan_v(const uint32_t *in, uint32_t *out, uint64_t n
     div.shift = 18 + cl;
     div.mul = (uint32_t)(((1ull << div.shift) + l32 - 1) / l32);
     const bool small = seg_len < 4;
+    // Independent tiles (256 x 16 = 16384 elements each).
+    constexpr uint64_t TI = 256 * 16 * 4;
+    if (!small && TI % seg_len == 0 && head % seg_len == 0) {
+        const uint64_t nti = tiles_for(n, head, TI);
+        auto ik = vec_out ? segscan_independent_kernel<256, 16, true>
+                          : segscan_independent_kernel<256, 16, false>;
+        hipLaunchKernelGGL(ik, dim3((uint32_t)nti), dim3(256), 0, stream, ibase, obase,
+                           (uint64_t)head, n + head, seg_len, lg, div, seg_sums);
+        return hipGetLastError();
+    }
     auto kern = vec_out ? (small ? segscan_kernel<BLOCK, V, true, true> : segscan_kernel<BLOCK, V, true, false>)
                         : (small ? segscan_kernel<BLOCK, V, false, true> : segscan_kernel<BLOCK, V, false, false>);
     uint64_t grid = (uint64_t)resident_grid((const void *)kern, BLOCK);
