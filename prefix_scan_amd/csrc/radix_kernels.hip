@@ -301,8 +301,53 @@ __global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__res
     }
 }
 
-// Scatter one tile by its digit.  base[d * ntiles + tile] is the exclusive
-// scan of the digit-major histogram: where digit d of this tile starts.
+// Scatter by digit.  base[d * ntiles + tile] is the exclusive scan of the
+// digit-major histogram: where digit d of a tile starts in the output.
+// Tiles do not depend on each other, so a grid that fills the GPU walks
+// them round-robin and loads each workgroup's next tile into a second
+// register set while the current one is sorted.  A tile is sorted by digit
+// in LDS with two stable two-bit splits (low pair of digit bits first):
+// each element's rank in its bucket comes from one tile scan of packed
+// one-hot counters (four 16-bit buckets in two words), so each split costs
+// one pass through LDS.  Then each digit's run goes to its base.
+template <int BLOCK, int V, bool FIRST, bool LAST>
+struct DigitTile {
+    static constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
+    u32x4 key[V], idx[V];       // idx: not loaded by the first pass
+
+    // The same V loads (per array) for every tile: chunks outside the valid
+    // range read a clamped chunk inside it (their slots are never used), so
+    // the loads take no branch and can stay in flight while another tile is
+    // sorted.  A partly valid chunk is one aligned 16-byte granule, which
+    // never leaves its page.
+    __device__ __forceinline__ void load(const uint32_t *kbase, const uint32_t *iin, uint64_t vlo,
+                                         uint64_t vhi, uint32_t t)
+    {
+        const uint64_t qlo = vlo / 4, qhi = (vhi - 1) / 4;
+        const uint64_t q0 = (uint64_t)t * (T / 4) + threadIdx.x;
+        const u32x4 *ka = reinterpret_cast<const u32x4 *>(kbase);
+        const u32x4 *ia = reinterpret_cast<const u32x4 *>(iin);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            uint64_t q = q0 + (uint64_t)k * BLOCK;
+            q = q < qlo ? qlo : (q > qhi ? qhi : q);
+            key[k] = __builtin_nontemporal_load(ka + q);
+            if (!FIRST)
+                idx[k] = __builtin_nontemporal_load(ia + q);
+        }
+    }
+};
+
+// Packed one-hot counters of bucket b (0..3): buckets 0 and 1 in the low and
+// high half of w0, 2 and 3 in w1; nothing when !valid.  A tile holds at most
+// 2^15 pairs, so no half overflows into the next.
+__device__ __forceinline__ void bucket_onehot(uint32_t b, bool valid, uint32_t &w0, uint32_t &w1)
+{
+    const uint32_t one = valid ? (1u << ((b & 1u) * 16u)) : 0u;
+    w0 = b < 2 ? one : 0u;
+    w1 = b < 2 ? 0u : one;
+}
+
 template <int BLOCK, int V, bool FIRST, bool LAST>
 __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
     const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,
@@ -310,115 +355,193 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
     uint32_t shift, uint32_t ntiles, const uint32_t *__restrict__ base)
 {
     using TS = TileScan<BLOCK, V>;
-    constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
-    __shared__ uint32_t s_cell[TS::NCELL];
+    using Tile = DigitTile<BLOCK, V, FIRST, LAST>;
+    constexpr uint32_t T = Tile::T;
+    static_assert(T < (1u << 16), "bucket counts are 16-bit fields");
+    __shared__ uint32_t s_c0[TS::NCELL], s_c1[TS::NCELL];
     __shared__ uint32_t s_key[T], s_idx[T];
-    __shared__ uint32_t s_zeros, s_base[16], s_start[16];
-    const uint32_t tile = blockIdx.x;
-    const uint64_t vstart = (uint64_t)tile * T;
+    __shared__ uint32_t s_tot[2], s_base[16], s_start[16];
     const uint64_t n = vhi - vlo;
-    const uint64_t lo = vstart > vlo ? vstart : vlo;
-    const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
-    const uint32_t skip = (uint32_t)(lo - vstart);
-    const uint32_t valid = (uint32_t)(hi - lo);
 
-    // Valid pairs into LDS, in order, at slots 0 .. valid-1.
-    {
-        u32x4 key[V], idx[V];
-        load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, key);
-        if (!FIRST)
-            load_tile<BLOCK, V>(iin, vstart, vlo, vhi, idx);
+    // One two-bit split of `valid` pairs held in (kk, ii), element order
+    // (chunk, thread, element): they land in LDS slots [0, valid) ordered by
+    // bucket, stable.  Pairs beyond `valid` are ignored.
+    auto split = [&](const uint32_t (&kk)[V][4], const uint32_t (&ii)[V][4], uint32_t bit,
+                     uint32_t valid) {
+        u32x4 c0[V], c1[V];
+        uint32_t w0[V], w1[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-            const uint64_t v0 = vstart + e0;
-            const uint32_t kk[4] = {key[k].x, key[k].y, key[k].z, key[k].w};
-            const uint32_t ii[4] = {idx[k].x, idx[k].y, idx[k].z, idx[k].w};
+            uint32_t a[4], b[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (v0 + j < vlo || v0 + j >= vhi)
-                    continue;
-                s_key[e0 + j - skip] = kk[j];
-                s_idx[e0 + j - skip] = FIRST ? (uint32_t)(v0 + j - vlo) : ii[j];
-            }
+            for (int j = 0; j < 4; ++j)
+                bucket_onehot((kk[k][j] >> bit) & 3u, e0 + j < valid, a[j], b[j]);
+            c0[k] = u32x4{a[0], a[1], a[2], a[3]};
+            c1[k] = u32x4{b[0], b[1], b[2], b[3]};
         }
-    }
-    __syncthreads();
-
-    // Four stable one-bit splits, least significant digit bit first: the
-    // tile ends up sorted by digit, equal digits in their original order.
-    // Slots at or past `valid` count as ones, so they stay at the end.
-    for (uint32_t b = shift; b < shift + 4; ++b) {
-        u32x4 z[V];
-        uint32_t w[V];
-        uint32_t kk[V][4], ii[V][4];
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-            uint32_t zz[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t e = e0 + j;
-                kk[k][j] = e < valid ? s_key[e] : 0u;
-                ii[k][j] = e < valid ? s_idx[e] : 0u;
-                zz[j] = e < valid && !((kk[k][j] >> b) & 1u);
-            }
-            z[k].x = zz[0];
-            z[k].y = zz[1];
-            z[k].z = zz[2];
-            z[k].w = zz[3];
-        }
-        TS::local(z, w, s_cell);
+        TS::local(c0, w0, s_c0);
+        TS::local(c1, w1, s_c1);
         __syncthreads();
         if (threadIdx.x < kWave) {
-            const uint32_t kz = TS::cells(s_cell);
-            if (threadIdx.x == 0)
-                s_zeros = kz;
+            const uint32_t t0 = TS::cells(s_c0);
+            const uint32_t t1 = TS::cells(s_c1);
+            if (threadIdx.x == 0) {
+                s_tot[0] = t0;
+                s_tot[1] = t1;
+            }
         }
         __syncthreads();
-        const uint32_t kz = s_zeros;
-        TS::template apply<false>(z, w, s_cell, 0u);
+        const uint32_t t0 = s_tot[0], t1 = s_tot[1];
+        const uint32_t n0 = t0 & 0xFFFFu, n1 = t0 >> 16, n2 = t1 & 0xFFFFu;
+        const uint32_t start[4] = {0u, n0, n0 + n1, n0 + n1 + n2};
+        TS::template apply<false>(c0, w0, s_c0, 0u);
+        TS::template apply<false>(c1, w1, s_c1, 0u);
+        __syncthreads();                        // every read of the previous order is done
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
-            const uint32_t zr[4] = {z[k].x, z[k].y, z[k].z, z[k].w};
+            const uint32_t r0[4] = {c0[k].x, c0[k].y, c0[k].z, c0[k].w};
+            const uint32_t r1[4] = {c1[k].x, c1[k].y, c1[k].z, c1[k].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t e = e0 + j;
-                if (e >= valid)
+                if (e0 + j >= valid)
                     continue;
-                const uint32_t p = ((kk[k][j] >> b) & 1u) ? kz + (e - zr[j]) : zr[j];
+                const uint32_t bkt = (kk[k][j] >> bit) & 3u;
+                const uint32_t word = bkt < 2 ? r0[j] : r1[j];
+                const uint32_t rank = (bkt & 1u) ? (word >> 16) : (word & 0xFFFFu);
+                const uint32_t p = start[bkt] + rank;
                 s_key[p] = kk[k][j];
                 s_idx[p] = ii[k][j];
             }
         }
         __syncthreads();
-    }
+    };
 
-    // Where each digit's run starts in the tile and in the output.
-    if (threadIdx.x < kWave) {
+    // Wave 0, lanes < 16: digit `lane`'s base for tile t and the next base
+    // (its end).  Read before the next tile's loads go out, so waiting for
+    // them never waits for those loads.
+    auto read_bases = [&](uint32_t t, uint32_t &b0, uint32_t &b1) {
+        b0 = 0;
+        b1 = 0;
         const uint32_t d = lane_id();
-        uint32_t b0 = 0, cnt = 0;
-        if (d < 16) {
-            const uint64_t f = (uint64_t)d * ntiles + tile;
+        if (threadIdx.x < 16) {
+            const uint64_t f = (uint64_t)d * ntiles + t;
             b0 = base[f];
-            const uint32_t nx = (f + 1 < 16ull * ntiles) ? base[f + 1] : (uint32_t)n;
-            cnt = nx - b0;
+            b1 = (f + 1 < 16ull * ntiles) ? base[f + 1] : (uint32_t)n;
         }
-        const uint32_t incl = wave_incl_add(cnt);
-        if (d < 16) {
-            s_base[d] = b0;
-            s_start[d] = incl - cnt;
+    };
+
+    auto sort_tile = [&](const Tile &X, uint32_t t, uint32_t b0, uint32_t b1) {
+        const uint64_t vstart = (uint64_t)t * T;
+        const uint64_t lo = vstart > vlo ? vstart : vlo;
+        const uint64_t hi = vstart + T < vhi ? vstart + T : vhi;
+        const uint32_t skip = (uint32_t)(lo - vstart);
+        const uint32_t valid = (uint32_t)(hi - lo);
+        // The tile's valid pairs in order: registers hold them at slot
+        // e + skip; shift them to start at slot 0 only for partial tiles.
+        uint32_t kk[V][4], ii[V][4];
+        if (skip == 0) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+                kk[k][0] = X.key[k].x; kk[k][1] = X.key[k].y;
+                kk[k][2] = X.key[k].z; kk[k][3] = X.key[k].w;
+                if (FIRST) {
+                    const uint32_t i0 = (uint32_t)(vstart - vlo) + e0;
+                    ii[k][0] = i0; ii[k][1] = i0 + 1; ii[k][2] = i0 + 2; ii[k][3] = i0 + 3;
+                } else {
+                    ii[k][0] = X.idx[k].x; ii[k][1] = X.idx[k].y;
+                    ii[k][2] = X.idx[k].z; ii[k][3] = X.idx[k].w;
+                }
+            }
+        } else {
+            // Only the first pass's first tile starts after its slot 0.
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+                const uint32_t kv[4] = {X.key[k].x, X.key[k].y, X.key[k].z, X.key[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (e0 + j >= skip && e0 + j < skip + valid) {
+                        s_key[e0 + j - skip] = kv[j];
+                        s_idx[e0 + j - skip] =
+                            FIRST ? (uint32_t)(vstart + e0 + j - vlo)
+                                  : (j == 0 ? X.idx[k].x : j == 1 ? X.idx[k].y
+                                              : j == 2 ? X.idx[k].z : X.idx[k].w);
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kk[k][j] = e0 + j < valid ? s_key[e0 + j] : 0u;
+                    ii[k][j] = e0 + j < valid ? s_idx[e0 + j] : 0u;
+                }
+            }
         }
-    }
-    __syncthreads();
-    for (uint32_t p = threadIdx.x; p < valid; p += BLOCK) {
-        const uint32_t kv = s_key[p];
-        const uint32_t d = (kv >> shift) & 15u;
-        const uint32_t dest = s_base[d] + (p - s_start[d]);
-        if (!LAST)
-            kout[dest] = kv;
-        iout[dest] = s_idx[p];
+        split(kk, ii, shift, valid);
+        // The second split reads the first one's order back from LDS.
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kk[k][j] = s_key[e0 + j];
+                ii[k][j] = s_idx[e0 + j];
+            }
+        }
+        split(kk, ii, shift + 2, valid);
+        // Where each digit's run starts in the tile and in the output.
+        if (threadIdx.x < kWave) {
+            const uint32_t d = lane_id();
+            const uint32_t cnt = d < 16 ? b1 - b0 : 0u;
+            const uint32_t incl = wave_incl_add(cnt);
+            if (d < 16) {
+                s_base[d] = b0;
+                s_start[d] = incl - cnt;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < V * 4; ++i) {
+            const uint32_t p = (uint32_t)(i * BLOCK) + threadIdx.x;
+            if (p < valid) {
+                const uint32_t kv = s_key[p];
+                const uint32_t d = (kv >> shift) & 15u;
+                const uint32_t dest = s_base[d] + (p - s_start[d]);
+                if (!LAST)
+                    kout[dest] = kv;
+                iout[dest] = s_idx[p];
+            }
+        }
+        __syncthreads();                        // LDS is free for the next tile
+    };
+
+    uint32_t t = blockIdx.x;
+    if (t >= ntiles)
+        return;
+    Tile A, B;
+    uint32_t b0, b1;
+    A.load(kbase, iin, vlo, vhi, t);
+    for (;;) {
+        uint32_t tn = t + gridDim.x;
+        read_bases(t, b0, b1);
+        B.load(kbase, iin, vlo, vhi, tn < ntiles ? tn : t);
+        sort_tile(A, t, b0, b1);
+        if (tn >= ntiles)
+            break;
+        t = tn;
+        tn = t + gridDim.x;
+        read_bases(t, b0, b1);
+        A.load(kbase, iin, vlo, vhi, tn < ntiles ? tn : t);
+        sort_tile(B, t, b0, b1);
+        if (tn >= ntiles)
+            break;
+        t = tn;
     }
 }
 
@@ -547,18 +670,14 @@ hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bit
                                             spine.total_slot(), stream);
         if (e != hipSuccess)
             return e;
-        if (first)
-            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, true, false>),
-                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
-                               shift, (uint32_t)nt, hist);
-        else if (p == 7)
-            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, false, true>),
-                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
-                               shift, (uint32_t)nt, hist);
-        else
-            hipLaunchKernelGGL((digit_scatter_kernel<kBlock, kRadixChunks, false, false>),
-                               dim3((uint32_t)nt), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
-                               shift, (uint32_t)nt, hist);
+        auto sk = first ? digit_scatter_kernel<kBlock, kRadixChunks, true, false>
+                        : (p == 7 ? digit_scatter_kernel<kBlock, kRadixChunks, false, true>
+                                  : digit_scatter_kernel<kBlock, kRadixChunks, false, false>);
+        uint64_t grid = (uint64_t)resident_grid((const void *)sk, kBlock);
+        if (grid > nt)
+            grid = nt;
+        hipLaunchKernelGGL(sk, dim3((uint32_t)grid), blk, 0, stream, kin, vlo, n + vlo, iin, ko, io,
+                           shift, (uint32_t)nt, hist);
     }
     return hipGetLastError();
 }
