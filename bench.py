@@ -28,8 +28,8 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 METRIC = "GElem/s and % of HBM peak, U32 exclusive scan at n=2^28 (1 GPU)"
-KERNEL_SOURCES = ["prefix_scan_amd/csrc/device_common.hpp", "prefix_scan_amd/csrc/scan_kernels.hip",
-                  "prefix_scan_amd/csrc/launch.hpp"]
+KERNEL_SOURCES = ["prefix_scan_amd/csrc/device_common.hpp", "prefix_scan_amd/csrc/pipeline.hpp",
+                  "prefix_scan_amd/csrc/scan_kernels.hip", "prefix_scan_amd/csrc/launch.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_lookback_u32_n2p28_traffic.json")
 
 
@@ -154,7 +154,9 @@ def headline(args, torch, ps):
 
 
 def suite(args, torch, ps):
-    """One line per primitive workload (parity is the tests' job; this times)."""
+    """One line per primitive workload (parity is the tests' job; this times).
+    With --hbm-rows only the HBM-sized rows run (no 2^24 / 2^16 scans), so
+    every kernel runs at one size -- what the profile summaries group by."""
     out = []
 
     def row(name, n, bytes_per_elem, fn, reps=20, warm=3, setup=None):
@@ -177,8 +179,10 @@ def suite(args, torch, ps):
         print(json.dumps(rec), flush=True)
         out.append(rec)
 
-    for n, label in ((workloads.N_SCAN_LARGE, "2^28"), (workloads.N_SCAN_MID, "2^24 (cache-resident)"),
-                     (workloads.N_SCAN_SMALL, "2^16")):
+    sizes = [(workloads.N_SCAN_LARGE, "2^28")]
+    if not args.hbm_rows:
+        sizes += [(workloads.N_SCAN_MID, "2^24 (cache-resident)"), (workloads.N_SCAN_SMALL, "2^16")]
+    for n, label in sizes:
         d = torch.from_numpy(workloads.uniform_u32(n, 202).view(np.int32)).to("cuda")
         row("scan exclusive lookback n=" + label, n, 8, lambda: ps.scan_exclusive_u32(d, want_total=False))
         row("scan inclusive lookback n=" + label, n, 8, lambda: ps.scan_inclusive_u32(d, want_total=False))
@@ -219,14 +223,39 @@ def suite(args, torch, ps):
 # --------------------------------------------------------------------------
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o run -- "
-    "python3 bench.py --steps 20 --warmup 5 --no-cpu [--suite]",
+    "python3 bench.py --steps 20 --warmup 5 --no-cpu [--suite --hbm-rows]",
     "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o run -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite]",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite --hbm-rows]",
     "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o run -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite]",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite --hbm-rows]",
     "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
     "gpurun_out/prof_write [--suite]",
 ]
+
+
+def algorithmic_bytes(name, grid):
+    """Bytes a dispatch must move at the sizes of the --hbm-rows suite (scans
+    and copy at 2^28, compaction and segmented scan at 2^26, radix at 2^25),
+    or None for bookkeeping kernels."""
+    big = grid >= (1 << 16)            # threads: a data pass, not a table scan
+    n28, n26, n25 = 1 << 28, 1 << 26, 1 << 25
+    table = [
+        ("scan_pipelined_kernel", 8 * n28), ("copy_kernel", 8 * n28),
+        ("reduce_blocks_kernel", 4 * n28), ("compact_kernel", 8 * n26),
+        ("segscan_independent_kernel", 8 * n26 + 4 * (n26 // 16)),
+        ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
+        ("digit_hist_kernel", 4 * n25),
+    ]
+    for key, b in table:
+        if "::" + key + "<" in name:
+            return b
+    if "scan_lookback_kernel" in name or "scan_blocks_kernel" in name:
+        return 8 * n28 if big else None
+    if "radix1_pass_kernel" in name or "digit_scatter_kernel" in name:
+        first = ", true, false>" in name
+        last = ", false, true>" in name
+        return (12 if first or last else 16) * n25
+    return None
 COPY_KERNEL = "libscan::copy_kernel"
 SCAN_KERNEL = "libscan::scan_pipelined_kernel"
 SCAN_SHAPE = "<512, 16, false>"        # the default shape of the exclusive scan
@@ -250,68 +279,84 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     tag = "suite" if suite else "scan_lookback_u32_n2p28"
-    cmds = [c.replace(" [--suite]", " --suite" if suite else "") for c in PROFILE_COMMANDS]
+    cmds = [c.replace(" [--suite --hbm-rows]", " --suite --hbm-rows" if suite else "")
+             .replace(" [--suite]", " --suite" if suite else "") for c in PROFILE_COMMANDS]
+    n = 1 << 28
 
-    # Kernel trace statistics.
+    # Kernel trace statistics, per kernel and grid (one workload each).
     db = _rocpd(trace_dir)
-    top = db.execute("select name, total_calls, total_duration, average, percentage from top "
-                     "order by total_duration desc").fetchall()
-    lines = ["# Kernel trace: %s" % ("every primitive's workload (bench.py --suite)" if suite else
+    rows = db.execute("select name, grid_x * grid_y * grid_z, count(*), sum(duration), "
+                      "avg(duration) from kernels group by name, grid_x * grid_y * grid_z "
+                      "order by sum(duration) desc").fetchall()
+    total = sum(r[3] for r in rows) or 1
+    lines = ["# Kernel trace: %s" % ("the HBM-sized rows of bench.py --suite" if suite else
                                      "U32 exclusive scan, n = 2^28 (bench.py headline)"), "",
              "Commands (from the repository root on the MI355X box):", ""]
     lines += ["    " + c for c in cmds[:1]] + ["    " + cmds[3], ""]
-    lines += ["| kernel | calls | total (us) | average (us) | % |", "|---|---|---|---|---|"]
-    for name, calls, total, avg, pct in top:
-        lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (_short(name), calls, total, avg, pct))
-    n = 1 << 28
-    scan_avg = [r for r in top if SCAN_KERNEL in r[0] and SCAN_SHAPE in r[0]]
-    copy_avg = [r for r in top if COPY_KERNEL in r[0]]
+    lines += ["| kernel | grid (threads) | calls | total (us) | average (us) | % | "
+              "algorithmic GB/s |", "|---|---|---|---|---|---|---|"]
+    scan_us = copy_us = None
+    for name, grid, calls, tot, avg in rows:
+        ab = algorithmic_bytes(name, grid) if suite else (8 * n if (
+            SCAN_KERNEL in name or COPY_KERNEL in name) else None)
+        gbs = "%.1f" % (ab / avg) if ab else "-"          # bytes per ns = GB/s
+        lines.append("| `%s` | %d | %d | %.1f | %.2f | %.1f | %s |" % (
+            _short(name), grid, calls, tot / 1e3, avg / 1e3, 100.0 * tot / total, gbs))
+        if SCAN_KERNEL in name and SCAN_SHAPE in name:
+            scan_us = avg / 1e3
+        if COPY_KERNEL in name and grid >= (1 << 20):
+            copy_us = avg / 1e3
     lines.append("")
-    if scan_avg:
-        us = scan_avg[0][3]
+    if scan_us:
         lines.append("Exclusive look-back scan of 2^28 u32: average %.2f us per launch = %.1f GB/s "
                      "of algorithmic traffic (8 B/element), %.1f%% of the 8 TB/s HBM peak."
-                     % (us, 8.0 * n / (us * 1e-6) / 1e9, 100.0 * 8.0 * n / (us * 1e-6) / 8e12))
-    if copy_avg:
-        us = copy_avg[0][3]
+                     % (scan_us, 8.0 * n / (scan_us * 1e-6) / 1e9,
+                        100.0 * 8.0 * n / (scan_us * 1e-6) / 8e12))
+    if copy_us:
         lines.append("Copy kernel over the same 1 GiB: average %.2f us = %.1f GB/s." %
-                     (us, 8.0 * n / (us * 1e-6) / 1e9))
+                     (copy_us, 8.0 * n / (copy_us * 1e-6) / 1e9))
     with open(os.path.join(prof, "%s_kernel_trace.md" % tag), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    # HBM byte counters, calibrated on the copy kernel (known 4n + 4n bytes).
+    # HBM byte counters per kernel and grid, calibrated on the copy kernel
+    # over 2^28 (known: 1 GiB read, 1 GiB written).
     def per_kernel(path, counter):
         d = _rocpd(path)
-        rows = d.execute("select kernel_name, count(*), avg(value), avg(grid_size) from "
-                         "counters_collection where counter_name = ? group by kernel_name",
-                         (counter,)).fetchall()
-        return {r[0]: (r[1], r[2], r[3]) for r in rows}
+        rs = d.execute("select kernel_name, grid_size, count(*), avg(value) from "
+                       "counters_collection where counter_name = ? group by kernel_name, grid_size",
+                       (counter,)).fetchall()
+        return {(r[0], r[1]): (r[2], r[3]) for r in rs}
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
-    copy_name = [k for k in fetch if COPY_KERNEL in k and "<256, 8>" in k]
-    if not copy_name:
+    copies = [k for k in fetch if COPY_KERNEL in k[0] and "<256, 8>" in k[0]]
+    if not copies:
         raise SystemExit("the copy kernel is missing from the counter runs")
+    cal = max(copies, key=lambda k: k[1])               # the 2^28 copy: the largest grid
     known_kib = 4.0 * n / 1024
-    f_fetch = known_kib / fetch[copy_name[0]][1]
-    f_write = known_kib / write[copy_name[0]][1]
+    f_fetch = known_kib / fetch[cal][1]
+    f_write = known_kib / write[cal][1]
     lines = ["# HBM traffic from FETCH_SIZE / WRITE_SIZE: %s" % (
-        "every primitive's workload" if suite else "U32 exclusive scan, n = 2^28"), "",
+        "the HBM-sized rows of bench.py --suite" if suite else "U32 exclusive scan, n = 2^28"), "",
         "Commands (each counter in a run of its own):", ""]
     lines += ["    " + c for c in cmds[1:]] + [""]
     lines += ["Calibration on `copy_kernel<256, 8>` over 2^28 u32 (1 GiB read and 1 GiB "
               "written per dispatch): FETCH_SIZE reads %.1f KiB, WRITE_SIZE %.1f KiB, so the "
               "scale factors are %.4f (fetch) and %.4f (write)." %
-              (fetch[copy_name[0]][1], write[copy_name[0]][1], f_fetch, f_write), "",
-              "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | calibrated bytes |",
-              "|---|---|---|---|---|"]
+              (fetch[cal][1], write[cal][1], f_fetch, f_write), "",
+              "| kernel | grid (threads) | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | "
+              "calibrated bytes | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|---|---|"]
     traffic = None
     for k in sorted(fetch):
         if k not in write:
             continue
         fk, wk = fetch[k][1], write[k][1]
         b = (fk * f_fetch + wk * f_write) * 1024
-        lines.append("| `%s` | %d | %.1f | %.1f | %.4g |" % (_short(k), fetch[k][0], fk, wk, b))
-        if SCAN_KERNEL in k and SCAN_SHAPE in k:
+        ab = algorithmic_bytes(k[0], k[1]) if suite else (8 * n if SCAN_KERNEL in k[0] else None)
+        lines.append("| `%s` | %d | %d | %.1f | %.1f | %.4g | %s | %s |" % (
+            _short(k[0]), k[1], fetch[k][0], fk, wk, b, "%.4g" % ab if ab else "-",
+            "%.4f" % (b / ab) if ab else "-"))
+        if SCAN_KERNEL in k[0] and SCAN_SHAPE in k[0]:
             traffic = b
     if traffic is not None:
         lines += ["", "Exclusive look-back scan of 2^28 u32: %.4g bytes per launch against %.4g "
@@ -340,10 +385,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--suite", action="store_true", help="also time every primitive workload")
+    ap.add_argument("--hbm-rows", action="store_true",
+                    help="with --suite: only the HBM-sized rows (one size per kernel)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libscan has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -82,10 +82,14 @@ const char *libscan_strerror(int status);
 /* Library version string, e.g. "libscan 0.1 gfx950". */
 const char *libscan_version(void);
 
-/* Zero-fill `scratch_bytes` bytes of device scratch on `stream` with a fill
- * kernel (no hipMemset node, so it can be captured in a graph), and record the
- * buffer as clean, so the next call on it clears nothing.  Needed only after
- * something other than libscan has written to the buffer. */
+/* Reset a scratch buffer: zero its fixed 256-byte header (the tile tickets)
+ * on `stream` with a fill kernel (no hipMemset node, so it can be captured in
+ * a graph) and record that none of its body may be trusted, so the next call
+ * on it clears exactly the state it uses -- never the whole buffer.  Needed
+ * only after something other than libscan has written to the buffer (or a
+ * new allocation landed at the address of a freed one).  NULL with
+ * scratch_bytes 0 is a no-op; LIBSCAN_ERR_SCRATCH when the buffer cannot hold
+ * the header once its start is rounded up to 256 bytes. */
 int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */

@@ -237,13 +237,16 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
 {
     if (!scratch)
         return scratch_bytes ? LIBSCAN_ERR_NULL : LIBSCAN_OK;
-    hipError_t e = launch_fill_zero(scratch, scratch_bytes, stream);
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, 0, &s))
+        return LIBSCAN_ERR_SCRATCH;
+    // The header only: the record says no body byte is trusted, so each call
+    // clears the state it needs on first use.
+    hipError_t e = launch_fill_zero(s.base, kHeaderBytes, stream);
     if (e != hipSuccess)
         return hip_status(e);
-    Scratch s;
     std::lock_guard<std::mutex> lock(g_state_mu);
-    if (carve(scratch, scratch_bytes, 0, &s))
-        g_state[(uintptr_t)s.base] = StateRecord{kKindZero, 0, s.bytes - kHeaderBytes, 0};
+    g_state[(uintptr_t)s.base] = StateRecord{kKindZero, 0, 0, 0};
     return LIBSCAN_OK;
 }
 
