@@ -21,13 +21,16 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def check(flags, offset=0):
+def check(flags, offset=0, out_offset=None):
     ref, cref = oracle.compact_flags(flags)
     t = to_dev(flags.astype(np.int32), offset)
-    out, count = ps.compact_flags_u32(t)
+    out = None
+    if out_offset is not None:
+        out = to_dev(np.full(flags.size, 12345, dtype=np.int32), out_offset)
+    out, count = ps.compact_flags_u32(t, out=out)
     got = to_host_i32(out)
     msg = first_mismatch(got, ref)
-    assert msg is None, "%s n=%d offset=%d" % (msg, flags.size, offset)
+    assert msg is None, "%s n=%d offset=%d out_offset=%s" % (msg, flags.size, offset, out_offset)
     assert count == cref
 
 
@@ -85,3 +88,13 @@ def test_empty():
 def test_repeated_calls():
     for rep, n in enumerate([100000, 7, 1 << 18, 33333]):
         check(workloads.bernoulli_flags(n, 0.5, 40 + rep))
+
+
+@pytest.mark.parametrize("out_offset", [1, 2, 3])
+@pytest.mark.parametrize("p", [0.5, 0.03, 0.97])
+def test_unaligned_output(out_offset, p):
+    # Kept and -1 runs start at every 16-byte phase of the output, through
+    # tile boundaries (16384-flag tiles) and a ragged tail.
+    flags = workloads.bernoulli_flags(3 * 16384 + 77, p, 17 + out_offset)
+    check(flags, offset=0, out_offset=out_offset)
+    check(flags, offset=(out_offset + 1) % 4, out_offset=out_offset)
