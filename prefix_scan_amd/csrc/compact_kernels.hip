@@ -27,9 +27,13 @@ struct CompactOp {
     static constexpr int BLOCK = BLOCK_;
     static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     static_assert(V <= 16, "keep bits are packed into one 64-bit word");
+    static_assert(T <= 65536, "kept slots are staged as 16-bit tile offsets");
     using TS = TileScan<BLOCK, V>;
+    // A tile is held as its keep bits and the wave prefix of its chunk sums;
+    // the flags themselves live only from their load to the tile's reduce,
+    // and the chunk scans are rebuilt from the bits when the tile finishes.
     struct Regs {
-        u32x4 x[V];         // keep bits, then their scan inside the chunk
+        u32x4 x[V];         // the loaded flags (until local())
         uint32_t w[V];
         uint64_t kbits;     // 4 keep bits per chunk
     };
@@ -57,19 +61,36 @@ struct CompactOp {
             load_tile<BLOCK, V>(fbase, (uint64_t)t * T, vlo, vhi, r.x);   // outside: flag 0
     }
 
+    // Chunk k's keep bits, scanned inside the chunk.
+    __device__ static __forceinline__ u32x4 kept_scanned(uint64_t kbits, int k)
+    {
+        const uint32_t b = (uint32_t)(kbits >> (4 * k)) & 15u;
+        u32x4 z;
+        z.x = b & 1u;
+        z.y = z.x + ((b >> 1) & 1u);
+        z.z = z.y + ((b >> 2) & 1u);
+        z.w = z.z + ((b >> 3) & 1u);
+        return z;
+    }
+
     __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const
     {
         r.kbits = 0;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            r.x[k].x = r.x[k].x != 0u;
-            r.x[k].y = r.x[k].y != 0u;
-            r.x[k].z = r.x[k].z != 0u;
-            r.x[k].w = r.x[k].w != 0u;
-            r.kbits |= (uint64_t)(r.x[k].x | (r.x[k].y << 1) | (r.x[k].z << 2) | (r.x[k].w << 3))
-                       << (4 * k);
+            const uint32_t b = (r.x[k].x != 0u) | ((r.x[k].y != 0u) << 1) |
+                               ((r.x[k].z != 0u) << 2) | ((r.x[k].w != 0u) << 3);
+            r.kbits |= (uint64_t)b << (4 * k);
         }
-        TS::local(r.x, r.w, c.c);
+        const uint32_t wave = threadIdx.x / kWave;
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            r.w[k] = wave_incl_add(kept_scanned(r.kbits, k).w);
+        if (lane_id() == kWave - 1) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                c.c[k * TS::NW + wave] = r.w[k];
+        }
     }
 
     __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
@@ -82,23 +103,26 @@ struct CompactOp {
 
     __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const { *count_out = carry + in.value; }
 
-    // Kept indices staged in LDS at their rank inside the tile, then both
-    // ranges stored contiguously.
+    // Kept elements staged in LDS (as 16-bit tile offsets) at their rank
+    // inside the tile, then both ranges stored contiguously.
     __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t kept_before) const
     {
-        __shared__ int32_t s_idx[T];
+        __shared__ uint16_t s_off[T];
         const uint64_t vstart = (uint64_t)t * T;
         const uint32_t kept = c.kept;
-        TS::template apply<false>(r.x, r.w, c.c, 0u);
-        const int64_t first_index = (int64_t)vstart - (int64_t)vlo;   // index of tile slot 0
+        u32x4 z[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            z[k] = kept_scanned(r.kbits, k);
+        TS::template apply<false>(z, r.w, c.c, 0u);
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const uint32_t bits = (uint32_t)(r.kbits >> (4 * k)) & 15u;
-            const int64_t i0 = first_index + (int64_t)(k * BLOCK + threadIdx.x) * 4;
-            if (bits & 1u) s_idx[r.x[k].x] = (int32_t)(i0 + 0);
-            if (bits & 2u) s_idx[r.x[k].y] = (int32_t)(i0 + 1);
-            if (bits & 4u) s_idx[r.x[k].z] = (int32_t)(i0 + 2);
-            if (bits & 8u) s_idx[r.x[k].w] = (int32_t)(i0 + 3);
+            const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+            if (bits & 1u) s_off[z[k].x] = (uint16_t)(e0 + 0);
+            if (bits & 2u) s_off[z[k].y] = (uint16_t)(e0 + 1);
+            if (bits & 4u) s_off[z[k].z] = (uint16_t)(e0 + 2);
+            if (bits & 8u) s_off[z[k].w] = (uint16_t)(e0 + 3);
         }
         __syncthreads();
         const uint64_t lo = vstart > vlo ? vstart : vlo;
@@ -106,8 +130,9 @@ struct CompactOp {
         const uint32_t valid = (uint32_t)(hi - lo);
         const uint32_t dropped = valid - kept;
         const uint32_t dropped_before = (uint32_t)(lo - vlo) - kept_before;
+        const int32_t first_index = (int32_t)((int64_t)vstart - (int64_t)vlo);   // index of slot 0
         for (uint32_t j = threadIdx.x; j < kept; j += BLOCK)
-            out[kept_before + j] = s_idx[j];
+            out[kept_before + j] = first_index + (int32_t)s_off[j];
         int32_t *fill = out + (n - dropped_before - dropped);
         for (uint32_t j = threadIdx.x; j < dropped; j += BLOCK)
             fill[j] = -1;
@@ -176,6 +201,8 @@ hipError_t launch_compact(const int32_t *flags, int32_t *out, uint64_t n, const 
         return launch_compact_v<256, 8>(flags, out, n, s, count_out, stream);
     if (sh.block == 256 && sh.chunks == 16)
         return launch_compact_v<256, 16>(flags, out, n, s, count_out, stream);
+    if (sh.block == 512 && sh.chunks == 16)
+        return launch_compact_v<512, 16>(flags, out, n, s, count_out, stream);
     return launch_compact_v<512, 8>(flags, out, n, s, count_out, stream);
 }
 
