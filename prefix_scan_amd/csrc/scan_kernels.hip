@@ -91,9 +91,11 @@ struct ScanOp {
     static constexpr int BLOCK = BLOCK_;
     static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     using TS = TileScan<BLOCK, V>;
+    // The wave prefix of the chunk sums is not held across the step: finish
+    // rebuilds it from the chunk totals (one DPP scan per chunk run), which
+    // frees V registers per tile.
     struct Regs {
         u32x4 x[V];
-        uint32_t w[V];
     };
     struct Cells {
         uint32_t c[TS::NCELL];
@@ -116,7 +118,11 @@ struct ScanOp {
             load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
     }
 
-    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const { TS::local(r.x, r.w, c.c); }
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const
+    {
+        uint32_t w[V];
+        TS::local(r.x, w, c.c);
+    }
 
     __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
     {
@@ -127,7 +133,11 @@ struct ScanOp {
 
     __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
     {
-        TS::template apply<INCL>(r.x, r.w, c.c, carry);
+        uint32_t w[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            w[k] = wave_incl_add(r.x[k].w);
+        TS::template apply<INCL>(r.x, w, c.c, carry);
         if (whole(t))
             store_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
         else
