@@ -29,6 +29,10 @@ def load():
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.oracle_scan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_int]
     lib.oracle_scan_u32.restype = ctypes.c_uint32
+    lib.oracle_scan_op_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_scan_op_u32.restype = ctypes.c_uint32
+    lib.oracle_reduce_op_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_int]
+    lib.oracle_reduce_op_u32.restype = ctypes.c_uint32
     lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
     lib.oracle_scan_blocked_u32.restype = ctypes.c_int
     lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
@@ -61,6 +65,27 @@ def scan_u32(a, inclusive=False):
     total = load().oracle_scan_u32(_ptr(a, ctypes.c_uint32), _ptr(out, ctypes.c_uint32),
                                    a.size, 1 if inclusive else 0)
     return out, int(total)
+
+
+# Operator codes of oracle_scan_op_u32 / oracle_reduce_op_u32 ([cairn]
+# "reduce and compact": add_wrap, mul_wrap, &, |, ^, min, max).
+OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6}
+
+
+def scan_op_u32(a, op, inclusive=False):
+    """O1c: (out, total) -- scan of a under the operator named `op` (a key of
+    OPS); the exclusive form starts from the operator's identity."""
+    a = _u32(a)
+    out = np.empty_like(a)
+    total = load().oracle_scan_op_u32(_ptr(a, ctypes.c_uint32), _ptr(out, ctypes.c_uint32),
+                                      a.size, OPS[op], 1 if inclusive else 0)
+    return out, int(total)
+
+
+def reduce_op_u32(a, op):
+    """O1c: the fold of a under the operator named `op`."""
+    a = _u32(a)
+    return int(load().oracle_reduce_op_u32(_ptr(a, ctypes.c_uint32), a.size, OPS[op]))
 
 
 def scan_exclusive_u32(a):

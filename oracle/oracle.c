@@ -66,6 +66,75 @@ uint32_t oracle_scan_u32(const uint32_t *a, uint32_t *out, uint64_t n, int inclu
 }
 
 /* ------------------------------------------------------------------------- */
+/* O1c -- scan and reduce under the other integer operators.                 */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [cairn] "reduce and compact": the integer operators of a reduction are
+ * add_wrap, mul_wrap, &, |, ^, min and max; [cairn] "scan": a scan takes the
+ * same operators, the inclusive form gives e(0) op .. op e(i), the exclusive
+ * form what came before i.  Readings: values are unsigned 32-bit (min and
+ * max compare them as unsigned); the exclusive output at 0, and the result
+ * of an empty range, is the operator's identity (0 for add_wrap, | , ^ and
+ * max; 1 for mul_wrap; 0xFFFFFFFF for & and min).
+ * Operator codes: 0 add_wrap, 1 mul_wrap, 2 &, 3 |, 4 ^, 5 min, 6 max.
+ */
+static uint32_t op_identity(int op)
+{
+    switch (op) {
+    case 1: return 1u;
+    case 2: return 0xFFFFFFFFu;
+    case 5: return 0xFFFFFFFFu;
+    default: return 0u;
+    }
+}
+
+static uint32_t op_apply(int op, uint32_t a, uint32_t b)
+{
+    switch (op) {
+    case 0: return a + b;
+    case 1: return a * b;
+    case 2: return a & b;
+    case 3: return a | b;
+    case 4: return a ^ b;
+    case 5: return a < b ? a : b;
+    case 6: return a > b ? a : b;
+    default: return 0u;
+    }
+}
+
+/* Returns the fold of all n values (the identity for n == 0); out may equal
+ * a.  An operator code outside 0..6 returns 0 and writes nothing. */
+uint32_t oracle_scan_op_u32(const uint32_t *a, uint32_t *out, uint64_t n, int op, int inclusive)
+{
+    if (op < 0 || op > 6)
+        return 0u;
+    uint32_t running = op_identity(op);
+    for (uint64_t j = 0; j < n; ++j) {
+        uint32_t x = a[j];
+        if (inclusive) {
+            running = op_apply(op, running, x);
+            out[j] = running;
+        } else {
+            out[j] = running;
+            running = op_apply(op, running, x);
+        }
+    }
+    return running;
+}
+
+/* [cairn] "reduce and compact": the fold of n values in index order. */
+uint32_t oracle_reduce_op_u32(const uint32_t *a, uint64_t n, int op)
+{
+    if (op < 0 || op > 6)
+        return 0u;
+    uint32_t acc = op_identity(op);
+    for (uint64_t j = 0; j < n; ++j)
+        acc = op_apply(op, acc, a[j]);
+    return acc;
+}
+
+/* ------------------------------------------------------------------------- */
 /* O1b -- the blocked three-pass scan of [bend], used only to check that      */
 /* every fork depth gives the same bits as O1.                                */
 /* ------------------------------------------------------------------------- */

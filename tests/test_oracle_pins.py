@@ -333,3 +333,102 @@ def test_radix_perm_is_bijection_and_sorts():
 def test_radix_rejects_bad_args():
     with pytest.raises(ValueError):
         oracle.radix_perm_u32(np.ones(4, dtype=np.uint32), 2)
+
+
+# ---------------------------------------------------------------------------
+# O1c -- scan and reduce under the other integer operators.
+# ---------------------------------------------------------------------------
+OP_IDENTITY = {"add": 0, "mul": 1, "and": 0xFFFFFFFF, "or": 0, "xor": 0, "min": 0xFFFFFFFF,
+               "max": 0}
+NP_ACCUMULATE = {"add": np.add, "mul": np.multiply, "and": np.bitwise_and, "or": np.bitwise_or,
+                 "xor": np.bitwise_xor, "min": np.minimum, "max": np.maximum}
+
+
+def test_op_scan_cairn_max_example():
+    # CAIRN "Concurrency", section "scan": the in-place max scan of the
+    # yields 2, 4, 6, 8 leaves 2 at index 0 and 8 at index 3.
+    g = golden("cairn_scan_max.json")
+    out, total = oracle.scan_op_u32(np.array(g["yields"], dtype=np.uint32), "max", inclusive=True)
+    for k, v in g["inclusive_at"].items():
+        assert int(out[int(k)]) == v
+    assert total == 8
+
+
+def test_op_reduce_cairn_weights():
+    # CAIRN "Concurrency", "reduce and compact": over i % 7 for n = 10000,
+    # reduce + is 29994 and reduce max is 6.
+    g = golden("cairn_reduce_weights.json")
+    w = (np.arange(g["n"]) % g["modulus"]).astype(np.uint32)
+    assert oracle.reduce_op_u32(w, "add") == g["sum"]
+    assert oracle.reduce_op_u32(w, "max") == g["max"]
+
+
+@pytest.mark.parametrize("op", sorted(OP_IDENTITY))
+@pytest.mark.parametrize("n", [1, 2, 7, 1000, 65537])
+def test_op_scan_matches_numpy_accumulate(op, n):
+    # numpy's ufunc accumulate in uint32 (wrapping for add and multiply).
+    rng = np.random.default_rng(1000 + n)
+    if op == "mul":
+        a = (rng.integers(0, 2**32, n, dtype=np.uint32) | 1).astype(np.uint32)   # odd: no collapse to 0
+    else:
+        a = rng.integers(0, 2**32, n, dtype=np.uint32)
+    ref = NP_ACCUMULATE[op].accumulate(a, dtype=np.uint32)
+    inc, total = oracle.scan_op_u32(a, op, inclusive=True)
+    assert np.array_equal(inc, ref)
+    exc, total_e = oracle.scan_op_u32(a, op, inclusive=False)
+    assert int(exc[0]) == OP_IDENTITY[op]
+    assert np.array_equal(exc[1:], ref[:-1])
+    assert total == total_e == int(ref[-1]) == oracle.reduce_op_u32(a, op)
+
+
+@pytest.mark.parametrize("op", sorted(OP_IDENTITY))
+def test_op_scan_brute_force_small(op):
+    # Python integers, reduced mod 2^32 after every step, over small arrays.
+    apply = {"add": lambda x, y: (x + y) % 2**32, "mul": lambda x, y: (x * y) % 2**32,
+             "and": lambda x, y: x & y, "or": lambda x, y: x | y, "xor": lambda x, y: x ^ y,
+             "min": min, "max": max}[op]
+    rng = np.random.default_rng(77)
+    for n in range(0, 12):
+        a = rng.choice(np.array([0, 1, 2, 3, 0x80000000, 0xFFFFFFFF, 0xDEADBEEF], dtype=np.uint32), n)
+        run, inc = OP_IDENTITY[op], []
+        for x in a.tolist():
+            run = apply(run, x)
+            inc.append(run)
+        got, total = oracle.scan_op_u32(a, op, inclusive=True)
+        assert got.tolist() == inc
+        assert total == (inc[-1] if n else OP_IDENTITY[op])
+
+
+def test_op_scan_closed_forms():
+    n = 1 << 12
+    i = np.arange(n, dtype=np.uint64)
+    # xor of 0..j: j, 1, j + 1, 0 for j mod 4 = 0, 1, 2, 3.
+    xr, _ = oracle.scan_op_u32(i.astype(np.uint32), "xor", inclusive=True)
+    want = np.select([i % 4 == 0, i % 4 == 1, i % 4 == 2], [i, np.ones_like(i), i + 1], 0)
+    assert np.array_equal(xr, want.astype(np.uint32))
+    # or of 2^(j mod 32) up to j: 2^(min(j, 31) + 1) - 1.
+    orr, _ = oracle.scan_op_u32((1 << (i % 32)).astype(np.uint32), "or", inclusive=True)
+    want = (2 ** (np.minimum(i, 31) + 1) - 1).astype(np.uint32)
+    assert np.array_equal(orr, want)
+    # product of j + 1 threes: 3^(j+1) mod 2^32.
+    pr, _ = oracle.scan_op_u32(np.full(64, 3, dtype=np.uint32), "mul", inclusive=True)
+    assert pr.tolist() == [pow(3, j + 1, 2**32) for j in range(64)]
+    # max of an increasing run and min of a decreasing run are the run itself.
+    inc = np.arange(5, 500, 3, dtype=np.uint32)
+    assert np.array_equal(oracle.scan_op_u32(inc, "max", inclusive=True)[0], inc)
+    assert np.array_equal(oracle.scan_op_u32(inc[::-1].copy(), "min", inclusive=True)[0], inc[::-1])
+    # and: all ones until the first zero bit pattern, then zero.
+    a = np.full(10, 0xFFFFFFFF, dtype=np.uint32)
+    a[6] = 0
+    ar, tot = oracle.scan_op_u32(a, "and", inclusive=True)
+    assert ar.tolist() == [0xFFFFFFFF] * 6 + [0] * 4 and tot == 0
+
+
+def test_op_scan_add_is_the_plain_scan_and_empty_is_identity():
+    a = np.random.default_rng(5).integers(0, 2**32, 10000, dtype=np.uint32)
+    for inclusive in (False, True):
+        assert np.array_equal(oracle.scan_op_u32(a, "add", inclusive)[0],
+                              oracle.scan_u32(a, inclusive)[0])
+    for op, ident in OP_IDENTITY.items():
+        assert oracle.scan_op_u32(np.zeros(0, dtype=np.uint32), op)[1] == ident
+        assert oracle.reduce_op_u32(np.zeros(0, dtype=np.uint32), op) == ident
