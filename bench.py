@@ -192,6 +192,14 @@ def suite(args, torch, ps):
             lambda: ps.scan_u32_ex(d, algo="threepass", want_total=False))
         dst = torch.empty_like(d)
         row("copy n=" + label, n, 8, lambda: ps.copy_u32(d, dst))
+        if n == workloads.N_SCAN_LARGE:
+            # The other integer operators (scan 8 B/element, reduction 4).
+            for op in ("mul", "and", "or", "xor", "min", "max"):
+                row("scan exclusive %s n=%s" % (op, label), n, 8,
+                    lambda: ps.scan_op_u32(d, op, want_total=False))
+            for op in ("add", "max"):
+                row("reduce %s n=%s" % (op, label), n, 4,
+                    lambda: ps.reduce_op_u32(d, op, want_total=False, total_dev=dst[:1]))
         del d, dst
     for p in (0.5, 0.01, 0.99):
         f = torch.from_numpy(workloads.compact_flags(p)).to("cuda")
@@ -244,7 +252,7 @@ def algorithmic_bytes(name, grid):
         ("reduce_blocks_kernel", 4 * n28), ("compact_kernel", 8 * n26),
         ("segscan_independent_kernel", 8 * n26 + 4 * (n26 // 16)),
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
-        ("digit_hist_kernel", 4 * n25),
+        ("digit_hist_kernel", 4 * n25), ("reduce_partial_kernel", 4 * n28),
     ]
     for key, b in table:
         if "::" + key + "<" in name:

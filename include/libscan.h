@@ -147,6 +147,55 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Scan and reduction under the other integer operators                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * CAIRN "Concurrency", section "reduce and compact": a reduction combines
+ * one value per index into a total, and its integer operators are add_wrap,
+ * mul_wrap, &, |, ^, min and max; section "scan": a scan takes the same
+ * operators, inclusive (out[i] = e(0) op .. op e(i)) or exclusive (what came
+ * before i).  Values are unsigned 32-bit; min and max compare them as
+ * unsigned; the exclusive output at index 0, and the result for n == 0, is
+ * the operator's identity (0 for ADD, OR, XOR and MAX; 1 for MUL; 0xFFFFFFFF
+ * for AND and MIN).  Every operator is associative and commutative, so the
+ * bits do not depend on how the library groups the work.
+ */
+enum {
+    LIBSCAN_OP_ADD = 0,     /* add_wrap (mod 2^32) */
+    LIBSCAN_OP_MUL = 1,     /* mul_wrap (mod 2^32) */
+    LIBSCAN_OP_AND = 2,
+    LIBSCAN_OP_OR = 3,
+    LIBSCAN_OP_XOR = 4,
+    LIBSCAN_OP_MIN = 5,
+    LIBSCAN_OP_MAX = 6
+};
+
+/*
+ * In-place scan of n u32 values under `op`; the fold of all n values goes to
+ * *total_host and/or *total_dev as for scan_exclusive_u32.  Scratch: at least
+ * scan_scratch_bytes(n).  Same layout, ownership and stream rules as
+ * scan_exclusive_u32.  Errors: LIBSCAN_ERR_ARG for an op outside
+ * LIBSCAN_OP_ADD..LIBSCAN_OP_MAX or inclusive not 0/1, plus those of
+ * scan_exclusive_u32.  (op = LIBSCAN_OP_ADD is scan_exclusive_u32 /
+ * scan_inclusive_u32.)
+ */
+int scan_op_u32(uint32_t *data, uint64_t n, int op, int inclusive, uint32_t *total_host,
+                uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * The fold of n u32 values under `op` (CAIRN "reduce and compact"); `data`
+ * is only read.  The result goes to *total_host (the call then waits)
+ * and/or *total_dev (4-byte aligned device u32).  Scratch: at least
+ * reduce_scratch_bytes(n) (a small constant).  Errors: LIBSCAN_ERR_ARG for
+ * an op outside the range; LIBSCAN_ERR_NULL, _SIZE, _ALIGN, _SCRATCH, _HIP
+ * as for the scans.
+ */
+size_t reduce_scratch_bytes(uint64_t n);
+int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host,
+                  uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Segmented scan and segment sums over regular segments                    */
 /* ------------------------------------------------------------------------ */
 

@@ -74,6 +74,12 @@ def lib():
             f.restype = i32
         L.scan_u32_ex.argtypes = [vp, u64, i32, i32, i32, u32p, vp, vp, sz, vp]
         L.scan_u32_ex.restype = i32
+        L.scan_op_u32.argtypes = [vp, u64, i32, i32, u32p, vp, vp, sz, vp]
+        L.scan_op_u32.restype = i32
+        L.reduce_scratch_bytes.argtypes = [u64]
+        L.reduce_scratch_bytes.restype = sz
+        L.reduce_op_u32.argtypes = [vp, u64, i32, u32p, vp, vp, sz, vp]
+        L.reduce_op_u32.restype = i32
         L.segscan_scratch_bytes.argtypes = [u64, u64]
         L.segscan_scratch_bytes.restype = sz
         L.segscan_u32.argtypes = [vp, vp, u64, u64, vp, vp, sz, vp]
@@ -192,6 +198,43 @@ def _scan(name, data, want_total, total_dev, stream):
     host, hp = _total_args(want_total, total_dev)
     _check(getattr(lib(), name)(_ptr(data), data.numel(), hp, _ptr(total_dev), _ptr(scr),
                                 scr.numel(), sh), name)
+    return int(host.value) if want_total else None
+
+
+# LIBSCAN_OP_* of libscan.h.
+OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6}
+
+
+def _op(op):
+    if op not in OPS:
+        raise ValueError("op must be one of %s, got %r" % (sorted(OPS), op))
+    return OPS[op]
+
+
+def scan_op_u32(data, op, inclusive=False, want_total=True, total_dev=None, stream=None):
+    """In-place scan of `data` under the operator named `op` ("add", "mul",
+    "and", "or", "xor", "min", "max"); returns the fold of all values (an
+    int, after waiting for the stream) when want_total, else None."""
+    _dev_u32(data, "data")
+    o = _op(op)
+    sh, s = _stream_handle(data.device, stream)
+    scr = _scratch_for(data.device, s, lib().scan_scratch_bytes(data.numel()))
+    host, hp = _total_args(want_total, total_dev)
+    _check(lib().scan_op_u32(_ptr(data), data.numel(), o, 1 if inclusive else 0, hp,
+                             _ptr(total_dev), _ptr(scr), scr.numel(), sh), "scan_op_u32")
+    return int(host.value) if want_total else None
+
+
+def reduce_op_u32(data, op, want_total=True, total_dev=None, stream=None):
+    """The fold of `data` under the operator named `op` (data is only read);
+    returns it as an int when want_total, else leaves it in total_dev."""
+    _dev_u32(data, "data")
+    o = _op(op)
+    sh, s = _stream_handle(data.device, stream)
+    scr = _scratch_for(data.device, s, lib().reduce_scratch_bytes(data.numel()))
+    host, hp = _total_args(want_total, total_dev)
+    _check(lib().reduce_op_u32(_ptr(data), data.numel(), o, hp, _ptr(total_dev), _ptr(scr),
+                               scr.numel(), sh), "reduce_op_u32")
     return int(host.value) if want_total else None
 
 

@@ -25,6 +25,7 @@ namespace libscan {
 template <int BLOCK_, int V>
 struct CompactOp {
     static constexpr int BLOCK = BLOCK_;
+    using Monoid = OpAdd;
     static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     static_assert(V <= 16, "keep bits are packed into one 64-bit word");
     static_assert(T <= 65536, "kept slots are staged as 16-bit tile offsets");

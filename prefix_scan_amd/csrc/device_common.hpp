@@ -87,6 +87,81 @@ __device__ __forceinline__ uint32_t wave_shr1(uint32_t x)
     return dpp<kDppWaveShr1, 0xF>(x);
 }
 
+// ---------------------------------------------------------------------------
+// The integer operators of a scan or reduction (CAIRN "Concurrency",
+// "reduce and compact"): add_wrap, mul_wrap, &, |, ^, min and max on
+// unsigned 32-bit values, each with its identity.  All are associative and
+// commutative, so any grouping gives the same bits.
+// ---------------------------------------------------------------------------
+struct OpAdd {
+    static constexpr uint32_t identity = 0u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a + b; }
+};
+struct OpMul {
+    static constexpr uint32_t identity = 1u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a * b; }
+};
+struct OpAnd {
+    static constexpr uint32_t identity = 0xFFFFFFFFu;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a & b; }
+};
+struct OpOr {
+    static constexpr uint32_t identity = 0u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a | b; }
+};
+struct OpXor {
+    static constexpr uint32_t identity = 0u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a ^ b; }
+};
+struct OpMin {
+    static constexpr uint32_t identity = 0xFFFFFFFFu;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a < b ? a : b; }
+};
+struct OpMax {
+    static constexpr uint32_t identity = 0u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a > b ? a : b; }
+};
+
+// DPP move whose disabled lanes (source outside the row, masked rows) read
+// `old` -- the operator's identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or(uint32_t x, uint32_t old)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive wave scan under Op (the same steps as wave_incl_add).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl(uint32_t x)
+{
+    if constexpr (__is_same(Op, OpAdd)) {
+        return wave_incl_add(x);
+    } else {
+        constexpr uint32_t e = Op::identity;
+        x = Op::apply(x, dpp_or<kDppRowShr1, 0xF>(x, e));
+        x = Op::apply(x, dpp_or<kDppRowShr2, 0xF>(x, e));
+        x = Op::apply(x, dpp_or<kDppRowShr4, 0xF>(x, e));
+        x = Op::apply(x, dpp_or<kDppRowShr8, 0xF>(x, e));
+        x = Op::apply(x, dpp_or<kDppRowBcast15, 0xA>(x, e));
+        x = Op::apply(x, dpp_or<kDppRowBcast31, 0xC>(x, e));
+        return x;
+    }
+}
+
+// The fold of the whole wave under Op, in every lane.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_fold(uint32_t x)
+{
+    return wave_bcast_last(wave_incl<Op>(x));
+}
+
+// The previous lane's value (Op's identity in lane 0).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_shr1_op(uint32_t x)
+{
+    return dpp_or<kDppWaveShr1, 0xF>(x, Op::identity);
+}
+
 // Segmented inclusive wave scan of (head flag, value) pairs under
 // (fa, va) . (fb, vb) = (fa | fb, fb ? vb : va + vb): a piece that holds a
 // segment head does not take the sum from the pieces before it.
@@ -244,11 +319,12 @@ __device__ __forceinline__ void store_tile(uint32_t *abase, uint64_t vstart, uin
 // carry from the tiles before.  Each thread reads only V cells, so the LDS
 // values never crowd the registers that hold the tile.
 // ---------------------------------------------------------------------------
-template <int BLOCK, int V>
+template <int BLOCK, int V, class Op = OpAdd>
 struct TileScan {
     static constexpr int NW = BLOCK / kWave;
     static constexpr int NCELL = NW * V;
     static constexpr int CELLS_PER_LANE = (NCELL + kWave - 1) / kWave;
+    static constexpr bool kAdd = __is_same(Op, OpAdd);
 
     // Phase 1.  x[k] becomes the inclusive scan inside its chunk; w[k] the
     // inclusive wave scan of the chunk sums.
@@ -258,10 +334,10 @@ struct TileScan {
         const uint32_t wave = threadIdx.x / kWave;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            x[k].y += x[k].x;
-            x[k].z += x[k].y;
-            x[k].w += x[k].z;
-            w[k] = wave_incl_add(x[k].w);
+            x[k].y = Op::apply(x[k].y, x[k].x);
+            x[k].z = Op::apply(x[k].z, x[k].y);
+            x[k].w = Op::apply(x[k].w, x[k].z);
+            w[k] = wave_incl<Op>(x[k].w);
         }
         if (lane_id() == kWave - 1) {
 #pragma unroll
@@ -271,32 +347,36 @@ struct TileScan {
     }
 
     // Phase 2, called by one whole wave after a barrier: the cells become
-    // their exclusive scan; returns the tile's sum in every lane.
+    // their exclusive scan; returns the tile's fold in every lane.
     __device__ static __forceinline__ uint32_t cells(uint32_t *s_cell)
     {
         const uint32_t lane = lane_id();
         uint32_t v[CELLS_PER_LANE];
-        uint32_t mine = 0;
+        uint32_t mine = Op::identity;
 #pragma unroll
         for (int j = 0; j < CELLS_PER_LANE; ++j) {
             const uint32_t c = lane * CELLS_PER_LANE + j;
-            v[j] = c < (uint32_t)NCELL ? s_cell[c] : 0u;
-            mine += v[j];
+            v[j] = c < (uint32_t)NCELL ? s_cell[c] : Op::identity;
+            mine = Op::apply(mine, v[j]);
         }
-        const uint32_t incl = wave_incl_add(mine);
-        uint32_t run = incl - mine;
+        const uint32_t incl = wave_incl<Op>(mine);
+        uint32_t run;
+        if constexpr (kAdd)
+            run = incl - mine;
+        else
+            run = wave_shr1_op<Op>(incl);
 #pragma unroll
         for (int j = 0; j < CELLS_PER_LANE; ++j) {
             const uint32_t c = lane * CELLS_PER_LANE + j;
             if (c < (uint32_t)NCELL)
                 s_cell[c] = run;
-            run += v[j];
+            run = Op::apply(run, v[j]);
         }
         return wave_bcast_last(incl);
     }
 
     // Phase 3, after the barrier that follows phase 2: the tile's outputs
-    // (exclusive or inclusive) plus `carry`.
+    // (exclusive or inclusive) combined with `carry`.
     template <bool INCL>
     __device__ static __forceinline__ void apply(u32x4 (&x)[V], const uint32_t (&w)[V],
                                                  const uint32_t *s_cell, uint32_t carry)
@@ -304,16 +384,22 @@ struct TileScan {
         const uint32_t wave = threadIdx.x / kWave;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            const uint32_t base = carry + s_cell[k * NW + wave] + (w[k] - x[k].w);
+            // Everything before this lane's chunk: the carry, the cells
+            // before this (chunk, wave) run, the lanes before this one.
+            uint32_t base;
+            if constexpr (kAdd)
+                base = carry + s_cell[k * NW + wave] + (w[k] - x[k].w);
+            else
+                base = Op::apply(Op::apply(carry, s_cell[k * NW + wave]), wave_shr1_op<Op>(w[k]));
             if (INCL) {
-                x[k].x += base;
-                x[k].y += base;
-                x[k].z += base;
-                x[k].w += base;
+                x[k].x = Op::apply(base, x[k].x);
+                x[k].y = Op::apply(base, x[k].y);
+                x[k].z = Op::apply(base, x[k].z);
+                x[k].w = Op::apply(base, x[k].w);
             } else {
-                x[k].w = base + x[k].z;
-                x[k].z = base + x[k].y;
-                x[k].y = base + x[k].x;
+                x[k].w = Op::apply(base, x[k].z);
+                x[k].z = Op::apply(base, x[k].y);
+                x[k].y = Op::apply(base, x[k].x);
                 x[k].x = base;
             }
         }
@@ -384,37 +470,40 @@ __device__ __forceinline__ LookbackWindow lookback_load(const uint64_t *desc, in
     return w;
 }
 
-// Folds one window into `excl`.  Returns 2 when a PREFIX was reached (excl
-// is the carry), 1 when all 64 tiles held aggregates (excl grew; look
-// further back), 0 when a tile before the nearest PREFIX is not ready yet
-// (nothing folded; read the same window again).
+// Folds one window into `excl` under Op.  Returns 2 when a PREFIX was
+// reached (excl is the carry), 1 when all 64 tiles held aggregates (excl
+// grew; look further back), 0 when a tile before the nearest PREFIX is not
+// ready yet (nothing folded; read the same window again).  Lanes before tile
+// 0 count as PREFIX with Op's identity.
+template <class Op = OpAdd>
 __device__ __forceinline__ int lookback_fold(const LookbackWindow &w, uint32_t tag,
                                              uint32_t &excl)
 {
     const uint32_t hi = (uint32_t)(w.d >> 32);
     const uint32_t st = w.before_start ? kStatusPrefix : (((hi & ~3u) == tag) ? (hi & 3u) : 0u);
-    const uint32_t val = w.before_start ? 0u : (uint32_t)w.d;
+    const uint32_t val = w.before_start ? Op::identity : (uint32_t)w.d;
     const uint64_t pref = ballot(st == kStatusPrefix);
     const uint64_t wait = ballot(st == 0);
     const uint32_t p = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
     const uint64_t upto = (p >= 63) ? ~0ull : ((2ull << p) - 1);
     if (wait & upto)
         return 0;
-    excl += wave_sum(lane_id() <= p ? val : 0u);
+    excl = Op::apply(excl, wave_fold<Op>(lane_id() <= p ? val : Op::identity));
     return pref ? 2 : 1;
 }
 
-// Called by one whole wave.  Returns, in every lane, the sum of the values
+// Called by one whole wave.  Returns, in every lane, the fold of the values
 // of tiles tile-1, tile-2, ... back to and including the nearest PREFIX: the
 // tile's exclusive carry.  Each step inspects 64 predecessors at once; `w` is
 // the window for base = tile - 1, which a caller may have loaded early.  The
 // first window is folded outside the retry loop, so waiting for it does not
 // wait for loads the caller issued after it.
+template <class Op = OpAdd>
 __device__ __forceinline__ uint32_t lookback_from(const uint64_t *desc, uint32_t tile,
                                                   uint32_t tag, LookbackWindow w)
 {
-    uint32_t excl = 0;
-    int r = lookback_fold(w, tag, excl);
+    uint32_t excl = Op::identity;
+    int r = lookback_fold<Op>(w, tag, excl);
     int64_t base = (int64_t)tile - 1;
     while (r != 2) {
         if (r == 1)
@@ -422,14 +511,15 @@ __device__ __forceinline__ uint32_t lookback_from(const uint64_t *desc, uint32_t
         else
             __builtin_amdgcn_s_sleep(1);
         w = lookback_load(desc, base);
-        r = lookback_fold(w, tag, excl);
+        r = lookback_fold<Op>(w, tag, excl);
     }
     return excl;
 }
 
+template <class Op = OpAdd>
 __device__ __forceinline__ uint32_t lookback(const uint64_t *desc, uint32_t tile, uint32_t tag)
 {
-    return lookback_from(desc, tile, tag, lookback_load(desc, (int64_t)tile - 1));
+    return lookback_from<Op>(desc, tile, tag, lookback_load(desc, (int64_t)tile - 1));
 }
 
 }  // namespace libscan

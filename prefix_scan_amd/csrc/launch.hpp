@@ -72,6 +72,17 @@ unsigned threepass_auto_depth(uint64_t n);
 unsigned floor_log2(uint64_t n);
 
 hipError_t launch_copy(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream);
+
+// Scan under operator `op` (0 add_wrap, 1 mul_wrap, 2 and, 3 or, 4 xor,
+// 5 min, 6 max), pipelined; and one u32 written on the stream.
+hipError_t launch_scan_op(uint32_t *data, uint64_t n, int op, bool inclusive, const Scratch &s,
+                          uint32_t *total_out, hipStream_t stream);
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, hipStream_t stream);
+
+// ---- reduction (reduce_kernels.hip) ----
+hipError_t launch_reduce_op(const uint32_t *data, uint64_t n, int op, const Scratch &s,
+                            uint32_t *total_out, hipStream_t stream);
+size_t reduce_body_bytes();
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 
 // ---- segmented scan (segscan_kernels.hip) ----

@@ -153,11 +153,11 @@ int read_back(uint32_t *host, const uint32_t *dev, hipStream_t stream)
     return hip_status(hipStreamSynchronize(stream));
 }
 
-// A zero result to report for an empty input.
-int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
+// A fixed result (the operator's identity) to report for an empty input.
+int report_value(uint32_t *host, uint32_t *dev, uint32_t value, hipStream_t stream)
 {
     if (dev) {
-        hipError_t e = launch_fill_zero(dev, sizeof(uint32_t), stream);
+        hipError_t e = launch_fill_u32(dev, value, stream);
         if (e != hipSuccess)
             return hip_status(e);
     }
@@ -165,9 +165,21 @@ int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
         hipError_t e = hipStreamSynchronize(stream);
         if (e != hipSuccess)
             return hip_status(e);
-        *host = 0;
+        *host = value;
     }
     return LIBSCAN_OK;
+}
+
+int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
+{
+    return report_value(host, dev, 0u, stream);
+}
+
+// Identities of the LIBSCAN_OP_* operators.
+uint32_t op_identity(int op)
+{
+    static const uint32_t id[7] = {0u, 1u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu, 0u};
+    return id[op];
 }
 
 int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_depth,
@@ -286,6 +298,66 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
         return LIBSCAN_ERR_ARG;
     return scan_common(data, n, inclusive, algo, fork_depth, total_host, total_dev, scratch,
                        scratch_bytes, stream);
+}
+
+int scan_op_u32(uint32_t *data, uint64_t n, int op, int inclusive, uint32_t *total_host,
+                uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX || (inclusive != 0 && inclusive != 1))
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(data) || misaligned4(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value(total_host, total_dev, op_identity(op), stream);
+    if (!data || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, scan_lookback_body_bytes(n, 3), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *tot = total_dev ? total_dev : s.total_slot();
+    hipError_t e = prepare_state(s, kKindDesc, 0, scan_lookback_body_bytes(n, 3), 1, stream);
+    if (e == hipSuccess)
+        e = launch_scan_op(data, n, op, inclusive != 0, s, tot, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (total_host)
+        return read_back(total_host, tot, stream);
+    return LIBSCAN_OK;
+}
+
+size_t reduce_scratch_bytes(uint64_t n)
+{
+    (void)n;
+    return with_header(reduce_body_bytes());
+}
+
+int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host,
+                  uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(data) || misaligned4(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value(total_host, total_dev, op_identity(op), stream);
+    if (!data || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, reduce_body_bytes(), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *tot = total_dev ? total_dev : s.total_slot();
+    hipError_t e = prepare_state(s, kKindData, 0, 0, 0, stream);
+    if (e == hipSuccess)
+        e = launch_reduce_op(data, n, op, s, tot, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (total_host)
+        return read_back(total_host, tot, stream);
+    return LIBSCAN_OK;
 }
 
 size_t segscan_scratch_bytes(uint64_t n, uint64_t seg_len)

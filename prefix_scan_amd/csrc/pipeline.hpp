@@ -33,6 +33,7 @@
 //
 // The per-operation part is a policy type `Op`:
 //   static constexpr int BLOCK;            threads per workgroup
+//   using Monoid;                          the operator of the carry (OpAdd ...)
 //   struct Regs;                           one tile's per-thread registers
 //   struct Cells;                          one tile's LDS between phases
 //   void load(Regs &, uint32_t tile);      issue the tile's loads
@@ -143,12 +144,13 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
                 info_next = op.summary(s_cells[nb], nxt);
                 publish_info(nxt, info_next);
             }
-            uint32_t excl = 0;
+            using M = typename Op::Monoid;
+            uint32_t excl = M::identity;
             if (carry_needed)
-                excl = lookback_from(desc, cur, tag, w0);
+                excl = lookback_from<M>(desc, cur, tag, w0);
             if (threadIdx.x == 0) {
                 if (cur != 0 && !info_cur.final)
-                    publish(desc, cur, tag, kStatusPrefix, excl + info_cur.value);
+                    publish(desc, cur, tag, kStatusPrefix, M::apply(excl, info_cur.value));
                 s_carry = excl;
                 if (cur == ntiles - 1)
                     op.last(excl, info_cur);

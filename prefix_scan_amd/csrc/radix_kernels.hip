@@ -93,6 +93,7 @@ __global__ __launch_bounds__(BLOCK) void bit_ones_kernel(const uint32_t *__restr
 template <int BLOCK_, int V, bool FIRST, bool LAST>
 struct Radix1Op {
     static constexpr int BLOCK = BLOCK_;
+    using Monoid = OpAdd;
     static constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
     using TS = TileScan<BLOCK, V>;
     // The zero flags and their scan inside each chunk are recomputed from

@@ -86,11 +86,12 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
 // once, two tiles per workgroup, a tile's carry folded only after the next
 // tile is loaded and its aggregate published (pipeline.hpp).
 // ---------------------------------------------------------------------------
-template <int BLOCK_, int V, bool INCL>
+template <int BLOCK_, int V, bool INCL, class M = OpAdd>
 struct ScanOp {
     static constexpr int BLOCK = BLOCK_;
     static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    using TS = TileScan<BLOCK, V>;
+    using Monoid = M;
+    using TS = TileScan<BLOCK, V, M>;
     // The wave prefix of the chunk sums is not held across the step: finish
     // rebuilds it from the chunk totals (one DPP scan per chunk run), which
     // frees V registers per tile.
@@ -118,8 +119,23 @@ struct ScanOp {
             load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
     }
 
-    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
     {
+        if constexpr (M::identity != 0u) {
+            // The guarded loads read slots outside the array as 0; under an
+            // operator whose identity is not 0 they must hold the identity.
+            if (!whole(t)) {
+                const uint64_t vs = (uint64_t)t * T;
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const uint64_t v0 = vs + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
+                    if (!(v0 + 0 >= vlo && v0 + 0 < vhi)) r.x[k].x = M::identity;
+                    if (!(v0 + 1 >= vlo && v0 + 1 < vhi)) r.x[k].y = M::identity;
+                    if (!(v0 + 2 >= vlo && v0 + 2 < vhi)) r.x[k].z = M::identity;
+                    if (!(v0 + 3 >= vlo && v0 + 3 < vhi)) r.x[k].w = M::identity;
+                }
+            }
+        }
         uint32_t w[V];
         TS::local(r.x, w, c.c);
     }
@@ -129,14 +145,17 @@ struct ScanOp {
         return TileInfo{TS::cells(c.c), false, true};
     }
 
-    __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const { *total_out = carry + in.value; }
+    __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const
+    {
+        *total_out = M::apply(carry, in.value);
+    }
 
     __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
     {
         uint32_t w[V];
 #pragma unroll
         for (int k = 0; k < V; ++k)
-            w[k] = wave_incl_add(r.x[k].w);
+            w[k] = wave_incl<M>(r.x[k].w);
         TS::template apply<INCL>(r.x, w, c.c, carry);
         if (whole(t))
             store_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
@@ -145,14 +164,14 @@ struct ScanOp {
     }
 };
 
-template <int BLOCK, int V, bool INCL>
+template <int BLOCK, int V, bool INCL, class M = OpAdd>
 __global__ __launch_bounds__(BLOCK) void scan_pipelined_kernel(uint32_t *__restrict__ abase,
                                                                uint64_t vlo, uint64_t vhi,
                                                                uint32_t ntiles, uint64_t *ticket,
                                                                uint32_t *exits, uint64_t *desc,
                                                                uint32_t *total_out)
 {
-    ScanOp<BLOCK, V, INCL> op{abase, vlo, vhi, total_out};
+    ScanOp<BLOCK, V, INCL, M> op{abase, vlo, vhi, total_out};
     pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
@@ -447,6 +466,47 @@ hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, uns
     }
     // Pass 3: each block rescanned in place from its base.
     launch_scan_blocks(data, n, blocks, bsize, sums, nullptr, inclusive, stream);
+    return hipGetLastError();
+}
+
+// Scan under another operator: the pipelined kernel at the default shape.
+template <class M>
+static hipError_t scan_op_m(uint32_t *data, uint64_t n, bool inclusive, const Scratch &s,
+                            uint32_t *total_out, hipStream_t stream)
+{
+    constexpr int B = 512, V = 16;
+    constexpr uint64_t T = (uint64_t)B * V * 4;
+    const uint32_t head = head_of(data);
+    const uint64_t ntiles = tiles_for(n, head, T);
+    auto kern = inclusive ? scan_pipelined_kernel<B, V, true, M> : scan_pipelined_kernel<B, V, false, M>;
+    uint64_t grid = (uint64_t)resident_grid((const void *)kern, B);
+    if (grid > ntiles)
+        grid = ntiles;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(B), 0, stream, data - head, (uint64_t)head,
+                       n + head, (uint32_t)ntiles, s.ticket(), s.exits(), s.desc(), total_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_op(uint32_t *data, uint64_t n, int op, bool inclusive, const Scratch &s,
+                          uint32_t *total_out, hipStream_t stream)
+{
+    switch (op) {
+    case 0: return launch_scan_lookback(data, n, inclusive, true, s, total_out, stream);
+    case 1: return scan_op_m<OpMul>(data, n, inclusive, s, total_out, stream);
+    case 2: return scan_op_m<OpAnd>(data, n, inclusive, s, total_out, stream);
+    case 3: return scan_op_m<OpOr>(data, n, inclusive, s, total_out, stream);
+    case 4: return scan_op_m<OpXor>(data, n, inclusive, s, total_out, stream);
+    case 5: return scan_op_m<OpMin>(data, n, inclusive, s, total_out, stream);
+    case 6: return scan_op_m<OpMax>(data, n, inclusive, s, total_out, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t value) { *p = value; }
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, hipStream_t stream)
+{
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(1), 0, stream, p, value);
     return hipGetLastError();
 }
 

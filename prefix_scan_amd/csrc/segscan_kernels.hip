@@ -100,6 +100,7 @@ __device__ __forceinline__ uint64_t segment_ending_at(const HeadMap &h, uint32_t
 template <int BLOCK_, int V, bool VEC_OUT, bool SMALL_L>
 struct SegscanOp {
     static constexpr int BLOCK = BLOCK_;
+    using Monoid = OpAdd;
     static constexpr int NW = BLOCK / kWave;
     static constexpr int NCELL = NW * V;
     static constexpr int CPL = (NCELL + kWave - 1) / kWave;

@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
     for must in ["scan_exclusive_u32", "scan_inclusive_u32", "scan_u32_ex", "segscan_u32",
                  "compact_flags_u32", "radix_perm_u32", "scan_scratch_bytes",
                  "segscan_scratch_bytes", "compact_scratch_bytes", "radix_scratch_bytes",
-                 "libscan_strerror", "libscan_scratch_init", "copy_u32"]:
+                 "libscan_strerror", "libscan_scratch_init", "copy_u32", "scan_op_u32",
+                 "reduce_op_u32", "reduce_scratch_bytes"]:
         assert must in names
 
 
@@ -152,3 +153,25 @@ def test_python_binding_rejects_cpu_tensors():
         ps.scan_exclusive_u32(torch.zeros(8, dtype=torch.float32))
     with pytest.raises(TypeError):
         ps.scan_exclusive_u32([1, 2, 3])
+
+
+def test_operator_scan_and_reduce_argument_errors():
+    L = ps.lib()
+    big = 1 << 20
+    for op in (-1, 7):
+        assert L.scan_op_u32(FAKE, 16, op, 0, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+        assert L.reduce_op_u32(FAKE, 16, op, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+    assert L.scan_op_u32(FAKE, 16, 6, 2, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+    assert L.scan_op_u32(NULLP, 16, 6, 0, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.reduce_op_u32(FAKE, 16, 5, NOHOST, NULLP, NULLP, big, NULLP) == ps.ERR_NULL
+    assert L.scan_op_u32(ctypes.c_void_p(0x100002), 16, 1, 0, NOHOST, NULLP, FAKE, big,
+                         NULLP) == ps.ERR_ALIGN
+    assert L.reduce_op_u32(FAKE, (1 << 36) + 1, 2, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.scan_op_u32(FAKE, 1 << 24, 3, 1, NOHOST, NULLP, FAKE,
+                         L.scan_scratch_bytes(1 << 24) - 300, NULLP) == ps.ERR_SCRATCH
+    assert L.reduce_op_u32(FAKE, 16, 4, NOHOST, NULLP, FAKE, 100, NULLP) == ps.ERR_SCRATCH
+    # Empty: OK, nothing launched when no result is asked for.
+    assert L.scan_op_u32(NULLP, 0, 6, 1, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
+    assert L.reduce_op_u32(NULLP, 0, 1, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
+    with pytest.raises(ValueError):
+        ps._op("sum")
