@@ -27,9 +27,9 @@ def shaped(op, n, seed):
     if op == "mul":
         return (rng.integers(0, 2**32, n, dtype=np.uint32) | 1).astype(np.uint32)
     if op == "max":
-        return ((i * 16) % 2**32 + rng.integers(0, 64, n)).astype(np.uint32)
+        return (((i * 16) + rng.integers(0, 64, n, dtype=np.uint64)) % 2**32).astype(np.uint32)
     if op == "min":
-        return ((2**32 - 1 - (i * 16) % 2**32) - rng.integers(0, 64, n)).astype(np.uint32)
+        return (np.uint64(2**32 - 1) - ((i * 16) + rng.integers(0, 64, n, dtype=np.uint64)) % 2**32).astype(np.uint32)
     # one bit, whose position climbs through 0..31 along the array
     bit = (i * 32 // max(n, 1)).astype(np.uint64)
     if op == "or":
