@@ -33,6 +33,11 @@ def load():
     lib.oracle_scan_op_u32.restype = ctypes.c_uint32
     lib.oracle_reduce_op_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_int]
     lib.oracle_reduce_op_u32.restype = ctypes.c_uint32
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.oracle_scan_op_u64.argtypes = [u64p, u64p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_scan_op_u64.restype = ctypes.c_uint64
+    lib.oracle_reduce_op_u64.argtypes = [u64p, ctypes.c_uint64, ctypes.c_int]
+    lib.oracle_reduce_op_u64.restype = ctypes.c_uint64
     lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
     lib.oracle_scan_blocked_u32.restype = ctypes.c_int
     lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
@@ -86,6 +91,29 @@ def reduce_op_u32(a, op):
     """O1c: the fold of a under the operator named `op`."""
     a = _u32(a)
     return int(load().oracle_reduce_op_u32(_ptr(a, ctypes.c_uint32), a.size, OPS[op]))
+
+
+def _u64(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint64:
+        raise TypeError("expected a uint64 array, got %s" % a.dtype)
+    return a
+
+
+def scan_op_u64(a, op, inclusive=False):
+    """O1d: (out, total) -- scan of the u64 array a under the operator named
+    `op`, mod 2^64; the exclusive form starts from the operator's identity."""
+    a = _u64(a)
+    out = np.empty_like(a)
+    total = load().oracle_scan_op_u64(_ptr(a, ctypes.c_uint64), _ptr(out, ctypes.c_uint64),
+                                      a.size, OPS[op], 1 if inclusive else 0)
+    return out, int(total)
+
+
+def reduce_op_u64(a, op):
+    """O1d: the fold of the u64 array a under the operator named `op`."""
+    a = _u64(a)
+    return int(load().oracle_reduce_op_u64(_ptr(a, ctypes.c_uint64), a.size, OPS[op]))
 
 
 def scan_exclusive_u32(a):

@@ -9,7 +9,7 @@
  * Every function below is the plain definition of its result, written as a
  * loop in index order, in 32-bit unsigned arithmetic (C defines unsigned
  * overflow as wrap-around mod 2^32, which is the wrapping add the pages
- * require).  Where a page describes a schedule (the blocked three-pass scan,
+ * require) -- and, for the u64 rows, in 64-bit unsigned arithmetic mod 2^64.  Where a page describes a schedule (the blocked three-pass scan,
  * the one-bit radix passes), that schedule is written out step by step as a
  * second function, used by the tests to check that every schedule reaches the
  * same bits as the definition.
@@ -18,7 +18,8 @@
  *   [bend]  bendlib, "scan.bend source": header comment (contract, fork depth,
  *           three passes), "Loops (one lane)", "Pass 1", "Pass 3", "Driver",
  *           "API".
- *   [cairn] CAIRN, "Concurrency": sections "reduce and compact" and "scan".
+ *   [cairn] CAIRN, "Concurrency": sections "Tasks and leases", "reduce and
+ *           compact" and "scan".
  *   [futh]  Futhark 0.7.4, Futhark.Pass.ExtractKernels.Segmented:
  *           regularSegmentedRedomap (Large / Small), regularSegmentedScan.
  *   [ent]   entelechy docs, package "parallel": kernel table rows
@@ -131,6 +132,73 @@ uint32_t oracle_reduce_op_u32(const uint32_t *a, uint64_t n, int op)
     uint32_t acc = op_identity(op);
     for (uint64_t j = 0; j < n; ++j)
         acc = op_apply(op, acc, a[j]);
+    return acc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O1d -- the same scan and reduction on unsigned 64-bit values.             */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [cairn] "Tasks and leases", "reduce and compact" and "scan": the page's own
+ * rows are u64 (fill and total with add_wrap, the weights, the checksum's
+ * mul_wrap and ^), and its pooled scan is measured on u64 elements.  The
+ * operators, the operator codes and the identities are those of O1c, taken
+ * mod 2^64 (C defines uint64_t overflow as wrap-around mod 2^64); the
+ * identity of & and min is 2^64 - 1.
+ */
+static uint64_t op_identity64(int op)
+{
+    switch (op) {
+    case 1: return 1u;
+    case 2: return UINT64_MAX;
+    case 5: return UINT64_MAX;
+    default: return 0u;
+    }
+}
+
+static uint64_t op_apply64(int op, uint64_t a, uint64_t b)
+{
+    switch (op) {
+    case 0: return a + b;
+    case 1: return a * b;
+    case 2: return a & b;
+    case 3: return a | b;
+    case 4: return a ^ b;
+    case 5: return a < b ? a : b;
+    case 6: return a > b ? a : b;
+    default: return 0u;
+    }
+}
+
+/* Returns the fold of all n values (the identity for n == 0); out may equal
+ * a.  An operator code outside 0..6 returns 0 and writes nothing. */
+uint64_t oracle_scan_op_u64(const uint64_t *a, uint64_t *out, uint64_t n, int op, int inclusive)
+{
+    if (op < 0 || op > 6)
+        return 0u;
+    uint64_t running = op_identity64(op);
+    for (uint64_t j = 0; j < n; ++j) {
+        uint64_t x = a[j];
+        if (inclusive) {
+            running = op_apply64(op, running, x);
+            out[j] = running;
+        } else {
+            out[j] = running;
+            running = op_apply64(op, running, x);
+        }
+    }
+    return running;
+}
+
+/* [cairn] "reduce and compact": the fold of n u64 values in index order. */
+uint64_t oracle_reduce_op_u64(const uint64_t *a, uint64_t n, int op)
+{
+    if (op < 0 || op > 6)
+        return 0u;
+    uint64_t acc = op_identity64(op);
+    for (uint64_t j = 0; j < n; ++j)
+        acc = op_apply64(op, acc, a[j]);
     return acc;
 }
 

@@ -432,3 +432,104 @@ def test_op_scan_add_is_the_plain_scan_and_empty_is_identity():
     for op, ident in OP_IDENTITY.items():
         assert oracle.scan_op_u32(np.zeros(0, dtype=np.uint32), op)[1] == ident
         assert oracle.reduce_op_u32(np.zeros(0, dtype=np.uint32), op) == ident
+
+
+# ---------------------------------------------------------------------------
+# O1d -- the same operators on u64 values, mod 2^64.
+# ---------------------------------------------------------------------------
+M64 = 1 << 64
+OP_IDENTITY64 = {"add": 0, "mul": 1, "and": M64 - 1, "or": 0, "xor": 0, "min": M64 - 1, "max": 0}
+
+
+def test_op64_cairn_examples():
+    # CAIRN "Concurrency": the page's rows are u64.  "Tasks and leases":
+    # samples = 0..899, total with add_wrap 404550.  "reduce and compact":
+    # weights i % 7 over 10000, sum 29994, max 6.  "scan": sizes i + 1,
+    # exclusive offsets [0, 1, 3, 6] with total 10; max scan of 2, 4, 6, 8.
+    g = golden("cairn_tasks_total.json")
+    samples = np.arange(g["n"], dtype=np.uint64)
+    assert oracle.reduce_op_u64(samples, "add") == g["total"]
+    assert oracle.scan_op_u64(samples, "add")[1] == g["total"]
+    g = golden("cairn_reduce_weights.json")
+    w = (np.arange(g["n"]) % g["modulus"]).astype(np.uint64)
+    assert oracle.reduce_op_u64(w, "add") == g["sum"]
+    assert oracle.reduce_op_u64(w, "max") == g["max"]
+    g = golden("cairn_scan_offsets.json")
+    ex, tot = oracle.scan_op_u64(np.array(g["input"], dtype=np.uint64), "add")
+    assert tot == g["total"]
+    for j, v in g["exclusive_at"].items():
+        assert int(ex[int(j)]) == v
+    g = golden("cairn_scan_max.json")
+    out, tot = oracle.scan_op_u64(np.array(g["yields"], dtype=np.uint64), "max", inclusive=True)
+    for k, v in g["inclusive_at"].items():
+        assert int(out[int(k)]) == v
+
+
+@pytest.mark.parametrize("op", sorted(OP_IDENTITY64))
+@pytest.mark.parametrize("n", [1, 2, 7, 1000, 65537])
+def test_op64_scan_matches_numpy_accumulate(op, n):
+    # numpy's ufunc accumulate in uint64 (wrapping mod 2^64 for add and multiply).
+    rng = np.random.default_rng(2000 + n)
+    a = rng.integers(0, 2**64, n, dtype=np.uint64)
+    if op == "mul":
+        a |= np.uint64(1)
+    ref = NP_ACCUMULATE[op].accumulate(a, dtype=np.uint64)
+    inc, total = oracle.scan_op_u64(a, op, inclusive=True)
+    assert np.array_equal(inc, ref)
+    exc, total_e = oracle.scan_op_u64(a, op, inclusive=False)
+    assert int(exc[0]) == OP_IDENTITY64[op]
+    assert np.array_equal(exc[1:], ref[:-1])
+    assert total == total_e == int(ref[-1]) == oracle.reduce_op_u64(a, op)
+
+
+@pytest.mark.parametrize("op", sorted(OP_IDENTITY64))
+def test_op64_scan_brute_force_small(op):
+    # Python integers reduced mod 2^64 after every step.
+    apply = {"add": lambda x, y: (x + y) % M64, "mul": lambda x, y: (x * y) % M64,
+             "and": lambda x, y: x & y, "or": lambda x, y: x | y, "xor": lambda x, y: x ^ y,
+             "min": min, "max": max}[op]
+    vals = np.array([0, 1, 3, 2**31, 2**32 - 1, 2**32, 2**63, M64 - 1, 0xDEADBEEFCAFEF00D],
+                    dtype=np.uint64)
+    rng = np.random.default_rng(78)
+    for n in range(0, 12):
+        a = rng.choice(vals, n)
+        run, inc, exc = OP_IDENTITY64[op], [], []
+        for x in a.tolist():
+            exc.append(run)
+            run = apply(run, x)
+            inc.append(run)
+        got, total = oracle.scan_op_u64(a, op, inclusive=True)
+        assert got.tolist() == inc and total == run
+        got, total = oracle.scan_op_u64(a, op, inclusive=False)
+        assert got.tolist() == exc and total == run
+
+
+def test_op64_carry_crosses_the_32_bit_boundary():
+    # Sums of 2^32 - 1 climb into the high word: exclusive j * (2^32 - 1)
+    # (a 32-bit sum would wrap); 2^63 alternates 0, 2^63; all-ones wraps to -j.
+    n = 1 << 12
+    j = [int(x) for x in range(n)]
+    ex, tot = oracle.scan_op_u64(np.full(n, 2**32 - 1, dtype=np.uint64), "add")
+    assert ex.tolist() == [k * (2**32 - 1) for k in j] and tot == n * (2**32 - 1)
+    ex, tot = oracle.scan_op_u64(np.full(n, 2**63, dtype=np.uint64), "add")
+    assert ex.tolist() == [(k % 2) * 2**63 for k in j] and tot == 0
+    ex, tot = oracle.scan_op_u64(np.full(n, M64 - 1, dtype=np.uint64), "add")
+    assert ex.tolist() == [(-k) % M64 for k in j] and tot == (-n) % M64
+    # product of j + 1 threes mod 2^64.
+    pr, _ = oracle.scan_op_u64(np.full(64, 3, dtype=np.uint64), "mul", inclusive=True)
+    assert pr.tolist() == [pow(3, k + 1, M64) for k in range(64)]
+
+
+@pytest.mark.parametrize("op", sorted(OP_IDENTITY64))
+def test_op64_agrees_with_u32_below_2_32(op):
+    # On values below 2^32 every operator's u64 result, taken mod 2^32 (for
+    # add and mul) or as is (the others), is the u32 oracle's.
+    a = np.random.default_rng(9).integers(0, 2**32, 5000, dtype=np.uint32)
+    if op == "mul":
+        a |= np.uint32(1)
+    r64, t64 = oracle.scan_op_u64(a.astype(np.uint64), op, inclusive=True)
+    r32, t32 = oracle.scan_op_u32(a, op, inclusive=True)
+    assert np.array_equal((r64 % M).astype(np.uint32), r32)
+    assert t64 % M == t32
+    assert oracle.scan_op_u64(np.zeros(0, dtype=np.uint64), op)[1] == OP_IDENTITY64[op]
+    assert oracle.reduce_op_u64(np.zeros(0, dtype=np.uint64), op) == OP_IDENTITY64[op]
