@@ -201,6 +201,16 @@ def suite(args, torch, ps):
                 row("reduce %s n=%s" % (op, label), n, 4,
                     lambda: ps.reduce_op_u32(d, op, want_total=False, total_dev=dst[:1]))
         del d, dst
+    # u64 values at the same byte size (scan 16 B/element, reduction 8).
+    d = torch.from_numpy(workloads.uniform_u64(workloads.N_SCAN_U64, workloads.SEED_SCAN_U64)
+                         .view(np.int64)).to("cuda")
+    tot = torch.empty(1, dtype=torch.int64, device="cuda")
+    for op in ("add", "max"):
+        row("scan exclusive u64 %s n=2^27" % op, d.numel(), 16,
+            lambda: ps.scan_op_u64(d, op, want_total=False))
+    row("reduce u64 add n=2^27", d.numel(), 8,
+        lambda: ps.reduce_op_u64(d, "add", want_total=False, total_dev=tot))
+    del d, tot
     for p in (0.5, 0.01, 0.99):
         f = torch.from_numpy(workloads.compact_flags(p)).to("cuda")
         o = torch.empty_like(f)
@@ -243,16 +253,17 @@ PROFILE_COMMANDS = [
 
 def algorithmic_bytes(name, grid):
     """Bytes a dispatch must move at the sizes of the --hbm-rows suite (scans
-    and copy at 2^28, compaction and segmented scan at 2^26, radix at 2^25),
-    or None for bookkeeping kernels."""
+    and copy at 2^28, u64 scan and reduction at 2^27, compaction and segmented
+    scan at 2^26, radix at 2^25), or None for bookkeeping kernels."""
     big = grid >= (1 << 16)            # threads: a data pass, not a table scan
-    n28, n26, n25 = 1 << 28, 1 << 26, 1 << 25
+    n28, n27, n26, n25 = 1 << 28, 1 << 27, 1 << 26, 1 << 25
     table = [
         ("scan_pipelined_kernel", 8 * n28), ("copy_kernel", 8 * n28),
         ("reduce_blocks_kernel", 4 * n28), ("compact_kernel", 8 * n26),
         ("segscan_independent_kernel", 8 * n26 + 4 * (n26 // 16)),
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
         ("digit_hist_kernel", 4 * n25), ("reduce_partial_kernel", 4 * n28),
+        ("scan64_pipelined_kernel", 16 * n27), ("reduce64_partial_kernel", 8 * n27),
     ]
     for key, b in table:
         if "::" + key + "<" in name:

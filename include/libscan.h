@@ -187,13 +187,31 @@ int scan_op_u32(uint32_t *data, uint64_t n, int op, int inclusive, uint32_t *tot
  * The fold of n u32 values under `op` (CAIRN "reduce and compact"); `data`
  * is only read.  The result goes to *total_host (the call then waits)
  * and/or *total_dev (4-byte aligned device u32).  Scratch: at least
- * reduce_scratch_bytes(n) (a small constant).  Errors: LIBSCAN_ERR_ARG for
+ * reduce_scratch_bytes(n) (a small constant, enough for reduce_op_u64 too).  Errors: LIBSCAN_ERR_ARG for
  * an op outside the range; LIBSCAN_ERR_NULL, _SIZE, _ALIGN, _SCRATCH, _HIP
  * as for the scans.
  */
 size_t reduce_scratch_bytes(uint64_t n);
 int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host,
                   uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/*
+ * The same scan and reduction over n u64 values, mod 2^64.  CAIRN
+ * "Concurrency" writes its rows as u64 ("Tasks and leases": the add_wrap
+ * total of 0..899 is 404550; "reduce and compact": u64 weights, a checksum
+ * mixed with mul_wrap and ^; "scan": its scan is measured on u64 elements).
+ * Operators and identities as above, with 2^64 - 1 the identity of AND and
+ * MIN.  `data` and `total_dev` must be 8-byte aligned (LIBSCAN_ERR_ALIGN
+ * otherwise); element i is at byte offset 8*i.  Scan scratch: at least
+ * scan_op_u64_scratch_bytes(n); reduction scratch: reduce_scratch_bytes(n),
+ * which covers both widths.  Ownership, stream, result and error rules as
+ * for scan_op_u32 / reduce_op_u32.
+ */
+size_t scan_op_u64_scratch_bytes(uint64_t n);
+int scan_op_u64(uint64_t *data, uint64_t n, int op, int inclusive, uint64_t *total_host,
+                uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host,
+                  uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Segmented scan and segment sums over regular segments                    */

@@ -7,7 +7,8 @@ computation runs in the library's HIP kernels; there is no CPU fallback, and
 a missing ``libscan.so`` raises.
 
 PyTorch supplies device memory and streams.  Tensors must be on a CUDA (HIP)
-device, contiguous, with 4-byte elements (torch.int32 or torch.uint32).
+device, contiguous, with 4-byte elements (torch.int32 or torch.uint32), or
+8-byte elements (torch.int64 or torch.uint64) for the *_u64 entry points.
 """
 import ctypes
 import os
@@ -18,6 +19,7 @@ import torch
 __all__ = [
     "LibscanError", "lib", "version",
     "scan_exclusive_u32", "scan_inclusive_u32", "scan_u32_ex",
+    "scan_op_u32", "reduce_op_u32", "scan_op_u64", "reduce_op_u64",
     "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
     "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
     "compact_scratch_bytes", "radix_scratch_bytes",
@@ -80,6 +82,13 @@ def lib():
         L.reduce_scratch_bytes.restype = sz
         L.reduce_op_u32.argtypes = [vp, u64, i32, u32p, vp, vp, sz, vp]
         L.reduce_op_u32.restype = i32
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        L.scan_op_u64_scratch_bytes.argtypes = [u64]
+        L.scan_op_u64_scratch_bytes.restype = sz
+        L.scan_op_u64.argtypes = [vp, u64, i32, i32, u64p, vp, vp, sz, vp]
+        L.scan_op_u64.restype = i32
+        L.reduce_op_u64.argtypes = [vp, u64, i32, u64p, vp, vp, sz, vp]
+        L.reduce_op_u64.restype = i32
         L.segscan_scratch_bytes.argtypes = [u64, u64]
         L.segscan_scratch_bytes.restype = sz
         L.segscan_u32.argtypes = [vp, vp, u64, u64, vp, vp, sz, vp]
@@ -114,6 +123,18 @@ def _dev_u32(t, name):
         raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
     if t.dtype not in (torch.int32, torch.uint32):
         raise TypeError("%s must be int32 or uint32, got %s" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _dev_u64(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if t.dtype not in (torch.int64, torch.uint64):
+        raise TypeError("%s must be int64 or uint64, got %s" % (name, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t
@@ -235,6 +256,41 @@ def reduce_op_u32(data, op, want_total=True, total_dev=None, stream=None):
     host, hp = _total_args(want_total, total_dev)
     _check(lib().reduce_op_u32(_ptr(data), data.numel(), o, hp, _ptr(total_dev), _ptr(scr),
                                scr.numel(), sh), "reduce_op_u32")
+    return int(host.value) if want_total else None
+
+
+def _total64_args(want_total, total_dev):
+    host = ctypes.c_uint64(0)
+    hp = ctypes.pointer(host) if want_total else ctypes.POINTER(ctypes.c_uint64)()
+    if total_dev is not None:
+        _dev_u64(total_dev, "total_dev")
+    return host, hp
+
+
+def scan_op_u64(data, op, inclusive=False, want_total=True, total_dev=None, stream=None):
+    """In-place scan of the 64-bit tensor `data` (int64 or uint64, taken as
+    unsigned) under `op`, mod 2^64; returns the fold of all values as an int
+    in [0, 2^64) when want_total, else None."""
+    _dev_u64(data, "data")
+    o = _op(op)
+    sh, s = _stream_handle(data.device, stream)
+    scr = _scratch_for(data.device, s, lib().scan_op_u64_scratch_bytes(data.numel()))
+    host, hp = _total64_args(want_total, total_dev)
+    _check(lib().scan_op_u64(_ptr(data), data.numel(), o, 1 if inclusive else 0, hp,
+                             _ptr(total_dev), _ptr(scr), scr.numel(), sh), "scan_op_u64")
+    return int(host.value) if want_total else None
+
+
+def reduce_op_u64(data, op, want_total=True, total_dev=None, stream=None):
+    """The fold of the 64-bit tensor `data` under `op`, mod 2^64 (data is
+    only read)."""
+    _dev_u64(data, "data")
+    o = _op(op)
+    sh, s = _stream_handle(data.device, stream)
+    scr = _scratch_for(data.device, s, lib().reduce_scratch_bytes(data.numel()))
+    host, hp = _total64_args(want_total, total_dev)
+    _check(lib().reduce_op_u64(_ptr(data), data.numel(), o, hp, _ptr(total_dev), _ptr(scr),
+                               scr.numel(), sh), "reduce_op_u64")
     return int(host.value) if want_total else None
 
 

@@ -122,6 +122,37 @@ struct OpMax {
     __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a > b ? a : b; }
 };
 
+// The same operators on unsigned 64-bit values (CAIRN writes its rows as
+// u64), each with its identity mod 2^64.
+struct OpAdd64 {
+    static constexpr uint64_t identity = 0u;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a + b; }
+};
+struct OpMul64 {
+    static constexpr uint64_t identity = 1u;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a * b; }
+};
+struct OpAnd64 {
+    static constexpr uint64_t identity = ~0ull;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a & b; }
+};
+struct OpOr64 {
+    static constexpr uint64_t identity = 0u;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a | b; }
+};
+struct OpXor64 {
+    static constexpr uint64_t identity = 0u;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a ^ b; }
+};
+struct OpMin64 {
+    static constexpr uint64_t identity = ~0ull;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a < b ? a : b; }
+};
+struct OpMax64 {
+    static constexpr uint64_t identity = 0u;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a > b ? a : b; }
+};
+
 // DPP move whose disabled lanes (source outside the row, masked rows) read
 // `old` -- the operator's identity.
 template <int CTRL, int ROW_MASK>
@@ -160,6 +191,50 @@ template <class Op>
 __device__ __forceinline__ uint32_t wave_shr1_op(uint32_t x)
 {
     return dpp_or<kDppWaveShr1, 0xF>(x, Op::identity);
+}
+
+// 64-bit lanes: each DPP step moves the two halves with the same control,
+// so a lane always receives one whole value (or the identity's halves).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp64_or(uint64_t x, uint64_t old)
+{
+    const uint32_t lo = dpp_or<CTRL, ROW_MASK>((uint32_t)x, (uint32_t)old);
+    const uint32_t hi = dpp_or<CTRL, ROW_MASK>((uint32_t)(x >> 32), (uint32_t)(old >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive wave scan of u64 values under Op (the steps of wave_incl_add).
+template <class Op>
+__device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
+{
+    constexpr uint64_t e = Op::identity;
+    x = Op::apply(x, dpp64_or<kDppRowShr1, 0xF>(x, e));
+    x = Op::apply(x, dpp64_or<kDppRowShr2, 0xF>(x, e));
+    x = Op::apply(x, dpp64_or<kDppRowShr4, 0xF>(x, e));
+    x = Op::apply(x, dpp64_or<kDppRowShr8, 0xF>(x, e));
+    x = Op::apply(x, dpp64_or<kDppRowBcast15, 0xA>(x, e));
+    x = Op::apply(x, dpp64_or<kDppRowBcast31, 0xC>(x, e));
+    return x;
+}
+
+__device__ __forceinline__ uint64_t wave_bcast_last64(uint64_t x)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <class Op>
+__device__ __forceinline__ uint64_t wave_fold64(uint64_t x)
+{
+    return wave_bcast_last64(wave_incl64<Op>(x));
+}
+
+// The previous lane's value (Op's identity in lane 0).
+template <class Op>
+__device__ __forceinline__ uint64_t wave_shr1_64(uint64_t x)
+{
+    return dpp64_or<kDppWaveShr1, 0xF>(x, Op::identity);
 }
 
 // Segmented inclusive wave scan of (head flag, value) pairs under
@@ -304,6 +379,41 @@ __device__ __forceinline__ void store_tile(uint32_t *abase, uint64_t vstart, uin
         for (int k = 0; k < V; ++k)
             store4_guarded(abase, q0 + (uint64_t)k * BLOCK, x[k], vlo, vhi);
     }
+}
+
+// u64 arrays use the same 16-byte chunks, two elements each: the virtual
+// index is v = i + head with head = (address / 8) mod 2, so virtual chunk q
+// holds u64 elements 2q and 2q + 1 (lanes x, y and z, w of the u32x4).
+__device__ __forceinline__ uint64_t chunk_lo64(const u32x4 &c) { return ((uint64_t)c.y << 32) | c.x; }
+__device__ __forceinline__ uint64_t chunk_hi64(const u32x4 &c) { return ((uint64_t)c.w << 32) | c.z; }
+__device__ __forceinline__ u32x4 chunk_of64(uint64_t e0, uint64_t e1)
+{
+    return u32x4{(uint32_t)e0, (uint32_t)(e0 >> 32), (uint32_t)e1, (uint32_t)(e1 >> 32)};
+}
+
+// Chunk q of a u64 array with every element outside [vlo, vhi) read as fill.
+__device__ __forceinline__ u32x4 load2_guarded64(const uint64_t *abase, uint64_t q, uint64_t vlo,
+                                                 uint64_t vhi, uint64_t fill)
+{
+    const uint64_t v0 = q * 2;
+    if (v0 >= vlo && v0 + 2 <= vhi)
+        return load4(reinterpret_cast<const uint32_t *>(abase), q);
+    const uint64_t e0 = (v0 >= vlo && v0 < vhi) ? abase[v0] : fill;
+    const uint64_t e1 = (v0 + 1 >= vlo && v0 + 1 < vhi) ? abase[v0 + 1] : fill;
+    return chunk_of64(e0, e1);
+}
+
+// Store only the u64 elements of chunk q inside [vlo, vhi).
+__device__ __forceinline__ void store2_guarded64(uint64_t *abase, uint64_t q, u32x4 c,
+                                                 uint64_t vlo, uint64_t vhi)
+{
+    const uint64_t v0 = q * 2;
+    if (v0 >= vlo && v0 + 2 <= vhi) {
+        store4(reinterpret_cast<uint32_t *>(abase), q, c);
+        return;
+    }
+    if (v0 >= vlo && v0 < vhi) abase[v0] = chunk_lo64(c);
+    if (v0 + 1 >= vlo && v0 + 1 < vhi) abase[v0 + 1] = chunk_hi64(c);
 }
 
 // ---------------------------------------------------------------------------
@@ -520,6 +630,79 @@ template <class Op = OpAdd>
 __device__ __forceinline__ uint32_t lookback(const uint64_t *desc, uint32_t tile, uint32_t tag)
 {
     return lookback_from<Op>(desc, tile, tag, lookback_load(desc, (int64_t)tile - 1));
+}
+
+// ---------------------------------------------------------------------------
+// Chained carry of a u64 value: two descriptor words per tile, 2t holding
+// {tag | status, low half} and 2t + 1 {tag | status, high half}.  Each word
+// is one agent-scope atomic store, and a tile publishes each status once per
+// launch, so a reader that finds the same tag and status in both words holds
+// one publication's value; a pair caught between AGG and PREFIX disagrees
+// and is read again, like a tile not yet ready.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish64(uint64_t *desc, uint32_t tile, uint32_t tag,
+                                          uint32_t status, uint64_t value)
+{
+    const uint64_t head = (uint64_t)(tag | status) << 32;
+    __hip_atomic_store(desc + 2 * (uint64_t)tile + 1, head | (value >> 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(desc + 2 * (uint64_t)tile, head | (uint32_t)value, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct LookbackWindow64 {
+    uint64_t lo, hi;
+    bool before_start;
+};
+
+__device__ __forceinline__ LookbackWindow64 lookback64_load(const uint64_t *desc, int64_t base)
+{
+    const int64_t pi = base - (int64_t)lane_id();
+    const uint64_t q = pi < 0 ? 0 : (uint64_t)pi;
+    LookbackWindow64 w;
+    w.before_start = pi < 0;
+    w.lo = __hip_atomic_load(desc + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w.hi = __hip_atomic_load(desc + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return w;
+}
+
+// As lookback_fold, for u64 values.
+template <class Op>
+__device__ __forceinline__ int lookback64_fold(const LookbackWindow64 &w, uint32_t tag,
+                                               uint64_t &excl)
+{
+    const uint32_t hl = (uint32_t)(w.lo >> 32);
+    const uint32_t hh = (uint32_t)(w.hi >> 32);
+    const uint32_t st = w.before_start ? kStatusPrefix
+                                       : (((hl & ~3u) == tag && hl == hh) ? (hl & 3u) : 0u);
+    const uint64_t val =
+        w.before_start ? Op::identity : (((uint64_t)(uint32_t)w.hi << 32) | (uint32_t)w.lo);
+    const uint64_t pref = ballot(st == kStatusPrefix);
+    const uint64_t wait = ballot(st == 0);
+    const uint32_t p = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
+    const uint64_t upto = (p >= 63) ? ~0ull : ((2ull << p) - 1);
+    if (wait & upto)
+        return 0;
+    excl = Op::apply(excl, wave_fold64<Op>(lane_id() <= p ? val : Op::identity));
+    return pref ? 2 : 1;
+}
+
+template <class Op>
+__device__ __forceinline__ uint64_t lookback64_from(const uint64_t *desc, uint32_t tile,
+                                                    uint32_t tag, LookbackWindow64 w)
+{
+    uint64_t excl = Op::identity;
+    int r = lookback64_fold<Op>(w, tag, excl);
+    int64_t base = (int64_t)tile - 1;
+    while (r != 2) {
+        if (r == 1)
+            base -= kWave;
+        else
+            __builtin_amdgcn_s_sleep(1);
+        w = lookback64_load(desc, base);
+        r = lookback64_fold<Op>(w, tag, excl);
+    }
+    return excl;
 }
 
 }  // namespace libscan

@@ -21,8 +21,8 @@ constexpr int kBlock = 256;
 //   [8, 12)     exit counter A (grid-filling kernels)
 //   [16, 24)    ticket B (the radix histogram scan)
 //   [24, 28)    exit counter B
-//   [64, 68)    total / count slot, used when the caller asks for the result
-//               on the host only
+//   [64, 72)    total / count slot (a u32, or a u64 for the u64 entry points),
+//               used when the caller asks for the result on the host only
 // Body, from 256: each entry point's state (tile descriptors) first, then its
 // data (block sums, radix ping-pong rows).  Tickets and descriptors carry the
 // epoch of the launch that wrote them, so they stay valid from launch to
@@ -54,6 +54,7 @@ struct Scratch {
     uint32_t *exits() const { return reinterpret_cast<uint32_t *>(ticket_ptr + 1); }
     uint64_t *desc() const { return desc_ptr; }
     uint32_t *total_slot() const { return reinterpret_cast<uint32_t *>(base + kTotalSlotOffset); }
+    uint64_t *total_slot64() const { return reinterpret_cast<uint64_t *>(base + kTotalSlotOffset); }
     uint8_t *body() const { return base + kHeaderBytes; }
 };
 
@@ -84,6 +85,15 @@ hipError_t launch_reduce_op(const uint32_t *data, uint64_t n, int op, const Scra
                             uint32_t *total_out, hipStream_t stream);
 size_t reduce_body_bytes();
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
+
+// ---- u64 scan and reduction (scan64_kernels.hip) ----
+hipError_t launch_scan_op64(uint64_t *data, uint64_t n, int op, bool inclusive, const Scratch &s,
+                            uint64_t *total_out, hipStream_t stream);
+size_t scan64_body_bytes(uint64_t n, uint32_t head);
+hipError_t launch_reduce_op64(const uint64_t *data, uint64_t n, int op, const Scratch &s,
+                              uint64_t *total_out, hipStream_t stream);
+size_t reduce64_body_bytes();
+hipError_t launch_fill_u64(uint64_t *p, uint64_t value, hipStream_t stream);
 
 // ---- segmented scan (segscan_kernels.hip) ----
 hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,

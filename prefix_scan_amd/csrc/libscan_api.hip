@@ -153,6 +153,32 @@ int read_back(uint32_t *host, const uint32_t *dev, hipStream_t stream)
     return hip_status(hipStreamSynchronize(stream));
 }
 
+int read_back64(uint64_t *host, const uint64_t *dev, hipStream_t stream)
+{
+    hipError_t e = hipMemcpyAsync(host, dev, sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return hip_status(hipStreamSynchronize(stream));
+}
+
+int report_value64(uint64_t *host, uint64_t *dev, uint64_t value, hipStream_t stream)
+{
+    if (dev) {
+        hipError_t e = launch_fill_u64(dev, value, stream);
+        if (e != hipSuccess)
+            return hip_status(e);
+    }
+    if (host) {
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return hip_status(e);
+        *host = value;
+    }
+    return LIBSCAN_OK;
+}
+
+bool misaligned8(const void *p) { return ((uintptr_t)p & 7u) != 0; }
+
 // A fixed result (the operator's identity) to report for an empty input.
 int report_value(uint32_t *host, uint32_t *dev, uint32_t value, hipStream_t stream)
 {
@@ -179,6 +205,12 @@ int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
 uint32_t op_identity(int op)
 {
     static const uint32_t id[7] = {0u, 1u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu, 0u};
+    return id[op];
+}
+
+uint64_t op_identity64(int op)
+{
+    static const uint64_t id[7] = {0u, 1u, ~0ull, 0u, 0u, ~0ull, 0u};
     return id[op];
 }
 
@@ -330,7 +362,8 @@ int scan_op_u32(uint32_t *data, uint64_t n, int op, int inclusive, uint32_t *tot
 size_t reduce_scratch_bytes(uint64_t n)
 {
     (void)n;
-    return with_header(reduce_body_bytes());
+    const size_t a = reduce_body_bytes(), b = reduce64_body_bytes();
+    return with_header(a > b ? a : b);
 }
 
 int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host,
@@ -357,6 +390,65 @@ int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host
         return hip_status(e);
     if (total_host)
         return read_back(total_host, tot, stream);
+    return LIBSCAN_OK;
+}
+
+size_t scan_op_u64_scratch_bytes(uint64_t n)
+{
+    return with_header(scan64_body_bytes(n, 1));
+}
+
+int scan_op_u64(uint64_t *data, uint64_t n, int op, int inclusive, uint64_t *total_host,
+                uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX || (inclusive != 0 && inclusive != 1))
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned8(data) || misaligned8(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value64(total_host, total_dev, op_identity64(op), stream);
+    if (!data || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, scan64_body_bytes(n, 1), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint64_t *tot = total_dev ? total_dev : s.total_slot64();
+    hipError_t e = prepare_state(s, kKindDesc, 0, scan64_body_bytes(n, 1), 1, stream);
+    if (e == hipSuccess)
+        e = launch_scan_op64(data, n, op, inclusive != 0, s, tot, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (total_host)
+        return read_back64(total_host, tot, stream);
+    return LIBSCAN_OK;
+}
+
+int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host,
+                  uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned8(data) || misaligned8(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value64(total_host, total_dev, op_identity64(op), stream);
+    if (!data || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, reduce64_body_bytes(), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint64_t *tot = total_dev ? total_dev : s.total_slot64();
+    hipError_t e = prepare_state(s, kKindData, 0, 0, 0, stream);
+    if (e == hipSuccess)
+        e = launch_reduce_op64(data, n, op, s, tot, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (total_host)
+        return read_back64(total_host, tot, stream);
     return LIBSCAN_OK;
 }
 

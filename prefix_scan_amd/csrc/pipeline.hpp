@@ -34,27 +34,90 @@
 // The per-operation part is a policy type `Op`:
 //   static constexpr int BLOCK;            threads per workgroup
 //   using Monoid;                          the operator of the carry (OpAdd ...)
+//   using Carry;                           (optional) Carry64<M> for a u64 carry
 //   struct Regs;                           one tile's per-thread registers
 //   struct Cells;                          one tile's LDS between phases
 //   void load(Regs &, uint32_t tile);      issue the tile's loads
 //   void local(Regs &, Cells &, uint32_t tile);   phase 1 (all threads)
-//   TileInfo summary(Cells &, uint32_t tile);     phase 2 (wave 0 only)
-//   void finish(Regs &, Cells &, uint32_t tile, uint32_t carry);
+//   TileInfoT<T> summary(Cells &, uint32_t tile); phase 2 (wave 0 only)
+//   void finish(Regs &, Cells &, uint32_t tile, T carry);
 //                                          outputs + stores (all threads;
 //                                          may hold barriers of its own)
-//   void last(uint32_t carry, const TileInfo &);  thread 0, last tile only
+//   void last(T carry, const TileInfoT<T> &);     thread 0, last tile only
+// where T is the carry's value type (u32 unless the Op names Carry64).
 #pragma once
 
 #include "device_common.hpp"
 
+#include <type_traits>
+
 namespace libscan {
 
 // What phase 2 learned about a tile.
-struct TileInfo {
-    uint32_t value;     // published value: the tile's aggregate, or -- when
+template <class T>
+struct TileInfoT {
+    T value;            // published value: the tile's aggregate, or -- when
                         // `final` -- its inclusive prefix already
     bool final;         // the value needs no carry (publish PREFIX at once)
     bool need_carry;    // the tile's outputs depend on the tiles before it
+};
+using TileInfo = TileInfoT<uint32_t>;
+
+// How a carry of the monoid M travels between tiles: a u32 value in one
+// descriptor word per tile, or a u64 value in two.
+template <class M>
+struct Carry32 {
+    using T = uint32_t;
+    using Window = LookbackWindow;
+    static constexpr T identity = M::identity;
+    __device__ static __forceinline__ T apply(T a, T b) { return M::apply(a, b); }
+    __device__ static __forceinline__ void put(uint64_t *desc, uint32_t t, uint32_t tag,
+                                               uint32_t status, T v)
+    {
+        publish(desc, t, tag, status, v);
+    }
+    __device__ static __forceinline__ Window load(const uint64_t *desc, int64_t base)
+    {
+        return lookback_load(desc, base);
+    }
+    __device__ static __forceinline__ T from(const uint64_t *desc, uint32_t tile, uint32_t tag,
+                                             const Window &w)
+    {
+        return lookback_from<M>(desc, tile, tag, w);
+    }
+};
+
+template <class M>
+struct Carry64 {
+    using T = uint64_t;
+    using Window = LookbackWindow64;
+    static constexpr T identity = M::identity;
+    __device__ static __forceinline__ T apply(T a, T b) { return M::apply(a, b); }
+    __device__ static __forceinline__ void put(uint64_t *desc, uint32_t t, uint32_t tag,
+                                               uint32_t status, T v)
+    {
+        publish64(desc, t, tag, status, v);
+    }
+    __device__ static __forceinline__ Window load(const uint64_t *desc, int64_t base)
+    {
+        return lookback64_load(desc, base);
+    }
+    __device__ static __forceinline__ T from(const uint64_t *desc, uint32_t tile, uint32_t tag,
+                                             const Window &w)
+    {
+        return lookback64_from<M>(desc, tile, tag, w);
+    }
+};
+
+// An Op names its carry with `using Carry = ...`; without one it is the u32
+// carry of its Monoid.
+template <class Op, class = void>
+struct carry_of {
+    using type = Carry32<typename Op::Monoid>;
+};
+template <class Op>
+struct carry_of<Op, std::void_t<typename Op::Carry>> {
+    using type = typename Op::Carry;
 };
 
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
@@ -65,10 +128,14 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
 {
     constexpr int BLOCK = Op::BLOCK;
     constexpr int kDrawer = BLOCK - kWave;       // lane 0 of the last wave
+    using C = typename carry_of<Op>::type;
+    using CT = typename C::T;
+    using Info = TileInfoT<CT>;
     // Three cell buffers in rotation: a tile's cells are written two steps
     // after the buffer's previous tile was last read, with barriers between.
     __shared__ typename Op::Cells s_cells[3];
-    __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag, s_carry;
+    __shared__ uint32_t s_cur, s_nxt, s_nn, s_tag;
+    __shared__ CT s_carry;
 
     auto tile_of = [&](uint32_t raw) -> uint32_t { return raw < ntiles ? raw : kNoTile; };
     auto draw_num = [&]() -> uint32_t {
@@ -105,13 +172,13 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
         return;
 
     // Wave 0: a reduced tile's descriptor (tile 0's aggregate is its prefix).
-    auto publish_info = [&](uint32_t t, const TileInfo &in) {
+    auto publish_info = [&](uint32_t t, const Info &in) {
         if (threadIdx.x == 0)
-            publish(desc, t, tag, (t == 0 || in.final) ? kStatusPrefix : kStatusAgg, in.value);
+            C::put(desc, t, tag, (t == 0 || in.final) ? kStatusPrefix : kStatusAgg, in.value);
     };
 
     typename Op::Regs ra, rb;
-    TileInfo info_cur{0u, true, false};         // wave 0 only
+    Info info_cur{C::identity, true, false};   // wave 0 only
     int cb = 0;                                 // cell buffer of `cur`
 
     // Prologue: the first tile, loaded and reduced synchronously.
@@ -127,9 +194,9 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
     auto step = [&](typename Op::Regs &X, typename Op::Regs &Y) {
         const int nb = cb == 2 ? 0 : cb + 1;
         const bool carry_needed = cur != 0 && info_cur.need_carry;     // wave 0
-        LookbackWindow w0{0ull, true};
+        typename C::Window w0{};
         if (threadIdx.x < kWave && carry_needed)
-            w0 = lookback_load(desc, (int64_t)cur - 1);
+            w0 = C::load(desc, (int64_t)cur - 1);
         const bool drawing = threadIdx.x == kDrawer && nxt != kNoTile;
         const uint32_t nn_raw = drawing ? draw_num() : 0u;
         const bool have_next = nxt != kNoTile;
@@ -138,19 +205,18 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
             op.local(Y, s_cells[nb], nxt);
         }
         __syncthreads();
-        TileInfo info_next{0u, true, false};
+        Info info_next{C::identity, true, false};
         if (threadIdx.x < kWave) {
             if (have_next) {
                 info_next = op.summary(s_cells[nb], nxt);
                 publish_info(nxt, info_next);
             }
-            using M = typename Op::Monoid;
-            uint32_t excl = M::identity;
+            CT excl = C::identity;
             if (carry_needed)
-                excl = lookback_from<M>(desc, cur, tag, w0);
+                excl = C::from(desc, cur, tag, w0);
             if (threadIdx.x == 0) {
                 if (cur != 0 && !info_cur.final)
-                    publish(desc, cur, tag, kStatusPrefix, M::apply(excl, info_cur.value));
+                    C::put(desc, cur, tag, kStatusPrefix, C::apply(excl, info_cur.value));
                 s_carry = excl;
                 if (cur == ntiles - 1)
                     op.last(excl, info_cur);

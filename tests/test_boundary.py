@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
                  "compact_flags_u32", "radix_perm_u32", "scan_scratch_bytes",
                  "segscan_scratch_bytes", "compact_scratch_bytes", "radix_scratch_bytes",
                  "libscan_strerror", "libscan_scratch_init", "copy_u32", "scan_op_u32",
-                 "reduce_op_u32", "reduce_scratch_bytes"]:
+                 "reduce_op_u32", "reduce_scratch_bytes", "scan_op_u64", "reduce_op_u64",
+                 "scan_op_u64_scratch_bytes"]:
         assert must in names
 
 
@@ -175,3 +176,29 @@ def test_operator_scan_and_reduce_argument_errors():
     assert L.reduce_op_u32(NULLP, 0, 1, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
     with pytest.raises(ValueError):
         ps._op("sum")
+
+
+def test_u64_scan_and_reduce_argument_errors():
+    L = ps.lib()
+    big = 1 << 20
+    NOHOST64 = ctypes.POINTER(ctypes.c_uint64)()
+    for op in (-1, 7):
+        assert L.scan_op_u64(FAKE, 16, op, 0, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+        assert L.reduce_op_u64(FAKE, 16, op, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+    assert L.scan_op_u64(FAKE, 16, 0, 2, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
+    assert L.scan_op_u64(NULLP, 16, 0, 0, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.reduce_op_u64(FAKE, 16, 5, NOHOST64, NULLP, NULLP, big, NULLP) == ps.ERR_NULL
+    # u64 arrays and totals need 8-byte alignment
+    assert L.scan_op_u64(ctypes.c_void_p(0x100004), 16, 0, 0, NOHOST64, NULLP, FAKE, big,
+                         NULLP) == ps.ERR_ALIGN
+    assert L.reduce_op_u64(FAKE, 16, 0, NOHOST64, ctypes.c_void_p(0x200004), FAKE, big,
+                           NULLP) == ps.ERR_ALIGN
+    assert L.scan_op_u64(FAKE, (1 << 36) + 1, 0, 0, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.scan_op_u64(FAKE, 1 << 24, 3, 1, NOHOST64, NULLP, FAKE,
+                         L.scan_op_u64_scratch_bytes(1 << 24) - 300, NULLP) == ps.ERR_SCRATCH
+    assert L.reduce_op_u64(FAKE, 16, 4, NOHOST64, NULLP, FAKE, 100, NULLP) == ps.ERR_SCRATCH
+    # two descriptor words per 16384-element tile
+    assert L.scan_op_u64_scratch_bytes(1 << 27) >= ((1 << 27) // 16384) * 16
+    assert L.reduce_scratch_bytes(1) >= 4096 * 8
+    assert L.scan_op_u64(NULLP, 0, 6, 1, NOHOST64, NULLP, NULLP, 0, NULLP) == ps.OK
+    assert L.reduce_op_u64(NULLP, 0, 1, NOHOST64, NULLP, NULLP, 0, NULLP) == ps.OK

@@ -18,6 +18,7 @@ The workloads (sizes, value ranges, seeds):
   radix_uniform   n = 2^25 uniform u32 keys (seed 501)
   radix_distinct  n = 2^25 keys drawn from 256 distinct uniform u32 values
                   (seed 502)
+  scan_u64        n = 2^27 uniform u64 (seed 601): the byte size of scan_large
 """
 import numpy as np
 
@@ -30,6 +31,7 @@ SEED_COMPACT = {0.5: 301, 0.01: 302, 0.99: 303}
 SEED_SEGSCAN = 401
 SEED_RADIX_UNIFORM = 501
 SEED_RADIX_DISTINCT = 502
+SEED_SCAN_U64 = 601
 
 N_SCAN_SMALL = 1 << 16
 N_SCAN_MID = 1 << 24
@@ -38,6 +40,7 @@ N_COMPACT = 1 << 26
 N_SEGSCAN = 1 << 26
 SEG_LENS = (16, 1 << 20)
 N_RADIX = 1 << 25
+N_SCAN_U64 = 1 << 27
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -47,6 +50,11 @@ def rng(seed: int) -> np.random.Generator:
 def uniform_u32(n: int, seed: int) -> np.ndarray:
     """n values uniform over [0, 2^32)."""
     return rng(seed).integers(0, 1 << 32, size=n, dtype=np.uint32)
+
+
+def uniform_u64(n: int, seed: int) -> np.ndarray:
+    """n values uniform over [0, 2^64)."""
+    return rng(seed).integers(0, 1 << 64, size=n, dtype=np.uint64)
 
 
 def ones_u32(n: int) -> np.ndarray:
