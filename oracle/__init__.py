@@ -38,6 +38,14 @@ def load():
     lib.oracle_scan_op_u64.restype = ctypes.c_uint64
     lib.oracle_reduce_op_u64.argtypes = [u64p, ctypes.c_uint64, ctypes.c_int]
     lib.oracle_reduce_op_u64.restype = ctypes.c_uint64
+    lib.oracle_runs_u32.argtypes = [u32p, u32p, ctypes.c_uint64]
+    lib.oracle_runs_u32.restype = ctypes.c_uint32
+    lib.oracle_runs_slots.argtypes = [i32p, ctypes.c_uint64]
+    lib.oracle_runs_slots.restype = None
+    lib.oracle_runs_owner_all.argtypes = [u32p, ctypes.c_uint64, i32p, ctypes.c_uint64]
+    lib.oracle_runs_owner_all.restype = ctypes.c_int
+    lib.oracle_runs_owner.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_runs_owner.restype = ctypes.c_int32
     lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
     lib.oracle_scan_blocked_u32.restype = ctypes.c_int
     lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
@@ -178,3 +186,42 @@ def radix_perm_u32(keys, bits_per_pass=1):
     if rc != 0:
         raise ValueError("bits_per_pass must be 1 or 4 and n below 2^31")
     return perm
+
+
+def runs_u32(counts):
+    """O5: (ends, entries) -- inclusive prefix sum of the u32 counts (mod 2^32)
+    and max(total, 1)."""
+    c = _u32(counts)
+    ends = np.empty_like(c)
+    entries = load().oracle_runs_u32(_ptr(c, ctypes.c_uint32), _ptr(ends, ctypes.c_uint32), c.size)
+    return ends, int(entries)
+
+
+def runs_slots(entries):
+    """O5: the row of `entries` slots, every one -1."""
+    out = np.zeros(entries, dtype=np.int32)
+    load().oracle_runs_slots(_ptr(out, ctypes.c_int32), entries)
+    return out
+
+
+def runs_owner_all(counts):
+    """O5: every entry's owner, owner i emitting counts[i] entries in order."""
+    c = _u32(counts)
+    total = int(c.sum(dtype=np.uint64))
+    out = np.empty(total, dtype=np.int32)
+    if load().oracle_runs_owner_all(_ptr(c, ctypes.c_uint32), c.size, _ptr(out, ctypes.c_int32),
+                                    total) != 0:
+        raise ValueError("counts do not sum to their total")
+    return out
+
+
+def runs_owner(ends, e):
+    """O5: owner(e, ends) -- the least i with ends[i] > e, else -1; e may be
+    an int or an array of u32 queries."""
+    ends = _u32(ends)
+    L = load()
+    if np.isscalar(e):
+        return int(L.oracle_runs_owner(_ptr(ends, ctypes.c_uint32), ends.size, int(e)))
+    q = np.asarray(e, dtype=np.uint32)
+    return np.array([L.oracle_runs_owner(_ptr(ends, ctypes.c_uint32), ends.size, int(x))
+                     for x in q.tolist()], dtype=np.int32)

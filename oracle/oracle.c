@@ -24,8 +24,9 @@
  *           regularSegmentedRedomap (Large / Small), regularSegmentedScan.
  *   [ent]   entelechy docs, package "parallel": kernel table rows
  *           compact_blank, compact_offsets, compact_gather, compact_total,
- *           sort_identity, sort_zeros, sort_place, sort_next_bit, and the
- *           interface rows compact, sort, sort_pass.
+ *           sort_identity, sort_zeros, sort_place, sort_next_bit,
+ *           runs_ends, runs_entries, runs_slots, the function owner, and the
+ *           interface rows compact, sort, sort_pass, runs.
  *
  * Parity status: every function here is pinned by CPU tests against values
  * and properties fixed outside this file (worked examples printed on the
@@ -490,4 +491,69 @@ int oracle_radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int b
     free(next);
     free(zeros);
     return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O5 -- runs: entries laid out by owner.                                     */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [ent] runs_ends: where each owner's run ends -- an inclusive prefix sum of
+ * the counts, so owner i's run is [ends[i] - counts[i], ends[i]).
+ * [ent] runs_entries: how many entries the runs hold, at least one, so the
+ * row they are laid in is never empty.
+ * Readings: counts are unsigned 32-bit and the sums wrap at 2^32 as the scan's
+ * do; for n == 0 the runs hold nothing and entries is 1.
+ * Writes ends[0..n) and returns entries = max(ends[n-1], 1).
+ */
+uint32_t oracle_runs_u32(const uint32_t *counts, uint32_t *ends, uint64_t n)
+{
+    uint32_t running = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        running += counts[i];
+        ends[i] = running;
+    }
+    return running > 1u ? running : 1u;
+}
+
+/* [ent] runs_slots: the row the runs are laid in, every slot -1. */
+void oracle_runs_slots(int32_t *slots, uint64_t entries)
+{
+    for (uint64_t k = 0; k < entries; ++k)
+        slots[k] = -1;
+}
+
+/*
+ * Every entry's owner, by the scatter [ent] "runs" describes: a walk over
+ * the owners in order in which owner i emits its counts[i] entries at
+ * ends[i] - counts[i] plus their rank.  `owner` has room for `total` entries
+ * (the sum of the counts, which must not wrap); returns 0, or -1 if the
+ * counts do not sum to `total`.
+ */
+int oracle_runs_owner_all(const uint32_t *counts, uint64_t n, int32_t *owner, uint64_t total)
+{
+    uint64_t at = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        for (uint32_t r = 0; r < counts[i]; ++r) {
+            if (at >= total)
+                return -1;
+            owner[at++] = (int32_t)i;
+        }
+    }
+    return at == total ? 0 : -1;
+}
+
+/*
+ * [ent] owner(e, ends): the owner whose run holds entry e -- the least i
+ * with ends[i] > e, since runs [ends[i] - counts[i], ends[i]) follow one
+ * another in order and an empty run holds nothing.  Reading: an entry no
+ * run holds (e >= ends[n-1]) has owner -1, the page's "nothing" value.
+ * Walks the ends one by one (no search).
+ */
+int32_t oracle_runs_owner(const uint32_t *ends, uint64_t n, uint32_t e)
+{
+    for (uint64_t i = 0; i < n; ++i)
+        if (ends[i] > e)
+            return (int32_t)i;
+    return -1;
 }

@@ -533,3 +533,77 @@ def test_op64_agrees_with_u32_below_2_32(op):
     assert t64 % M == t32
     assert oracle.scan_op_u64(np.zeros(0, dtype=np.uint64), op)[1] == OP_IDENTITY64[op]
     assert oracle.reduce_op_u64(np.zeros(0, dtype=np.uint64), op) == OP_IDENTITY64[op]
+
+
+# ---------------------------------------------------------------------------
+# O5 -- runs (entelechy "parallel": runs_ends, runs_entries, runs_slots, owner)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gen,n", [("uniform", 1000), ("sparse", 5000), ("uniform", 65537)])
+def test_runs_ends_and_entries_match_numpy(gen, n):
+    c = getattr(workloads, "runs_counts_" + gen)(n)
+    ends, entries = oracle.runs_u32(c)
+    assert np.array_equal(ends, np.cumsum(c, dtype=np.uint32))
+    assert entries == max(int(c.sum()), 1)
+    # owner i's run is [ends[i] - counts[i], ends[i])
+    assert np.array_equal(ends - c, np.concatenate([[0], ends[:-1]]).astype(np.uint32))
+
+
+def test_runs_entries_at_least_one_and_slots():
+    for c in (np.zeros(0, dtype=np.uint32), np.zeros(17, dtype=np.uint32)):
+        ends, entries = oracle.runs_u32(c)
+        assert entries == 1 and ends.size == c.size and not ends.any()
+    assert oracle.runs_slots(1).tolist() == [-1]
+    s = oracle.runs_slots(1000)
+    assert s.dtype == np.int32 and (s == -1).all()
+
+
+@pytest.mark.parametrize("gen,n", [("uniform", 3000), ("sparse", 20000)])
+def test_runs_owner_all_matches_numpy_repeat(gen, n):
+    c = getattr(workloads, "runs_counts_" + gen)(n)
+    own = oracle.runs_owner_all(c)
+    assert np.array_equal(own, np.repeat(np.arange(n, dtype=np.int32), c))
+
+
+@pytest.mark.parametrize("gen,n", [("uniform", 700), ("sparse", 3000)])
+def test_runs_owner_matches_searchsorted_and_run_bounds(gen, n):
+    c = getattr(workloads, "runs_counts_" + gen)(n)
+    ends, _ = oracle.runs_u32(c)
+    total = int(ends[-1])
+    e = np.arange(total + 5, dtype=np.uint32)
+    got = oracle.runs_owner(ends, e)
+    want = np.searchsorted(ends, e, side="right").astype(np.int64)
+    want[e >= total] = -1
+    assert np.array_equal(got, want)
+    assert np.array_equal(got[:total], oracle.runs_owner_all(c))
+    for i in np.flatnonzero(c)[:200]:
+        assert oracle.runs_owner(ends, int(ends[i] - c[i])) == i
+        assert oracle.runs_owner(ends, int(ends[i] - 1)) == i
+
+
+def test_runs_brute_force_tiny():
+    # Every count vector of length <= 4 over {0, 1, 2}: the owner of each
+    # entry by listing the runs with Python loops.
+    for n in range(0, 5):
+        for c in itertools.product(range(3), repeat=n):
+            c = np.array(c, dtype=np.uint32)
+            listed = [i for i in range(n) for _ in range(int(c[i]))]
+            ends, entries = oracle.runs_u32(c)
+            assert entries == max(len(listed), 1)
+            assert oracle.runs_owner_all(c).tolist() == listed
+            for e in range(len(listed) + 2):
+                want = listed[e] if e < len(listed) else -1
+                assert oracle.runs_owner(ends, e) == want
+
+
+def test_runs_special_cases():
+    n = 1000
+    ends, entries = oracle.runs_u32(np.ones(n, dtype=np.uint32))
+    assert ends.tolist() == list(range(1, n + 1)) and entries == n
+    assert oracle.runs_owner(ends, np.arange(n + 1)).tolist() == list(range(n)) + [-1]
+    one = np.array([9], dtype=np.uint32)
+    ends, _ = oracle.runs_u32(one)
+    assert oracle.runs_owner(ends, np.arange(11)).tolist() == [0] * 9 + [-1, -1]
+    # the sums wrap at 2^32 as the scan's do
+    ends, entries = oracle.runs_u32(np.full(3, 0xFFFFFFFF, dtype=np.uint32))
+    assert ends.tolist() == [0xFFFFFFFF, 0xFFFFFFFE, 0xFFFFFFFD] and entries == 0xFFFFFFFD

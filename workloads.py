@@ -19,6 +19,10 @@ The workloads (sizes, value ranges, seeds):
   radix_distinct  n = 2^25 keys drawn from 256 distinct uniform u32 values
                   (seed 502)
   scan_u64        n = 2^27 uniform u64 (seed 601): the byte size of scan_large
+  runs_uniform    n = 2^24 owners, entry counts uniform over [0, 8) (seed 701):
+                  about 5.9e7 entries, one owner in eight empty
+  runs_sparse     n = 2^24 owners, nine in ten empty, the rest uniform over
+                  [1, 64) (seed 702): long stretches of empty runs
 """
 import numpy as np
 
@@ -32,6 +36,8 @@ SEED_SEGSCAN = 401
 SEED_RADIX_UNIFORM = 501
 SEED_RADIX_DISTINCT = 502
 SEED_SCAN_U64 = 601
+SEED_RUNS_UNIFORM = 701
+SEED_RUNS_SPARSE = 702
 
 N_SCAN_SMALL = 1 << 16
 N_SCAN_MID = 1 << 24
@@ -41,6 +47,7 @@ N_SEGSCAN = 1 << 26
 SEG_LENS = (16, 1 << 20)
 N_RADIX = 1 << 25
 N_SCAN_U64 = 1 << 27
+N_RUNS = 1 << 24
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -102,3 +109,16 @@ def radix_keys_distinct(n: int = N_RADIX, distinct: int = 256,
 def small_random_u32(n: int, seed: int, high: int = 1 << 32) -> np.ndarray:
     """Generic seeded u32 array for the small parity cases."""
     return rng(seed).integers(0, high, size=n, dtype=np.uint32)
+
+
+def runs_counts_uniform(n: int = N_RUNS, seed: int = SEED_RUNS_UNIFORM) -> np.ndarray:
+    """Per-owner entry counts, uniform over [0, 8)."""
+    return rng(seed).integers(0, 8, size=n, dtype=np.uint32)
+
+
+def runs_counts_sparse(n: int = N_RUNS, seed: int = SEED_RUNS_SPARSE) -> np.ndarray:
+    """Per-owner entry counts: 0 with probability 0.9, else uniform over [1, 64)."""
+    g = rng(seed)
+    c = g.integers(1, 64, size=n, dtype=np.uint32)
+    c[g.random(n) < 0.9] = 0
+    return c
