@@ -224,6 +224,30 @@ def suite(args, torch, ps):
         row("segscan L=%d n=2^26" % L, v.numel(), 8 + 4.0 / L,
             lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums))
     del v, o
+    # Runs laid out by owner: the ends (8 B per owner), the -1 slots (4 B per
+    # entry), every entry's owner (4 B per owner + 4 B per entry), and owner
+    # queries (one binary search each; counted per query).
+    for kind, gen in (("uniform", workloads.runs_counts_uniform),
+                      ("sparse", workloads.runs_counts_sparse)):
+        c = torch.from_numpy(gen().view(np.int32)).to("cuda")
+        ends = torch.empty_like(c)
+        _, entries = ps.runs_layout_u32(c, ends=ends)
+        total = int(ends[-1].item())
+        row("runs ends %s n=2^24" % kind, c.numel(), 8,
+            lambda: ps.runs_layout_u32(c, ends=ends, want_entries=False))
+        own = torch.empty(total, dtype=torch.int32, device="cuda")
+        row("runs owner_all %s n=2^24 entries=%d" % (kind, total), c.numel() + total, 4,
+            lambda: ps.runs_owner_all_u32(ends, total, owner=own))
+        if kind == "uniform":
+            slots = torch.empty(entries, dtype=torch.int32, device="cuda")
+            row("runs slots entries=%d" % entries, entries, 4, lambda: ps.runs_slots_i32(slots))
+            q = torch.from_numpy(workloads.rng(703).integers(0, total, 1 << 24, dtype=np.uint32)
+                                 .view(np.int32)).to("cuda")
+            qo = torch.empty_like(q)
+            row("runs owner queries m=2^24", q.numel(), 8,
+                lambda: ps.runs_owner_u32(ends, q, owner=qo))
+            del slots, q, qo
+        del c, ends, own
     for kind, gen in (("uniform", workloads.radix_keys_uniform), ("256 distinct", workloads.radix_keys_distinct)):
         k = torch.from_numpy(gen().view(np.int32)).to("cuda")
         perm = torch.empty_like(k)
@@ -254,7 +278,8 @@ PROFILE_COMMANDS = [
 def algorithmic_bytes(name, grid):
     """Bytes a dispatch must move at the sizes of the --hbm-rows suite (scans
     and copy at 2^28, u64 scan and reduction at 2^27, compaction and segmented
-    scan at 2^26, radix at 2^25), or None for bookkeeping kernels."""
+    scan at 2^26, radix at 2^25, runs at 2^24 owners), or None for bookkeeping
+    kernels."""
     big = grid >= (1 << 16)            # threads: a data pass, not a table scan
     n28, n27, n26, n25 = 1 << 28, 1 << 27, 1 << 26, 1 << 25
     table = [
@@ -264,12 +289,17 @@ def algorithmic_bytes(name, grid):
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
         ("digit_hist_kernel", 4 * n25), ("reduce_partial_kernel", 4 * n28),
         ("scan64_pipelined_kernel", 16 * n27), ("reduce64_partial_kernel", 8 * n27),
+        ("runs_ends_kernel", 8 * (1 << 24)),
     ]
     for key, b in table:
         if "::" + key + "<" in name:
             return b
     if "scan_lookback_kernel" in name or "scan_blocks_kernel" in name:
         return 8 * n28 if big else None
+    if "runs_owner_all_kernel" in name:
+        # 4 B per merged item (run end or entry), 4096 items per 256-thread
+        # workgroup: within 16 KiB of 4 (n + total).
+        return 64 * grid
     if "radix1_pass_kernel" in name or "digit_scatter_kernel" in name:
         first = ", true, false>" in name
         last = ", false, true>" in name

@@ -214,6 +214,45 @@ int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host
                   uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Runs: entries laid out by owner                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * entelechy "parallel" package, kernels runs_ends, runs_entries, runs_slots
+ * and the function owner (interface "runs").  From each owner's count of
+ * entries: where each owner's run ends, an inclusive prefix sum of the
+ * counts, so owner i's run is [ends[i] - counts[i], ends[i]); how many
+ * entries the runs hold, at least one so the row they are laid in is never
+ * empty; that row, every slot -1; and the owner of an entry.
+ *
+ * runs_layout_u32: ends[i] = counts[0] + .. + counts[i] (mod 2^32, as the
+ *   scan) for n u32 counts into a separate array `ends` (or ends == counts,
+ *   in place); entries = max(ends[n-1], 1) (1 for n == 0) to *entries_host
+ *   (the call then waits) and/or *entries_dev (4-byte aligned device u32).
+ *   Scratch: runs_scratch_bytes(n, 0).  Errors as for scan_exclusive_u32.
+ * runs_slots_i32: slots[0 .. entries) = -1 (int32, device).
+ * runs_owner_u32: owner[j] = owner(entry[j], ends), the least i with
+ *   ends[i] > entry[j], or -1 when no run holds the entry (entry[j] >=
+ *   ends[n-1], or n == 0), for m u32 queries.  ends must be non-decreasing
+ *   (counts whose sum stays below 2^32); otherwise the owners are
+ *   unspecified (the call still touches only its arrays).  n <= 2^31 - 1.
+ * runs_owner_all_u32: owner[e] = owner(e, ends) for every entry e in
+ *   [0, total), total <= 2^32 - 1 (normally ends[n-1]).  Scratch:
+ *   runs_scratch_bytes(n, total).  Same condition on ends.
+ * All arrays are device pointers the caller owns, 4-byte aligned, ordered
+ * on `stream`; errors as for the scans (LIBSCAN_ERR_SIZE beyond the limits
+ * above).
+ */
+size_t runs_scratch_bytes(uint64_t n, uint64_t total);
+int runs_layout_u32(const uint32_t *counts, uint32_t *ends, uint64_t n, uint32_t *entries_host,
+                    uint32_t *entries_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
+int runs_slots_i32(int32_t *slots, uint64_t entries, hipStream_t stream);
+int runs_owner_u32(const uint32_t *ends, uint64_t n, const uint32_t *entry, uint64_t m,
+                   int32_t *owner, hipStream_t stream);
+int runs_owner_all_u32(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Segmented scan and segment sums over regular segments                    */
 /* ------------------------------------------------------------------------ */
 

@@ -20,6 +20,7 @@ __all__ = [
     "LibscanError", "lib", "version",
     "scan_exclusive_u32", "scan_inclusive_u32", "scan_u32_ex",
     "scan_op_u32", "reduce_op_u32", "scan_op_u64", "reduce_op_u64",
+    "runs_layout_u32", "runs_slots_i32", "runs_owner_u32", "runs_owner_all_u32",
     "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
     "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
     "compact_scratch_bytes", "radix_scratch_bytes",
@@ -89,6 +90,16 @@ def lib():
         L.scan_op_u64.restype = i32
         L.reduce_op_u64.argtypes = [vp, u64, i32, u64p, vp, vp, sz, vp]
         L.reduce_op_u64.restype = i32
+        L.runs_scratch_bytes.argtypes = [u64, u64]
+        L.runs_scratch_bytes.restype = sz
+        L.runs_layout_u32.argtypes = [vp, vp, u64, u32p, vp, vp, sz, vp]
+        L.runs_layout_u32.restype = i32
+        L.runs_slots_i32.argtypes = [vp, u64, vp]
+        L.runs_slots_i32.restype = i32
+        L.runs_owner_u32.argtypes = [vp, u64, vp, u64, vp, vp]
+        L.runs_owner_u32.restype = i32
+        L.runs_owner_all_u32.argtypes = [vp, u64, vp, u64, vp, sz, vp]
+        L.runs_owner_all_u32.restype = i32
         L.segscan_scratch_bytes.argtypes = [u64, u64]
         L.segscan_scratch_bytes.restype = sz
         L.segscan_u32.argtypes = [vp, vp, u64, u64, vp, vp, sz, vp]
@@ -302,6 +313,65 @@ def scan_exclusive_u32(data, want_total=True, total_dev=None, stream=None):
 def scan_inclusive_u32(data, want_total=True, total_dev=None, stream=None):
     """data[j] <- data[0] + .. + data[j] in place (mod 2^32); returns the total."""
     return _scan("scan_inclusive_u32", data, want_total, total_dev, stream)
+
+
+def runs_layout_u32(counts, ends=None, want_entries=True, entries_dev=None, stream=None):
+    """ends <- inclusive prefix sum of the per-owner counts (pass ends=counts
+    for in place); returns (ends, entries) with entries = max(total, 1) as an
+    int when want_entries, else None (then see entries_dev)."""
+    _dev_u32(counts, "counts")
+    n = counts.numel()
+    if ends is None:
+        ends = torch.empty_like(counts)
+    _dev_u32(ends, "ends")
+    if ends.numel() != n:
+        raise ValueError("ends must have as many elements as counts")
+    sh, s = _stream_handle(counts.device, stream)
+    scr = _scratch_for(counts.device, s, lib().runs_scratch_bytes(n, 0))
+    host, hp = _total_args(want_entries, entries_dev)
+    _check(lib().runs_layout_u32(_ptr(counts), _ptr(ends), n, hp, _ptr(entries_dev), _ptr(scr),
+                                 scr.numel(), sh), "runs_layout_u32")
+    return ends, (int(host.value) if want_entries else None)
+
+
+def runs_slots_i32(slots, stream=None):
+    """Every slot of the int32 tensor `slots` set to -1 (the row the runs are
+    laid in); returns it."""
+    _dev_u32(slots, "slots")
+    sh, _ = _stream_handle(slots.device, stream)
+    _check(lib().runs_slots_i32(_ptr(slots), slots.numel(), sh), "runs_slots_i32")
+    return slots
+
+
+def runs_owner_u32(ends, entry, owner=None, stream=None):
+    """owner[j] = owner(entry[j], ends): the least i with ends[i] > entry[j],
+    or -1 when no run holds the entry."""
+    _dev_u32(ends, "ends")
+    _dev_u32(entry, "entry")
+    if owner is None:
+        owner = torch.empty(entry.numel(), dtype=torch.int32, device=entry.device)
+    _dev_u32(owner, "owner")
+    if owner.numel() != entry.numel():
+        raise ValueError("owner must have as many elements as entry")
+    sh, _ = _stream_handle(entry.device, stream)
+    _check(lib().runs_owner_u32(_ptr(ends), ends.numel(), _ptr(entry), entry.numel(), _ptr(owner),
+                                sh), "runs_owner_u32")
+    return owner
+
+
+def runs_owner_all_u32(ends, total, owner=None, stream=None):
+    """The owner of every entry 0 .. total-1 (an int32 tensor of `total`)."""
+    _dev_u32(ends, "ends")
+    if owner is None:
+        owner = torch.empty(total, dtype=torch.int32, device=ends.device)
+    _dev_u32(owner, "owner")
+    if owner.numel() != total:
+        raise ValueError("owner must have `total` elements")
+    sh, s = _stream_handle(ends.device, stream)
+    scr = _scratch_for(ends.device, s, lib().runs_scratch_bytes(ends.numel(), total))
+    _check(lib().runs_owner_all_u32(_ptr(ends), ends.numel(), _ptr(owner), total, _ptr(scr),
+                                    scr.numel(), sh), "runs_owner_all_u32")
+    return owner
 
 
 def segscan_scratch_bytes(n, seg_len):

@@ -95,6 +95,17 @@ hipError_t launch_reduce_op64(const uint64_t *data, uint64_t n, int op, const Sc
 size_t reduce64_body_bytes();
 hipError_t launch_fill_u64(uint64_t *p, uint64_t value, hipStream_t stream);
 
+// ---- runs laid out by owner (runs_kernels.hip) ----
+hipError_t launch_runs_ends(const uint32_t *counts, uint32_t *ends, uint64_t n, const Scratch &s,
+                            uint32_t *entries_out, hipStream_t stream);
+size_t runs_body_bytes(uint64_t n);
+hipError_t launch_fill_value(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream);
+hipError_t launch_runs_owner(const uint32_t *ends, uint64_t n, const uint32_t *query, uint64_t m,
+                             int32_t *owner, hipStream_t stream);
+hipError_t launch_runs_owner_all(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
+                                 const Scratch &s, hipStream_t stream);
+uint64_t runs_owner_all_parts(uint64_t n, uint64_t total);
+
 // ---- segmented scan (segscan_kernels.hip) ----
 hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
                           uint32_t *seg_sums, const Scratch &s, hipStream_t stream);

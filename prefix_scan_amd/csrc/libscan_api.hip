@@ -452,6 +452,95 @@ int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host
     return LIBSCAN_OK;
 }
 
+size_t runs_scratch_bytes(uint64_t n, uint64_t total)
+{
+    const size_t a = runs_body_bytes(n);
+    const size_t b = (size_t)(runs_owner_all_parts(n, total) + 1) * sizeof(uint32_t);
+    return with_header(a > b ? a : b);
+}
+
+int runs_layout_u32(const uint32_t *counts, uint32_t *ends, uint64_t n, uint32_t *entries_host,
+                    uint32_t *entries_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (n > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(counts) || misaligned4(ends) || misaligned4(entries_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value(entries_host, entries_dev, 1u, stream);
+    if (!counts || !ends || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, runs_body_bytes(n), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *ent = entries_dev ? entries_dev : s.total_slot();
+    hipError_t e = prepare_state(s, kKindDesc, 0, runs_body_bytes(n), 1, stream);
+    if (e == hipSuccess)
+        e = launch_runs_ends(counts, ends, n, s, ent, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (entries_host)
+        return read_back(entries_host, ent, stream);
+    return LIBSCAN_OK;
+}
+
+int runs_slots_i32(int32_t *slots, uint64_t entries, hipStream_t stream)
+{
+    if (entries > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(slots))
+        return LIBSCAN_ERR_ALIGN;
+    if (entries == 0)
+        return LIBSCAN_OK;
+    if (!slots)
+        return LIBSCAN_ERR_NULL;
+    return hip_status(launch_fill_value(reinterpret_cast<uint32_t *>(slots), entries, 0xFFFFFFFFu,
+                                        stream));
+}
+
+int runs_owner_u32(const uint32_t *ends, uint64_t n, const uint32_t *entry, uint64_t m,
+                   int32_t *owner, hipStream_t stream)
+{
+    if (n > LIBSCAN_MAX_N_INDEX || m > LIBSCAN_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(ends) || misaligned4(entry) || misaligned4(owner))
+        return LIBSCAN_ERR_ALIGN;
+    if (m == 0)
+        return LIBSCAN_OK;
+    if (!entry || !owner || (n != 0 && !ends))
+        return LIBSCAN_ERR_NULL;
+    if (n == 0)       // no run holds anything
+        return hip_status(launch_fill_value(reinterpret_cast<uint32_t *>(owner), m, 0xFFFFFFFFu,
+                                            stream));
+    return hip_status(launch_runs_owner(ends, n, entry, m, owner, stream));
+}
+
+int runs_owner_all_u32(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
+                       void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (n > LIBSCAN_MAX_N_INDEX || total > 0xFFFFFFFFull)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(ends) || misaligned4(owner))
+        return LIBSCAN_ERR_ALIGN;
+    if (total == 0)
+        return LIBSCAN_OK;
+    if (!owner || (n != 0 && !ends))
+        return LIBSCAN_ERR_NULL;
+    if (n == 0)
+        return hip_status(launch_fill_value(reinterpret_cast<uint32_t *>(owner), total, 0xFFFFFFFFu,
+                                            stream));
+    if (!scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    const size_t body = (size_t)(runs_owner_all_parts(n, total) + 1) * sizeof(uint32_t);
+    if (!carve(scratch, scratch_bytes, body, &s))
+        return LIBSCAN_ERR_SCRATCH;
+    hipError_t e = prepare_state(s, kKindData, 0, 0, 0, stream);
+    if (e == hipSuccess)
+        e = launch_runs_owner_all(ends, n, owner, total, s, stream);
+    return hip_status(e);
+}
+
 size_t segscan_scratch_bytes(uint64_t n, uint64_t seg_len)
 {
     return with_header(segscan_body_bytes(n, seg_len));

@@ -1,0 +1,299 @@
+// runs_kernels.hip -- entries laid out in runs by owner, on gfx950.
+//
+// entelechy "parallel" package, kernels runs_ends, runs_entries, runs_slots
+// and the function owner (interface "runs"): from each owner's count of
+// entries, where each owner's run ends (an inclusive prefix sum of the
+// counts, so owner i's run is [ends[i] - counts[i], ends[i])), how many
+// entries there are (at least one), the row of -1 they are laid in, and the
+// owner of an entry.
+//
+//  * runs_ends_kernel: the out-of-place inclusive scan of the counts on the
+//    pipelined chained-carry driver (scan_op.hpp); its last tile writes
+//    entries = max(total, 1).  8 bytes per owner.
+//  * fill_value_kernel: the slots, -1 with 16-byte stores.  4 bytes per slot.
+//  * runs_owner_kernel: owner(e, ends) for a batch of entries, a binary
+//    search over the ends per query.
+//  * runs_partition_kernel + runs_owner_all_kernel: the owner of every entry
+//    0 .. total-1.  The ends and the entries are merged as two sorted lists
+//    (the end of run i comes before entry e when ends[i] <= e), so an entry's
+//    owner is the number of run ends before it.  Each workgroup takes an
+//    equal share of the merged items -- run ends and entries together -- so
+//    long stretches of empty runs cost as much as entries, never more: the
+//    ends are read once (4 bytes per owner) and each owner written once (4
+//    bytes per entry), staged in LDS and stored in order.
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "pipeline.hpp"
+#include "scan_op.hpp"
+
+namespace libscan {
+
+// ---------------------------------------------------------------------------
+// ends: inclusive scan of the counts into another array.
+// ---------------------------------------------------------------------------
+template <int BLOCK_, int V, bool VEC_OUT>
+struct RunsEndsOp : ScanOp<BLOCK_, V, true, OpAdd> {
+    using Base = ScanOp<BLOCK_, V, true, OpAdd>;
+    using Regs = typename Base::Regs;
+    using Cells = typename Base::Cells;
+    using TS = typename Base::TS;
+    static constexpr int BLOCK = BLOCK_;
+
+    uint32_t *obase;        // the ends, addressed with the counts' virtual index
+    uint32_t *entries_out;  // max(total, 1)
+
+    __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const
+    {
+        const uint32_t total = carry + in.value;
+        *entries_out = total > 1u ? total : 1u;
+    }
+
+    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
+    {
+        uint32_t w[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            w[k] = wave_incl_add(r.x[k].w);
+        TS::template apply<true>(r.x, w, c.c, carry);
+        const uint64_t vstart = (uint64_t)t * Base::T;
+        if constexpr (VEC_OUT) {
+            if (this->whole(t))
+                store_tile_full<BLOCK, V>(obase, vstart, r.x);
+            else
+                store_tile<BLOCK, V>(obase, vstart, this->vlo, this->vhi, r.x);
+        } else {
+            // The ends sit at another 16-byte phase than the counts.
+            const uint64_t q0 = vstart / 4 + threadIdx.x;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint64_t v0 = (q0 + (uint64_t)k * BLOCK) * 4;
+                const uint32_t vals[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (v0 + j >= this->vlo && v0 + j < this->vhi)
+                        obase[v0 + j] = vals[j];
+            }
+        }
+    }
+};
+
+template <int BLOCK, int V, bool VEC_OUT>
+__global__ __launch_bounds__(BLOCK) void runs_ends_kernel(const uint32_t *ibase, uint32_t *obase,
+                                                          uint64_t vlo, uint64_t vhi,
+                                                          uint32_t ntiles, uint64_t *ticket,
+                                                          uint32_t *exits, uint64_t *desc,
+                                                          uint32_t *entries_out)
+{
+    RunsEndsOp<BLOCK, V, VEC_OUT> op{{const_cast<uint32_t *>(ibase), vlo, vhi, nullptr}, obase,
+                                     entries_out};
+    pipelined_chain(op, ntiles, ticket, exits, desc);
+}
+
+constexpr int kRunsBlock = 512;
+constexpr int kRunsChunks = 16;
+constexpr uint64_t kRunsTile = (uint64_t)kRunsBlock * kRunsChunks * 4;
+
+size_t runs_body_bytes(uint64_t n)
+{
+    return round_up((size_t)tiles_for(n, 3, kRunsTile) * sizeof(uint64_t), 256);
+}
+
+hipError_t launch_runs_ends(const uint32_t *counts, uint32_t *ends, uint64_t n, const Scratch &s,
+                            uint32_t *entries_out, hipStream_t stream)
+{
+    const uint32_t head = head_of(counts);
+    const uint64_t ntiles = tiles_for(n, head, kRunsTile);
+    const bool vec_out = head_of(ends) == head;
+    auto kern = vec_out ? runs_ends_kernel<kRunsBlock, kRunsChunks, true>
+                        : runs_ends_kernel<kRunsBlock, kRunsChunks, false>;
+    uint64_t grid = (uint64_t)resident_grid((const void *)kern, kRunsBlock);
+    if (grid > ntiles)
+        grid = ntiles;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kRunsBlock), 0, stream, counts - head,
+                       ends - head, (uint64_t)head, n + head, (uint32_t)ntiles, s.ticket(),
+                       s.exits(), s.desc(), entries_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// slots: every element of a u32 array set to one value.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_value_kernel(uint32_t *vbase, uint64_t vlo,
+                                                         uint64_t vhi, uint32_t value)
+{
+    const u32x4 v4 = {value, value, value, value};
+    const uint64_t q_hi = (vhi + 3) / 4;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t q = vlo / 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; q < q_hi;
+         q += stride) {
+        const uint64_t v0 = q * 4;
+        if (v0 >= vlo && v0 + 4 <= vhi) {
+            store4(vbase, q, v4);
+        } else {
+            for (int j = 0; j < 4; ++j)
+                if (v0 + j >= vlo && v0 + j < vhi)
+                    vbase[v0 + j] = value;
+        }
+    }
+}
+
+hipError_t launch_fill_value(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream)
+{
+    const uint32_t head = head_of(p);
+    const uint64_t chunks = (n + head + 3) / 4;
+    uint64_t grid = (chunks + 255) / 256;
+    if (grid > 8192)
+        grid = 8192;
+    hipLaunchKernelGGL(fill_value_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p - head,
+                       (uint64_t)head, n + head, value);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// owner(e, ends) for a batch of entries.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void runs_owner_kernel(const uint32_t *__restrict__ ends,
+                                                         uint32_t n,
+                                                         const uint32_t *__restrict__ query,
+                                                         uint64_t m, int32_t *__restrict__ owner)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < m; j += stride) {
+        const uint32_t e = query[j];
+        uint32_t lo = 0, hi = n;               // the least i with ends[i] > e
+        while (lo < hi) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            if (ends[mid] > e)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        owner[j] = lo < n ? (int32_t)lo : -1;
+    }
+}
+
+hipError_t launch_runs_owner(const uint32_t *ends, uint64_t n, const uint32_t *query, uint64_t m,
+                             int32_t *owner, hipStream_t stream)
+{
+    uint64_t grid = (m + 255) / 256;
+    if (grid > 8192)
+        grid = 8192;
+    hipLaunchKernelGGL(runs_owner_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, ends,
+                       (uint32_t)n, query, m, owner);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The owner of every entry: merge path over (run ends, entries).
+//
+// The merged list puts the end of run i before entry e when ends[i] <= e;
+// with `total` entries an end past total counts as total.  Before the end of
+// run i come i earlier ends and min(ends[i], total) entries, so among the
+// first d merged items there are i ends for the largest i with
+// min(ends[i-1], total) + i <= d (i = 0 always qualifies).  An entry e met
+// after i ends has owner i (or -1 once every run has ended).
+// ---------------------------------------------------------------------------
+constexpr int kMpBlock = 256;
+constexpr int kMpItems = 16;
+constexpr uint64_t kMpTile = (uint64_t)kMpBlock * kMpItems;    // merged items per workgroup
+
+__device__ __forceinline__ uint64_t merge_split(const uint32_t *ends, uint64_t n, uint64_t total,
+                                                uint64_t d)
+{
+    uint64_t lo = d > total ? d - total : 0;
+    uint64_t hi = d < n ? d : n;
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi + 1) / 2;
+        const uint64_t em = ends[mid - 1];
+        if ((em < total ? em : total) + mid <= d)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void runs_partition_kernel(const uint32_t *__restrict__ ends,
+                                                             uint64_t n, uint64_t total,
+                                                             uint64_t nparts,
+                                                             uint32_t *__restrict__ splits)
+{
+    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b > nparts)
+        return;
+    const uint64_t d = b * kMpTile < n + total ? b * kMpTile : n + total;
+    splits[b] = (uint32_t)merge_split(ends, n, total, d);
+}
+
+__global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
+    const uint32_t *__restrict__ ends, uint64_t n, uint64_t total,
+    const uint32_t *__restrict__ splits, int32_t *__restrict__ owner)
+{
+    // The workgroup's run ends at [0, ni), its owners from ni: together
+    // exactly its merged items, at most kMpTile.
+    __shared__ uint32_t s_buf[kMpTile];
+    const uint64_t b = blockIdx.x;
+    const uint64_t d0 = b * kMpTile;
+    const uint64_t d1 = d0 + kMpTile < n + total ? d0 + kMpTile : n + total;
+    const uint64_t i0 = splits[b];
+    uint64_t i1 = splits[b + 1];
+    // Non-decreasing ends give i0 <= i1 <= i0 + (d1 - d0).  Ends that are not
+    // (sums that wrapped) have no defined owners; the clamp keeps every
+    // access inside the workgroup's share even then.
+    if (i1 < i0 || i1 - i0 > d1 - d0)
+        i1 = i0;
+    const uint64_t e0 = d0 - i0, e1 = d1 - i1;
+    const uint32_t ni = (uint32_t)(i1 - i0);
+    const uint32_t ne = (uint32_t)(e1 - e0);
+    for (uint32_t j = threadIdx.x; j < ni; j += kMpBlock)
+        s_buf[j] = ends[i0 + j];
+    __syncthreads();
+    const uint64_t da = d0 + (uint64_t)threadIdx.x * kMpItems;
+    if (da < d1) {
+        // This thread's split inside the workgroup's share.
+        uint64_t lo = da > e1 + i0 ? da - e1 : i0;
+        uint64_t hi = da - e0 < i1 ? da - e0 : i1;
+        while (lo < hi) {
+            const uint64_t mid = (lo + hi + 1) / 2;
+            const uint64_t em = s_buf[mid - 1 - i0];
+            if ((em < total ? em : total) + mid <= da)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        uint64_t i = lo, e = da - lo;
+        const uint64_t db = da + kMpItems < d1 ? da + kMpItems : d1;
+        for (uint64_t d = da; d < db; ++d) {
+            if (i < i1 && (s_buf[i - i0] <= e || e >= total)) {
+                ++i;                                // run i ended at or before entry e
+            } else {
+                if (e - e0 < ne)
+                    s_buf[ni + (e - e0)] = i < n ? (uint32_t)i : 0xFFFFFFFFu;
+                ++e;
+            }
+        }
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < ne && e0 + j < total; j += kMpBlock)
+        owner[e0 + j] = (int32_t)s_buf[ni + j];
+}
+
+uint64_t runs_owner_all_parts(uint64_t n, uint64_t total)
+{
+    return (n + total + kMpTile - 1) / kMpTile;
+}
+
+hipError_t launch_runs_owner_all(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
+                                 const Scratch &s, hipStream_t stream)
+{
+    const uint64_t nparts = runs_owner_all_parts(n, total);
+    uint32_t *splits = reinterpret_cast<uint32_t *>(s.body());
+    const uint64_t pgrid = (nparts + 1 + 255) / 256;
+    hipLaunchKernelGGL(runs_partition_kernel, dim3((uint32_t)pgrid), dim3(256), 0, stream, ends, n,
+                       total, nparts, splits);
+    hipLaunchKernelGGL(runs_owner_all_kernel, dim3((uint32_t)nparts), dim3(kMpBlock), 0, stream,
+                       ends, n, total, splits, owner);
+    return hipGetLastError();
+}
+
+}  // namespace libscan

@@ -17,6 +17,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
+#include "scan_op.hpp"
 
 #include <stdlib.h>
 
@@ -80,89 +81,6 @@ __global__ __launch_bounds__(BLOCK) void scan_lookback_kernel(uint32_t *__restri
     TS::template apply<INCL>(x, w, s_cell, s_carry);
     store_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
 }
-
-// ---------------------------------------------------------------------------
-// Pipelined variant of the same single-pass scan: a grid that fills the GPU
-// once, two tiles per workgroup, a tile's carry folded only after the next
-// tile is loaded and its aggregate published (pipeline.hpp).
-// ---------------------------------------------------------------------------
-template <int BLOCK_, int V, bool INCL, class M = OpAdd>
-struct ScanOp {
-    static constexpr int BLOCK = BLOCK_;
-    static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    using Monoid = M;
-    using TS = TileScan<BLOCK, V, M>;
-    // The wave prefix of the chunk sums is not held across the step: finish
-    // rebuilds it from the chunk totals (one DPP scan per chunk run), which
-    // frees V registers per tile.
-    struct Regs {
-        u32x4 x[V];
-    };
-    struct Cells {
-        uint32_t c[TS::NCELL];
-    };
-
-    uint32_t *abase;
-    uint64_t vlo, vhi;
-    uint32_t *total_out;
-
-    __device__ __forceinline__ bool whole(uint32_t t) const
-    {
-        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
-    }
-
-    __device__ __forceinline__ void load(Regs &r, uint32_t t) const
-    {
-        if (whole(t))
-            load_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
-        else
-            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
-    }
-
-    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
-    {
-        if constexpr (M::identity != 0u) {
-            // The guarded loads read slots outside the array as 0; under an
-            // operator whose identity is not 0 they must hold the identity.
-            if (!whole(t)) {
-                const uint64_t vs = (uint64_t)t * T;
-#pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const uint64_t v0 = vs + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
-                    if (!(v0 + 0 >= vlo && v0 + 0 < vhi)) r.x[k].x = M::identity;
-                    if (!(v0 + 1 >= vlo && v0 + 1 < vhi)) r.x[k].y = M::identity;
-                    if (!(v0 + 2 >= vlo && v0 + 2 < vhi)) r.x[k].z = M::identity;
-                    if (!(v0 + 3 >= vlo && v0 + 3 < vhi)) r.x[k].w = M::identity;
-                }
-            }
-        }
-        uint32_t w[V];
-        TS::local(r.x, w, c.c);
-    }
-
-    __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
-    {
-        return TileInfo{TS::cells(c.c), false, true};
-    }
-
-    __device__ __forceinline__ void last(uint32_t carry, const TileInfo &in) const
-    {
-        *total_out = M::apply(carry, in.value);
-    }
-
-    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
-    {
-        uint32_t w[V];
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            w[k] = wave_incl<M>(r.x[k].w);
-        TS::template apply<INCL>(r.x, w, c.c, carry);
-        if (whole(t))
-            store_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
-        else
-            store_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
-    }
-};
 
 template <int BLOCK, int V, bool INCL, class M = OpAdd>
 __global__ __launch_bounds__(BLOCK) void scan_pipelined_kernel(uint32_t *__restrict__ abase,

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
                  "segscan_scratch_bytes", "compact_scratch_bytes", "radix_scratch_bytes",
                  "libscan_strerror", "libscan_scratch_init", "copy_u32", "scan_op_u32",
                  "reduce_op_u32", "reduce_scratch_bytes", "scan_op_u64", "reduce_op_u64",
-                 "scan_op_u64_scratch_bytes"]:
+                 "scan_op_u64_scratch_bytes", "runs_layout_u32", "runs_slots_i32",
+                 "runs_owner_u32", "runs_owner_all_u32", "runs_scratch_bytes"]:
         assert must in names
 
 
@@ -202,3 +203,30 @@ def test_u64_scan_and_reduce_argument_errors():
     assert L.reduce_scratch_bytes(1) >= 4096 * 8
     assert L.scan_op_u64(NULLP, 0, 6, 1, NOHOST64, NULLP, NULLP, 0, NULLP) == ps.OK
     assert L.reduce_op_u64(NULLP, 0, 1, NOHOST64, NULLP, NULLP, 0, NULLP) == ps.OK
+
+
+def test_runs_argument_errors():
+    L = ps.lib()
+    big = 1 << 20
+    assert L.runs_layout_u32(FAKE, FAKE, (1 << 36) + 1, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.runs_layout_u32(NULLP, FAKE, 16, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.runs_layout_u32(FAKE, NULLP, 16, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.runs_layout_u32(FAKE, ctypes.c_void_p(0x100002), 16, NOHOST, NULLP, FAKE, big,
+                             NULLP) == ps.ERR_ALIGN
+    assert L.runs_layout_u32(FAKE, FAKE, 1 << 24, NOHOST, NULLP, FAKE, 600, NULLP) == ps.ERR_SCRATCH
+    assert L.runs_slots_i32(NULLP, 5, NULLP) == ps.ERR_NULL
+    assert L.runs_slots_i32(ctypes.c_void_p(0x100001), 5, NULLP) == ps.ERR_ALIGN
+    assert L.runs_owner_u32(FAKE, 1 << 31, FAKE, 5, FAKE, NULLP) == ps.ERR_SIZE
+    assert L.runs_owner_u32(FAKE, 16, NULLP, 5, FAKE, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_u32(NULLP, 16, FAKE, 5, FAKE, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_all_u32(FAKE, 16, FAKE, 1 << 32, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.runs_owner_all_u32(FAKE, 1 << 31, FAKE, 5, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.runs_owner_all_u32(FAKE, 16, NULLP, 5, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_all_u32(FAKE, 1 << 20, FAKE, 1 << 30, FAKE, 100, NULLP) == ps.ERR_SCRATCH
+    # merge-path partition: one u32 per 4096 merged items, plus one
+    assert L.runs_scratch_bytes(1 << 24, 1 << 26) >= ((1 << 24) + (1 << 26)) // 4096 * 4
+    # nothing to do: OK without touching anything
+    assert L.runs_slots_i32(NULLP, 0, NULLP) == ps.OK
+    assert L.runs_owner_u32(NULLP, 16, NULLP, 0, NULLP, NULLP) == ps.OK
+    assert L.runs_owner_all_u32(NULLP, 16, NULLP, 0, NULLP, 0, NULLP) == ps.OK
+    assert L.runs_layout_u32(NULLP, NULLP, 0, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
