@@ -46,6 +46,8 @@ def load():
     lib.oracle_runs_owner_all.restype = ctypes.c_int
     lib.oracle_runs_owner.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_runs_owner.restype = ctypes.c_int32
+    lib.oracle_segscan_flags_u32.argtypes = [u32p, u32p, u32p, ctypes.c_uint64, u32p]
+    lib.oracle_segscan_flags_u32.restype = ctypes.c_uint64
     lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
     lib.oracle_scan_blocked_u32.restype = ctypes.c_int
     lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
@@ -225,3 +227,19 @@ def runs_owner(ends, e):
     q = np.asarray(e, dtype=np.uint32)
     return np.array([L.oracle_runs_owner(_ptr(ends, ctypes.c_uint32), ends.size, int(x))
                      for x in q.tolist()], dtype=np.int32)
+
+
+def segscan_flags_u32(a, flags):
+    """O2b: (out, sums) -- inclusive scan of a restarted at every element
+    whose flag is non-zero (and at element 0), and each segment's total."""
+    a = _u32(a)
+    f = np.ascontiguousarray(flags).view(np.uint32) if np.asarray(flags).dtype.itemsize == 4 \
+        else np.ascontiguousarray(flags, dtype=np.uint32)
+    if f.size != a.size:
+        raise ValueError("flags and values differ in length")
+    out = np.empty_like(a)
+    sums = np.empty(max(a.size, 1), dtype=np.uint32)
+    segs = load().oracle_segscan_flags_u32(_ptr(a, ctypes.c_uint32), _ptr(f, ctypes.c_uint32),
+                                           _ptr(out, ctypes.c_uint32), a.size,
+                                           _ptr(sums, ctypes.c_uint32))
+    return out, sums[:segs].copy()

@@ -557,3 +557,34 @@ int32_t oracle_runs_owner(const uint32_t *ends, uint64_t n, uint32_t e)
             return (int32_t)i;
     return -1;
 }
+
+/* ------------------------------------------------------------------------- */
+/* O2b -- segmented scan over irregular segments given by head flags.         */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [futh] names a segmented scan over regular segments only; here segments
+ * are irregular: element j starts a segment when j == 0 or flags[j] != 0
+ * (reading: element 0 always starts one, whatever flags[0] holds).
+ * out[j] = a[h] + .. + a[j] (mod 2^32) with h the last start at or before j;
+ * sums[s], when sums is not NULL, is the total of segment s (segments
+ * numbered from 0 in order).  out may equal a.  Returns the number of
+ * segments (0 for n == 0).
+ */
+uint64_t oracle_segscan_flags_u32(const uint32_t *a, const uint32_t *flags, uint32_t *out,
+                                  uint64_t n, uint32_t *sums)
+{
+    uint32_t running = 0;
+    uint64_t segs = 0;
+    for (uint64_t j = 0; j < n; ++j) {
+        if (j == 0 || flags[j] != 0) {
+            running = 0;
+            ++segs;
+        }
+        running += a[j];
+        out[j] = running;
+        if (sums)
+            sums[segs - 1] = running;
+    }
+    return segs;
+}

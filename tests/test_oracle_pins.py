@@ -607,3 +607,80 @@ def test_runs_special_cases():
     # the sums wrap at 2^32 as the scan's do
     ends, entries = oracle.runs_u32(np.full(3, 0xFFFFFFFF, dtype=np.uint32))
     assert ends.tolist() == [0xFFFFFFFF, 0xFFFFFFFE, 0xFFFFFFFD] and entries == 0xFFFFFFFD
+
+
+# ---------------------------------------------------------------------------
+# O2b -- segmented scan over irregular segments given by head flags.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,L", [(1000, 16), (65536, 64), (100000, 1 << 20), (7, 3)])
+def test_segflags_regular_heads_equal_the_regular_segscan(n, L):
+    a = workloads.small_random_u32(n, 11, 1 << 16)
+    flags = (np.arange(n) % L == 0).astype(np.int32)
+    out, sums = oracle.segscan_flags_u32(a, flags)
+    rout, rsums = oracle.segscan_u32(a, L)
+    assert np.array_equal(out, rout) and np.array_equal(sums, rsums)
+
+
+@pytest.mark.parametrize("mean", [16, 1 << 20])
+def test_segflags_matches_numpy(mean):
+    n = 200003
+    a = workloads.small_random_u32(n, 12)
+    flags = workloads.segment_heads(n, mean)
+    out, sums = oracle.segscan_flags_u32(a, flags)
+    starts = np.flatnonzero(flags)
+    assert np.array_equal(sums, np.add.reduceat(a, starts, dtype=np.uint32))
+    cs = np.cumsum(a, dtype=np.uint32)
+    seg_of = np.cumsum(flags) - 1
+    before = (cs[starts] - a[starts]).astype(np.uint32)      # the plain prefix before each start
+    assert np.array_equal(out, (cs - before[seg_of]).astype(np.uint32))
+
+
+def test_segflags_special_cases():
+    a = workloads.small_random_u32(5000, 13)
+    # no flag after element 0: the plain inclusive scan, one segment
+    out, sums = oracle.segscan_flags_u32(a, np.zeros(5000, dtype=np.int32))
+    inc, tot = oracle.scan_inclusive_u32(a)
+    assert np.array_equal(out, inc) and sums.tolist() == [tot]
+    # flag 0 at element 0 still starts a segment; every flag set: out = a
+    out, sums = oracle.segscan_flags_u32(a, np.ones(5000, dtype=np.int32))
+    assert np.array_equal(out, a) and np.array_equal(sums, a)
+    # any non-zero flag is a head, negative included
+    f = np.zeros(5000, dtype=np.int32)
+    f[[10, 20]] = [-1, 7]
+    out, sums = oracle.segscan_flags_u32(a, f)
+    assert sums.size == 3 and int(sums[1]) == int(a[10:20].sum(dtype=np.uint64) % M)
+    out, sums = oracle.segscan_flags_u32(np.zeros(0, dtype=np.uint32), np.zeros(0, dtype=np.int32))
+    assert out.size == 0 and sums.size == 0
+
+
+def test_segflags_brute_force_tiny():
+    vals = np.array([0, 1, 0xFFFFFFFF, 0x80000000], dtype=np.uint32)
+    for n in range(0, 6):
+        for bits in range(1 << n):
+            f = np.array([(bits >> j) & 1 for j in range(n)], dtype=np.int32)
+            a = vals[np.arange(n) % 4]
+            run, segs, want = 0, [], []
+            for j in range(n):
+                if j == 0 or f[j]:
+                    run = 0
+                    segs.append(0)
+                run = (run + int(a[j])) % M
+                want.append(run)
+                segs[-1] = run
+            out, sums = oracle.segscan_flags_u32(a, f)
+            assert out.tolist() == want and sums.tolist() == segs
+
+
+def test_segflags_over_runs_gives_per_owner_totals():
+    # Heads at the starts of the non-empty runs of a runs layout: the
+    # segment sums are the per-owner totals of the entries.
+    c = workloads.runs_counts_uniform(3000)
+    ends, _ = oracle.runs_u32(c)
+    own = oracle.runs_owner_all(c)
+    vals = workloads.small_random_u32(own.size, 14, 1000)
+    flags = np.zeros(own.size, dtype=np.int32)
+    flags[(ends - c)[c > 0]] = 1
+    _, sums = oracle.segscan_flags_u32(vals, flags)
+    per_owner = np.bincount(own, weights=vals, minlength=c.size).astype(np.uint64)
+    assert np.array_equal(sums.astype(np.uint64), per_owner[c > 0])

@@ -23,6 +23,9 @@ The workloads (sizes, value ranges, seeds):
                   about 5.9e7 entries, one owner in eight empty
   runs_sparse     n = 2^24 owners, nine in ten empty, the rest uniform over
                   [1, 64) (seed 702): long stretches of empty runs
+  segflags        n = 2^26 u32 values uniform over [0, 2^16) (seed 401, as
+                  segscan) with head flags: segment lengths geometric with
+                  mean 16 (seed 801), and geometric with mean 2^20 (seed 802)
 """
 import numpy as np
 
@@ -38,6 +41,7 @@ SEED_RADIX_DISTINCT = 502
 SEED_SCAN_U64 = 601
 SEED_RUNS_UNIFORM = 701
 SEED_RUNS_SPARSE = 702
+SEED_SEGFLAGS = {16: 801, 1 << 20: 802}
 
 N_SCAN_SMALL = 1 << 16
 N_SCAN_MID = 1 << 24
@@ -122,3 +126,15 @@ def runs_counts_sparse(n: int = N_RUNS, seed: int = SEED_RUNS_SPARSE) -> np.ndar
     c = g.integers(1, 64, size=n, dtype=np.uint32)
     c[g.random(n) < 0.9] = 0
     return c
+
+
+def segment_heads(n: int, mean_len: int, seed: int = None) -> np.ndarray:
+    """int32 head flags for irregular segments: each element starts a new
+    segment with probability 1 / mean_len (geometric lengths), and element 0
+    always does."""
+    if seed is None:
+        seed = SEED_SEGFLAGS[mean_len]
+    f = (rng(seed).random(n) < 1.0 / mean_len).astype(np.int32)
+    if n:
+        f[0] = 1
+    return f
