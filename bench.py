@@ -223,6 +223,16 @@ def suite(args, torch, ps):
         sums = torch.empty((v.numel() + L - 1) // L, dtype=torch.int32, device="cuda")
         row("segscan L=%d n=2^26" % L, v.numel(), 8 + 4.0 / L,
             lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums))
+    # Irregular segments from head flags: value + flag read, output written
+    # (12 B per element) and one 4-byte total per segment.
+    f_means = (16, 1 << 20)
+    for mean in f_means:
+        fl = torch.from_numpy(workloads.segment_heads(v.numel(), mean)).to("cuda")
+        nseg = int(fl.count_nonzero().item())
+        sums = torch.empty(v.numel(), dtype=torch.int32, device="cuda")
+        row("segscan flags mean=%d n=2^26" % mean, v.numel(), 12 + 4.0 * nseg / v.numel(),
+            lambda: ps.segscan_flags_u32(v, fl, out=o, seg_sums=sums, want_nsegs=False))
+        del fl, sums
     del v, o
     # Runs laid out by owner: the ends (8 B per owner), the -1 slots (4 B per
     # entry), every entry's owner (4 B per owner + 4 B per entry), and owner
@@ -291,6 +301,8 @@ def algorithmic_bytes(name, grid):
         ("scan64_pipelined_kernel", 16 * n27), ("reduce64_partial_kernel", 8 * n27),
         ("runs_ends_kernel", 8 * (1 << 24)),
     ]
+    if "segflags_kernel" in name:
+        return 12 * n26                # + 4 B per segment, under 2% at mean length 16
     for key, b in table:
         if "::" + key + "<" in name:
             return b

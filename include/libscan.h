@@ -213,6 +213,28 @@ int scan_op_u64(uint64_t *data, uint64_t n, int op, int inclusive, uint64_t *tot
 int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host,
                   uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
 
+/*
+ * Segmented scan and segment sums over IRREGULAR segments given by head
+ * flags.  Futhark's segmented pass (Futhark.Pass.ExtractKernels.Segmented)
+ * names regular segments only; here element 0 and every element whose flag
+ * is non-zero start a segment (flags[0] is not read for that: element 0
+ * always starts one), so segments have any lengths.
+ *   out[j] = in[h] + .. + in[j] (mod 2^32), h the last start at or before j;
+ *   seg_sums[s] = total of segment s, segments numbered 0, 1, .. in order
+ *     (skipped when seg_sums is NULL; it needs room for every segment --
+ *     n entries always suffice);
+ *   the number of segments goes to *nsegs_host (the call then waits) and/or
+ *   *nsegs_dev (4-byte aligned device u32).
+ * in, flags (int32, n entries) and out (may equal in) are device arrays, any
+ * 4-byte alignment; partial overlap is undefined.  n <= 2^32 - 1 (segment
+ * numbers are u32).  Scratch: segscan_flags_scratch_bytes(n).  n == 0 is a
+ * no-op with 0 segments.  Errors as for segscan_u32.
+ */
+size_t segscan_flags_scratch_bytes(uint64_t n);
+int segscan_flags_u32(const uint32_t *in, const int32_t *flags, uint32_t *out, uint64_t n,
+                      uint32_t *seg_sums, uint32_t *nsegs_host, uint32_t *nsegs_dev,
+                      void *scratch, size_t scratch_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Runs: entries laid out by owner                                          */
 /* ------------------------------------------------------------------------ */

@@ -21,6 +21,7 @@ __all__ = [
     "scan_exclusive_u32", "scan_inclusive_u32", "scan_u32_ex",
     "scan_op_u32", "reduce_op_u32", "scan_op_u64", "reduce_op_u64",
     "runs_layout_u32", "runs_slots_i32", "runs_owner_u32", "runs_owner_all_u32",
+    "segscan_flags_u32",
     "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
     "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
     "compact_scratch_bytes", "radix_scratch_bytes",
@@ -90,6 +91,10 @@ def lib():
         L.scan_op_u64.restype = i32
         L.reduce_op_u64.argtypes = [vp, u64, i32, u64p, vp, vp, sz, vp]
         L.reduce_op_u64.restype = i32
+        L.segscan_flags_scratch_bytes.argtypes = [u64]
+        L.segscan_flags_scratch_bytes.restype = sz
+        L.segscan_flags_u32.argtypes = [vp, vp, vp, u64, vp, u32p, vp, vp, sz, vp]
+        L.segscan_flags_u32.restype = i32
         L.runs_scratch_bytes.argtypes = [u64, u64]
         L.runs_scratch_bytes.restype = sz
         L.runs_layout_u32.argtypes = [vp, vp, u64, u32p, vp, vp, sz, vp]
@@ -404,6 +409,43 @@ def segscan_u32(inp, seg_len, out=None, seg_sums=True, stream=None):
     _check(lib().segscan_u32(_ptr(inp), _ptr(out), n, seg_len, _ptr(seg_sums), _ptr(scr),
                              scr.numel(), sh), "segscan_u32")
     return out, seg_sums
+
+
+def segscan_flags_u32(inp, flags, out=None, seg_sums=True, want_nsegs=True, nsegs_dev=None,
+                      stream=None):
+    """Inclusive scan restarted at element 0 and wherever flags is non-zero,
+    and each segment's total.
+
+    out: output tensor (default: a new one; pass `inp` for in place).
+    seg_sums: True for a new tensor of n entries, a tensor with room for
+    every segment, or None to skip.  Returns (out, sums, nsegs): when
+    want_nsegs, nsegs is the segment count and sums (if made here) is cut to
+    it; else nsegs is None and the count goes to nsegs_dev."""
+    _dev_u32(inp, "inp")
+    _dev_u32(flags, "flags")
+    n = inp.numel()
+    if flags.numel() != n:
+        raise ValueError("flags must have as many elements as inp")
+    if out is None:
+        out = torch.empty_like(inp)
+    _dev_u32(out, "out")
+    if out.numel() != n:
+        raise ValueError("out must have as many elements as inp")
+    made = seg_sums is True
+    if made:
+        seg_sums = torch.empty(max(n, 1), dtype=inp.dtype, device=inp.device)
+    if seg_sums is not None:
+        _dev_u32(seg_sums, "seg_sums")
+    sh, s = _stream_handle(inp.device, stream)
+    scr = _scratch_for(inp.device, s, lib().segscan_flags_scratch_bytes(n))
+    host, hp = _total_args(want_nsegs, nsegs_dev)
+    _check(lib().segscan_flags_u32(_ptr(inp), _ptr(flags), _ptr(out), n, _ptr(seg_sums), hp,
+                                   _ptr(nsegs_dev), _ptr(scr), scr.numel(), sh),
+           "segscan_flags_u32")
+    nsegs = int(host.value) if want_nsegs else None
+    if made and nsegs is not None:
+        seg_sums = seg_sums[:nsegs]
+    return out, seg_sums, nsegs
 
 
 def compact_scratch_bytes(n):

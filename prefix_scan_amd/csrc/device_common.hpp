@@ -203,19 +203,28 @@ __device__ __forceinline__ uint64_t dpp64_or(uint64_t x, uint64_t old)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Inclusive wave scan of u64 values under Op (the steps of wave_incl_add).
+// Inclusive wave scan of u64 values under Op (the steps of wave_incl_add),
+// keeping operand order: lane l ends with x_0 op x_1 op .. op x_l, so Op
+// need not commute (the segmented pair of segflags_kernels.hip does not).
 template <class Op>
 __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
 {
     constexpr uint64_t e = Op::identity;
-    x = Op::apply(x, dpp64_or<kDppRowShr1, 0xF>(x, e));
-    x = Op::apply(x, dpp64_or<kDppRowShr2, 0xF>(x, e));
-    x = Op::apply(x, dpp64_or<kDppRowShr4, 0xF>(x, e));
-    x = Op::apply(x, dpp64_or<kDppRowShr8, 0xF>(x, e));
-    x = Op::apply(x, dpp64_or<kDppRowBcast15, 0xA>(x, e));
-    x = Op::apply(x, dpp64_or<kDppRowBcast31, 0xC>(x, e));
+    x = Op::apply(dpp64_or<kDppRowShr1, 0xF>(x, e), x);
+    x = Op::apply(dpp64_or<kDppRowShr2, 0xF>(x, e), x);
+    x = Op::apply(dpp64_or<kDppRowShr4, 0xF>(x, e), x);
+    x = Op::apply(dpp64_or<kDppRowShr8, 0xF>(x, e), x);
+    x = Op::apply(dpp64_or<kDppRowBcast15, 0xA>(x, e), x);
+    x = Op::apply(dpp64_or<kDppRowBcast31, 0xC>(x, e), x);
     return x;
 }
+
+// Op with its operands swapped.
+template <class Op>
+struct Reversed64 {
+    static constexpr uint64_t identity = Op::identity;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return Op::apply(b, a); }
+};
 
 __device__ __forceinline__ uint64_t wave_bcast_last64(uint64_t x)
 {
@@ -666,7 +675,8 @@ __device__ __forceinline__ LookbackWindow64 lookback64_load(const uint64_t *desc
     return w;
 }
 
-// As lookback_fold, for u64 values.
+// As lookback_fold, for u64 values, keeping operand order (tiles fold from
+// the farthest to the nearest), so Op need not commute.
 template <class Op>
 __device__ __forceinline__ int lookback64_fold(const LookbackWindow64 &w, uint32_t tag,
                                                uint64_t &excl)
@@ -683,7 +693,11 @@ __device__ __forceinline__ int lookback64_fold(const LookbackWindow64 &w, uint32
     const uint64_t upto = (p >= 63) ? ~0ull : ((2ull << p) - 1);
     if (wait & upto)
         return 0;
-    excl = Op::apply(excl, wave_fold64<Op>(lane_id() <= p ? val : Op::identity));
+    // Lane l holds tile base - l: the window's fold, farthest tile first, is
+    // the lanes folded in descending order, and it goes before the nearer
+    // windows already in excl.
+    const uint64_t win = wave_fold64<Reversed64<Op>>(lane_id() <= p ? val : Op::identity);
+    excl = Op::apply(win, excl);
     return pref ? 2 : 1;
 }
 

@@ -111,6 +111,12 @@ hipError_t launch_segscan(const uint32_t *in, uint32_t *out, uint64_t n, uint64_
                           uint32_t *seg_sums, const Scratch &s, hipStream_t stream);
 size_t segscan_body_bytes(uint64_t n, uint64_t seg_len);
 
+// ---- segmented scan over head flags (segflags_kernels.hip) ----
+hipError_t launch_segflags(const uint32_t *in, const uint32_t *flags, uint32_t *out, uint64_t n,
+                           uint32_t *sums, uint32_t *nsegs_out, const Scratch &s,
+                           hipStream_t stream);
+size_t segflags_body_bytes(uint64_t n);
+
 // ---- compaction (compact_kernels.hip) ----
 hipError_t launch_compact(const int32_t *flags, int32_t *out, uint64_t n, const Scratch &s,
                           uint32_t *count_out, hipStream_t stream);

@@ -568,6 +568,39 @@ int segscan_u32(const uint32_t *in, uint32_t *out, uint64_t n, uint64_t seg_len,
     return hip_status(launch_segscan(in, out, n, seg_len, seg_sums, s, stream));
 }
 
+size_t segscan_flags_scratch_bytes(uint64_t n)
+{
+    return with_header(segflags_body_bytes(n));
+}
+
+int segscan_flags_u32(const uint32_t *in, const int32_t *flags, uint32_t *out, uint64_t n,
+                      uint32_t *seg_sums, uint32_t *nsegs_host, uint32_t *nsegs_dev,
+                      void *scratch, size_t scratch_bytes, hipStream_t stream)
+{
+    if (n > 0xFFFFFFFFull)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(in) || misaligned4(flags) || misaligned4(out) || misaligned4(seg_sums) ||
+        misaligned4(nsegs_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_value(nsegs_host, nsegs_dev, 0u, stream);
+    if (!in || !flags || !out || !scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, segflags_body_bytes(n), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    uint32_t *cnt = nsegs_dev ? nsegs_dev : s.total_slot();
+    hipError_t e = prepare_state(s, kKindDesc, 0, segflags_body_bytes(n), 1, stream);
+    if (e == hipSuccess)
+        e = launch_segflags(in, reinterpret_cast<const uint32_t *>(flags), out, n, seg_sums, cnt,
+                            s, stream);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (nsegs_host)
+        return read_back(nsegs_host, cnt, stream);
+    return LIBSCAN_OK;
+}
+
 size_t compact_scratch_bytes(uint64_t n) { return with_header(compact_body_bytes(n)); }
 
 int compact_flags_u32(const int32_t *flags, int32_t *out_idx, uint64_t n, uint32_t *count_host,

@@ -64,7 +64,8 @@ struct TileInfoT {
 using TileInfo = TileInfoT<uint32_t>;
 
 // How a carry of the monoid M travels between tiles: a u32 value in one
-// descriptor word per tile, or a u64 value in two.
+// descriptor word per tile (M must commute: the look-back folds nearer tiles
+// first), or a u64 value in two (operand order kept, any associative M).
 template <class M>
 struct Carry32 {
     using T = uint32_t;

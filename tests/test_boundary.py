@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
                  "libscan_strerror", "libscan_scratch_init", "copy_u32", "scan_op_u32",
                  "reduce_op_u32", "reduce_scratch_bytes", "scan_op_u64", "reduce_op_u64",
                  "scan_op_u64_scratch_bytes", "runs_layout_u32", "runs_slots_i32",
-                 "runs_owner_u32", "runs_owner_all_u32", "runs_scratch_bytes"]:
+                 "runs_owner_u32", "runs_owner_all_u32", "runs_scratch_bytes",
+                 "segscan_flags_u32", "segscan_flags_scratch_bytes"]:
         assert must in names
 
 
@@ -230,3 +231,20 @@ def test_runs_argument_errors():
     assert L.runs_owner_u32(NULLP, 16, NULLP, 0, NULLP, NULLP) == ps.OK
     assert L.runs_owner_all_u32(NULLP, 16, NULLP, 0, NULLP, 0, NULLP) == ps.OK
     assert L.runs_layout_u32(NULLP, NULLP, 0, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
+
+
+def test_segscan_flags_argument_errors():
+    L = ps.lib()
+    big = 1 << 20
+    assert L.segscan_flags_u32(FAKE, FAKE, FAKE, 1 << 32, NULLP, NOHOST, NULLP, FAKE, big,
+                               NULLP) == ps.ERR_SIZE
+    assert L.segscan_flags_u32(NULLP, FAKE, FAKE, 16, NULLP, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.segscan_flags_u32(FAKE, NULLP, FAKE, 16, NULLP, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.segscan_flags_u32(FAKE, FAKE, NULLP, 16, NULLP, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.segscan_flags_u32(FAKE, ctypes.c_void_p(0x100001), FAKE, 16, NULLP, NOHOST, NULLP,
+                               FAKE, big, NULLP) == ps.ERR_ALIGN
+    assert L.segscan_flags_u32(FAKE, FAKE, FAKE, 1 << 26, NULLP, NOHOST, NULLP, FAKE,
+                               L.segscan_flags_scratch_bytes(1 << 26) - 300, NULLP) == ps.ERR_SCRATCH
+    # two descriptor words per 16384-element tile
+    assert L.segscan_flags_scratch_bytes(1 << 26) >= ((1 << 26) // 16384) * 16
+    assert L.segscan_flags_u32(NULLP, NULLP, NULLP, 0, NULLP, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
