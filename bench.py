@@ -29,7 +29,8 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
 METRIC = "GElem/s and % of HBM peak, U32 exclusive scan at n=2^28 (1 GPU)"
 KERNEL_SOURCES = ["prefix_scan_amd/csrc/device_common.hpp", "prefix_scan_amd/csrc/pipeline.hpp",
-                  "prefix_scan_amd/csrc/scan_kernels.hip", "prefix_scan_amd/csrc/launch.hpp"]
+                  "prefix_scan_amd/csrc/scan_op.hpp", "prefix_scan_amd/csrc/scan_kernels.hip",
+                  "prefix_scan_amd/csrc/launch.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_lookback_u32_n2p28_traffic.json")
 
 
@@ -319,7 +320,7 @@ def algorithmic_bytes(name, grid):
     return None
 COPY_KERNEL = "libscan::copy_kernel"
 SCAN_KERNEL = "libscan::scan_pipelined_kernel"
-SCAN_SHAPE = "<512, 16, false>"        # the default shape of the exclusive scan
+SCAN_SHAPE = "<512, 16, false, libscan::OpAdd>"    # the exclusive add scan's default shape
 
 
 def _rocpd(path):
