@@ -1,7 +1,8 @@
 """GPU parity at the sizes where 32-bit arithmetic would break.
 
-Arrays past 2^32 elements (scan, segmented scan) and compaction at the int32
-index limit (n = 2^31 - 1).  Inputs have closed-form results -- all ones for
+Arrays past 2^32 elements (scan, segmented scan, u64 scan), the segmented
+scan over head flags at its 2^32 - 1 limit, and compaction, radix and runs
+at the int32 index limit (n = 2^31 - 1).  Inputs have closed-form results -- all ones for
 the scans (the exclusive scan of ones is j mod 2^32, the segmented scan is
 (j mod L) + 1), every third flag kept for compaction (kept index k is 3k) --
 so the whole output is checked, element by element, on the GPU in slices.
@@ -125,3 +126,80 @@ def test_radix_at_int32_limit(bits):
         return r + 7 * (k - st[r])
     _check_slices(perm, expected, "radix %d-bit n=2^31-1" % bits)
     _free(perm)
+
+
+def test_u64_scan_beyond_2p32_elements():
+    # 2^32 + 4097 u64 (32 GiB), starting 8 bytes past a 16-byte boundary:
+    # exclusive scan of ones is j; the total is n.
+    n = (1 << 32) + 4097
+    buf = torch.ones(n + 3, dtype=torch.int64, device="cuda")
+    t = buf[1:1 + n]
+    assert ps.scan_op_u64(t, "add") == n
+    for start in range(0, n, SLICE):
+        stop = min(n, start + SLICE)
+        exp = torch.arange(start, stop, dtype=torch.int64, device="cuda")
+        bad = torch.nonzero(t[start:stop] != exp)
+        assert bad.numel() == 0, "u64 scan: first mismatch at %d" % (start + int(bad[0, 0]))
+    assert int(buf[0]) == 1 and int(buf[1 + n]) == 1
+    _free(buf, t)
+
+
+def test_segscan_flags_at_u32_limit():
+    # n = 2^32 - 1 ones with a segment start every 1000 elements: the output
+    # is (j mod 1000) + 1, the segment totals 1000 but the last, the count
+    # ceil(n / 1000).
+    n = (1 << 32) - 1
+    L = 1000
+    vals = torch.ones(n, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(n, dtype=torch.int32, device="cuda")
+    flags[::L] = 1
+    nseg = (n + L - 1) // L
+    sums = torch.empty(nseg, dtype=torch.int32, device="cuda")
+    out, _, count = ps.segscan_flags_u32(vals, flags, out=vals, seg_sums=sums)
+    assert count == nseg
+    del flags
+    torch.cuda.empty_cache()
+
+    def expected(start, stop):
+        return torch.arange(start, stop, dtype=torch.int64, device="cuda") % L + 1
+    _check_slices(out, expected, "segscan flags n=2^32-1")
+    lens = np.full(nseg, L, dtype=np.int64)
+    lens[-1] = n - (nseg - 1) * L
+    assert np.array_equal(_u32(sums).cpu().numpy(), lens)
+    _free(out, sums, vals)
+
+
+def test_runs_at_int32_limit():
+    # 2^31 - 1 owners with one entry each but every 5th owner empty: the run
+    # ends are j + 1 - floor((j + 1) / 5), the owner of entry e is
+    # 5 floor(e / 4) + e mod 4; checked whole, plus owner queries at the ends.
+    n = (1 << 31) - 1
+    i = torch.arange(n, dtype=torch.int64, device="cuda")
+    counts = (i % 5 != 4).to(torch.int32)            # owners 4, 9, 14, .. are empty
+    del i
+    torch.cuda.empty_cache()
+    ends, entries = ps.runs_layout_u32(counts)
+    total = n - n // 5
+    assert entries == total
+    del counts
+    torch.cuda.empty_cache()
+
+    def ends_of(start, stop):
+        j = torch.arange(start, stop, dtype=torch.int64, device="cuda")
+        return j + 1 - (j + 1) // 5
+    _check_slices(ends, ends_of, "runs ends n=2^31-1")
+    owner = ps.runs_owner_all_u32(ends, total)
+
+    def owner_of(start, stop):
+        # entry e belongs to the owner skipping every 5th: 5 * (e // 4) + e % 4
+        e = torch.arange(start, stop, dtype=torch.int64, device="cuda")
+        return 5 * (e // 4) + e % 4
+    _check_slices(owner, owner_of, "runs owner of every entry n=2^31-1")
+    del owner
+    torch.cuda.empty_cache()
+    q = torch.tensor([0, 3, 4, total - 1, total, 0xFFFFFFFF], dtype=torch.int64,
+                     device="cuda").to(torch.int32)
+    got = ps.runs_owner_u32(ends, q).cpu().numpy().tolist()
+    last = 5 * ((total - 1) // 4) + (total - 1) % 4
+    assert got == [0, 3, 5, last, -1, -1]
+    _free(ends, q)
