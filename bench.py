@@ -275,14 +275,14 @@ def suite(args, torch, ps):
 # wrote; see the commands in PROFILE_COMMANDS).
 # --------------------------------------------------------------------------
 PROFILE_COMMANDS = [
-    "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_trace -o run -- "
+    "rocprofv3 --kernel-trace --stats -d rocprof_out/trace -o run -- "
     "python3 bench.py --steps 20 --warmup 5 --no-cpu [--suite --hbm-rows]",
-    "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o run -- "
+    "rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run -- "
     "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite --hbm-rows]",
-    "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o run -- "
+    "rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run -- "
     "python3 bench.py --steps 3 --warmup 1 --no-cpu [--suite --hbm-rows]",
-    "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
-    "gpurun_out/prof_write [--suite]",
+    "python3 bench.py --summarize-profiles rocprof_out/trace rocprof_out/fetch "
+    "rocprof_out/write [--suite]",
 ]
 
 
