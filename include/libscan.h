@@ -258,6 +258,7 @@ int segscan_flags_u32(const uint32_t *in, const int32_t *flags, uint32_t *out, u
  *   ends[n-1], or n == 0), for m u32 queries.  ends must be non-decreasing
  *   (counts whose sum stays below 2^32); otherwise the owners are
  *   unspecified (the call still touches only its arrays).  n <= 2^31 - 1.
+ *   Scratch: runs_scratch_bytes(n, 0) (an index of every 32nd end).
  * runs_owner_all_u32: owner[e] = owner(e, ends) for every entry e in
  *   [0, total), total <= 2^32 - 1 (normally ends[n-1]).  Scratch:
  *   runs_scratch_bytes(n, total).  Same condition on ends.
@@ -270,7 +271,7 @@ int runs_layout_u32(const uint32_t *counts, uint32_t *ends, uint64_t n, uint32_t
                     uint32_t *entries_dev, void *scratch, size_t scratch_bytes, hipStream_t stream);
 int runs_slots_i32(int32_t *slots, uint64_t entries, hipStream_t stream);
 int runs_owner_u32(const uint32_t *ends, uint64_t n, const uint32_t *entry, uint64_t m,
-                   int32_t *owner, hipStream_t stream);
+                   int32_t *owner, void *scratch, size_t scratch_bytes, hipStream_t stream);
 int runs_owner_all_u32(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
                        void *scratch, size_t scratch_bytes, hipStream_t stream);
 

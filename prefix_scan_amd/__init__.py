@@ -101,7 +101,7 @@ def lib():
         L.runs_layout_u32.restype = i32
         L.runs_slots_i32.argtypes = [vp, u64, vp]
         L.runs_slots_i32.restype = i32
-        L.runs_owner_u32.argtypes = [vp, u64, vp, u64, vp, vp]
+        L.runs_owner_u32.argtypes = [vp, u64, vp, u64, vp, vp, sz, vp]
         L.runs_owner_u32.restype = i32
         L.runs_owner_all_u32.argtypes = [vp, u64, vp, u64, vp, sz, vp]
         L.runs_owner_all_u32.restype = i32
@@ -358,9 +358,10 @@ def runs_owner_u32(ends, entry, owner=None, stream=None):
     _dev_u32(owner, "owner")
     if owner.numel() != entry.numel():
         raise ValueError("owner must have as many elements as entry")
-    sh, _ = _stream_handle(entry.device, stream)
+    sh, s = _stream_handle(entry.device, stream)
+    scr = _scratch_for(entry.device, s, lib().runs_scratch_bytes(ends.numel(), 0))
     _check(lib().runs_owner_u32(_ptr(ends), ends.numel(), _ptr(entry), entry.numel(), _ptr(owner),
-                                sh), "runs_owner_u32")
+                                _ptr(scr), scr.numel(), sh), "runs_owner_u32")
     return owner
 
 

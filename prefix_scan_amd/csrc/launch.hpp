@@ -101,7 +101,8 @@ hipError_t launch_runs_ends(const uint32_t *counts, uint32_t *ends, uint64_t n, 
 size_t runs_body_bytes(uint64_t n);
 hipError_t launch_fill_value(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream);
 hipError_t launch_runs_owner(const uint32_t *ends, uint64_t n, const uint32_t *query, uint64_t m,
-                             int32_t *owner, hipStream_t stream);
+                             int32_t *owner, const Scratch &s, hipStream_t stream);
+uint64_t runs_index_entries(uint64_t n);
 hipError_t launch_runs_owner_all(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,
                                  const Scratch &s, hipStream_t stream);
 uint64_t runs_owner_all_parts(uint64_t n, uint64_t total);

@@ -456,7 +456,9 @@ size_t runs_scratch_bytes(uint64_t n, uint64_t total)
 {
     const size_t a = runs_body_bytes(n);
     const size_t b = (size_t)(runs_owner_all_parts(n, total) + 1) * sizeof(uint32_t);
-    return with_header(a > b ? a : b);
+    const size_t c = (size_t)runs_index_entries(n) * sizeof(uint32_t);
+    const size_t ab = a > b ? a : b;
+    return with_header(ab > c ? ab : c);
 }
 
 int runs_layout_u32(const uint32_t *counts, uint32_t *ends, uint64_t n, uint32_t *entries_host,
@@ -499,7 +501,7 @@ int runs_slots_i32(int32_t *slots, uint64_t entries, hipStream_t stream)
 }
 
 int runs_owner_u32(const uint32_t *ends, uint64_t n, const uint32_t *entry, uint64_t m,
-                   int32_t *owner, hipStream_t stream)
+                   int32_t *owner, void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
     if (n > LIBSCAN_MAX_N_INDEX || m > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;
@@ -512,7 +514,15 @@ int runs_owner_u32(const uint32_t *ends, uint64_t n, const uint32_t *entry, uint
     if (n == 0)       // no run holds anything
         return hip_status(launch_fill_value(reinterpret_cast<uint32_t *>(owner), m, 0xFFFFFFFFu,
                                             stream));
-    return hip_status(launch_runs_owner(ends, n, entry, m, owner, stream));
+    if (!scratch)
+        return LIBSCAN_ERR_NULL;
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, (size_t)runs_index_entries(n) * sizeof(uint32_t), &s))
+        return LIBSCAN_ERR_SCRATCH;
+    hipError_t e = prepare_state(s, kKindData, 0, 0, 0, stream);
+    if (e == hipSuccess)
+        e = launch_runs_owner(ends, n, entry, m, owner, s, stream);
+    return hip_status(e);
 }
 
 int runs_owner_all_u32(const uint32_t *ends, uint64_t n, int32_t *owner, uint64_t total,

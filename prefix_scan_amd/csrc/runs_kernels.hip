@@ -11,8 +11,9 @@
 //    pipelined chained-carry driver (scan_op.hpp); its last tile writes
 //    entries = max(total, 1).  8 bytes per owner.
 //  * fill_value_kernel: the slots, -1 with 16-byte stores.  4 bytes per slot.
-//  * runs_owner_kernel: owner(e, ends) for a batch of entries, a binary
-//    search over the ends per query.
+//  * runs_index_kernel + runs_owner_kernel: owner(e, ends) for a batch of
+//    entries, a search over an index of every 32nd end, then over one
+//    block of 32 ends.
 //  * runs_partition_kernel + runs_owner_all_kernel: the owner of every entry
 //    0 .. total-1.  The ends and the entries are merged as two sorted lists
 //    (the end of run i comes before entry e when ends[i] <= e), so an entry's
@@ -150,36 +151,79 @@ hipError_t launch_fill_value(uint32_t *p, uint64_t n, uint32_t value, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// owner(e, ends) for a batch of entries.
+// owner(e, ends) for a batch of entries.  A search straight over the ends
+// misses the cache on about seven 128-byte lines per query (the levels below
+// the ones every query shares).  So an index of the last end of every block
+// of 32 (one u32 per 128 bytes of ends: 2 MiB for 2^24 owners, which the L2
+// keeps) is built first; a query searches the index for its block, then the
+// block's 32 ends, one line.
 // ---------------------------------------------------------------------------
+constexpr uint64_t kIdxStride = 32;
+
+uint64_t runs_index_entries(uint64_t n) { return (n + kIdxStride - 1) / kIdxStride; }
+
+__global__ __launch_bounds__(256) void runs_index_kernel(const uint32_t *__restrict__ ends,
+                                                         uint64_t n, uint32_t *__restrict__ idx,
+                                                         uint64_t nidx)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nidx; k += stride) {
+        const uint64_t last = k * kIdxStride + kIdxStride - 1;
+        idx[k] = ends[last < n ? last : n - 1];
+    }
+}
+
 __global__ __launch_bounds__(256) void runs_owner_kernel(const uint32_t *__restrict__ ends,
                                                          uint32_t n,
+                                                         const uint32_t *__restrict__ idx,
+                                                         uint32_t nidx,
                                                          const uint32_t *__restrict__ query,
                                                          uint64_t m, int32_t *__restrict__ owner)
 {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < m; j += stride) {
         const uint32_t e = query[j];
-        uint32_t lo = 0, hi = n;               // the least i with ends[i] > e
+        // The least block whose last end exceeds e holds the least such end.
+        uint32_t lo = 0, hi = nidx;
         while (lo < hi) {
             const uint32_t mid = lo + (hi - lo) / 2;
-            if (ends[mid] > e)
+            if (idx[mid] > e)
                 hi = mid;
             else
                 lo = mid + 1;
         }
-        owner[j] = lo < n ? (int32_t)lo : -1;
+        int32_t r = -1;                         // no run holds e
+        if (lo < nidx) {
+            uint32_t a = lo * (uint32_t)kIdxStride;
+            uint32_t b = a + (uint32_t)kIdxStride < n ? a + (uint32_t)kIdxStride : n;
+            while (a < b) {                     // the least i in the block with ends[i] > e
+                const uint32_t mid = a + (b - a) / 2;
+                if (ends[mid] > e)
+                    b = mid;
+                else
+                    a = mid + 1;
+            }
+            r = (int32_t)a;
+        }
+        owner[j] = r;
     }
 }
 
 hipError_t launch_runs_owner(const uint32_t *ends, uint64_t n, const uint32_t *query, uint64_t m,
-                             int32_t *owner, hipStream_t stream)
+                             int32_t *owner, const Scratch &s, hipStream_t stream)
 {
+    const uint64_t nidx = runs_index_entries(n);
+    uint32_t *idx = reinterpret_cast<uint32_t *>(s.body());
+    uint64_t igrid = (nidx + 255) / 256;
+    if (igrid > 8192)
+        igrid = 8192;
+    hipLaunchKernelGGL(runs_index_kernel, dim3((uint32_t)igrid), dim3(256), 0, stream, ends, n, idx,
+                       nidx);
     uint64_t grid = (m + 255) / 256;
     if (grid > 8192)
         grid = 8192;
     hipLaunchKernelGGL(runs_owner_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, ends,
-                       (uint32_t)n, query, m, owner);
+                       (uint32_t)n, idx, (uint32_t)nidx, query, m, owner);
     return hipGetLastError();
 }
 

@@ -217,9 +217,13 @@ def test_runs_argument_errors():
     assert L.runs_layout_u32(FAKE, FAKE, 1 << 24, NOHOST, NULLP, FAKE, 600, NULLP) == ps.ERR_SCRATCH
     assert L.runs_slots_i32(NULLP, 5, NULLP) == ps.ERR_NULL
     assert L.runs_slots_i32(ctypes.c_void_p(0x100001), 5, NULLP) == ps.ERR_ALIGN
-    assert L.runs_owner_u32(FAKE, 1 << 31, FAKE, 5, FAKE, NULLP) == ps.ERR_SIZE
-    assert L.runs_owner_u32(FAKE, 16, NULLP, 5, FAKE, NULLP) == ps.ERR_NULL
-    assert L.runs_owner_u32(NULLP, 16, FAKE, 5, FAKE, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_u32(FAKE, 1 << 31, FAKE, 5, FAKE, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.runs_owner_u32(FAKE, 16, NULLP, 5, FAKE, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_u32(NULLP, 16, FAKE, 5, FAKE, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_u32(FAKE, 16, FAKE, 5, FAKE, NULLP, big, NULLP) == ps.ERR_NULL
+    assert L.runs_owner_u32(FAKE, 1 << 24, FAKE, 5, FAKE, FAKE, 1000, NULLP) == ps.ERR_SCRATCH
+    # the query index: one u32 per 32 ends
+    assert L.runs_scratch_bytes(1 << 24, 0) >= ((1 << 24) // 32) * 4
     assert L.runs_owner_all_u32(FAKE, 16, FAKE, 1 << 32, FAKE, big, NULLP) == ps.ERR_SIZE
     assert L.runs_owner_all_u32(FAKE, 1 << 31, FAKE, 5, FAKE, big, NULLP) == ps.ERR_SIZE
     assert L.runs_owner_all_u32(FAKE, 16, NULLP, 5, FAKE, big, NULLP) == ps.ERR_NULL
@@ -228,7 +232,7 @@ def test_runs_argument_errors():
     assert L.runs_scratch_bytes(1 << 24, 1 << 26) >= ((1 << 24) + (1 << 26)) // 4096 * 4
     # nothing to do: OK without touching anything
     assert L.runs_slots_i32(NULLP, 0, NULLP) == ps.OK
-    assert L.runs_owner_u32(NULLP, 16, NULLP, 0, NULLP, NULLP) == ps.OK
+    assert L.runs_owner_u32(NULLP, 16, NULLP, 0, NULLP, NULLP, 0, NULLP) == ps.OK
     assert L.runs_owner_all_u32(NULLP, 16, NULLP, 0, NULLP, 0, NULLP) == ps.OK
     assert L.runs_layout_u32(NULLP, NULLP, 0, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK
 
