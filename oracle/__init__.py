@@ -83,8 +83,10 @@ def scan_u32(a, inclusive=False):
 
 
 # Operator codes of oracle_scan_op_u32 / oracle_reduce_op_u32 ([cairn]
-# "reduce and compact": add_wrap, mul_wrap, &, |, ^, min, max).
-OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6}
+# "reduce and compact": add_wrap, mul_wrap, &, |, ^, min, max; min_s and
+# max_s compare the words as signed integers).
+OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6, "min_s": 7,
+       "max_s": 8}
 
 
 def scan_op_u32(a, op, inclusive=False):

@@ -78,8 +78,12 @@ uint32_t oracle_scan_u32(const uint32_t *a, uint32_t *out, uint64_t n, int inclu
  * form what came before i.  Readings: values are unsigned 32-bit (min and
  * max compare them as unsigned); the exclusive output at 0, and the result
  * of an empty range, is the operator's identity (0 for add_wrap, | , ^ and
- * max; 1 for mul_wrap; 0xFFFFFFFF for & and min).
- * Operator codes: 0 add_wrap, 1 mul_wrap, 2 &, 3 |, 4 ^, 5 min, 6 max.
+ * max; 1 for mul_wrap; 0xFFFFFFFF for & and min).  CAIRN's min and max are
+ * defined on integers, signed ones included: codes 7 and 8 compare the same
+ * 32-bit words as two's-complement int32 (identities INT32_MAX and
+ * INT32_MIN); the other operators give the same bits either way.
+ * Operator codes: 0 add_wrap, 1 mul_wrap, 2 &, 3 |, 4 ^, 5 min, 6 max,
+ * 7 signed min, 8 signed max.
  */
 static uint32_t op_identity(int op)
 {
@@ -87,6 +91,8 @@ static uint32_t op_identity(int op)
     case 1: return 1u;
     case 2: return 0xFFFFFFFFu;
     case 5: return 0xFFFFFFFFu;
+    case 7: return 0x7FFFFFFFu;
+    case 8: return 0x80000000u;
     default: return 0u;
     }
 }
@@ -101,15 +107,17 @@ static uint32_t op_apply(int op, uint32_t a, uint32_t b)
     case 4: return a ^ b;
     case 5: return a < b ? a : b;
     case 6: return a > b ? a : b;
+    case 7: return (int32_t)a < (int32_t)b ? a : b;
+    case 8: return (int32_t)a > (int32_t)b ? a : b;
     default: return 0u;
     }
 }
 
 /* Returns the fold of all n values (the identity for n == 0); out may equal
- * a.  An operator code outside 0..6 returns 0 and writes nothing. */
+ * a.  An operator code outside 0..8 returns 0 and writes nothing. */
 uint32_t oracle_scan_op_u32(const uint32_t *a, uint32_t *out, uint64_t n, int op, int inclusive)
 {
-    if (op < 0 || op > 6)
+    if (op < 0 || op > 8)
         return 0u;
     uint32_t running = op_identity(op);
     for (uint64_t j = 0; j < n; ++j) {
@@ -128,7 +136,7 @@ uint32_t oracle_scan_op_u32(const uint32_t *a, uint32_t *out, uint64_t n, int op
 /* [cairn] "reduce and compact": the fold of n values in index order. */
 uint32_t oracle_reduce_op_u32(const uint32_t *a, uint64_t n, int op)
 {
-    if (op < 0 || op > 6)
+    if (op < 0 || op > 8)
         return 0u;
     uint32_t acc = op_identity(op);
     for (uint64_t j = 0; j < n; ++j)
@@ -146,7 +154,8 @@ uint32_t oracle_reduce_op_u32(const uint32_t *a, uint64_t n, int op)
  * mul_wrap and ^), and its pooled scan is measured on u64 elements.  The
  * operators, the operator codes and the identities are those of O1c, taken
  * mod 2^64 (C defines uint64_t overflow as wrap-around mod 2^64); the
- * identity of & and min is 2^64 - 1.
+ * identity of & and min is 2^64 - 1; signed min and max (codes 7, 8)
+ * compare as int64 with identities INT64_MAX and INT64_MIN.
  */
 static uint64_t op_identity64(int op)
 {
@@ -154,6 +163,8 @@ static uint64_t op_identity64(int op)
     case 1: return 1u;
     case 2: return UINT64_MAX;
     case 5: return UINT64_MAX;
+    case 7: return (uint64_t)INT64_MAX;
+    case 8: return (uint64_t)INT64_MIN;
     default: return 0u;
     }
 }
@@ -168,15 +179,17 @@ static uint64_t op_apply64(int op, uint64_t a, uint64_t b)
     case 4: return a ^ b;
     case 5: return a < b ? a : b;
     case 6: return a > b ? a : b;
+    case 7: return (int64_t)a < (int64_t)b ? a : b;
+    case 8: return (int64_t)a > (int64_t)b ? a : b;
     default: return 0u;
     }
 }
 
 /* Returns the fold of all n values (the identity for n == 0); out may equal
- * a.  An operator code outside 0..6 returns 0 and writes nothing. */
+ * a.  An operator code outside 0..8 returns 0 and writes nothing. */
 uint64_t oracle_scan_op_u64(const uint64_t *a, uint64_t *out, uint64_t n, int op, int inclusive)
 {
-    if (op < 0 || op > 6)
+    if (op < 0 || op > 8)
         return 0u;
     uint64_t running = op_identity64(op);
     for (uint64_t j = 0; j < n; ++j) {
@@ -195,7 +208,7 @@ uint64_t oracle_scan_op_u64(const uint64_t *a, uint64_t *out, uint64_t n, int op
 /* [cairn] "reduce and compact": the fold of n u64 values in index order. */
 uint64_t oracle_reduce_op_u64(const uint64_t *a, uint64_t n, int op)
 {
-    if (op < 0 || op > 6)
+    if (op < 0 || op > 8)
         return 0u;
     uint64_t acc = op_identity64(op);
     for (uint64_t j = 0; j < n; ++j)

@@ -339,9 +339,24 @@ def test_radix_rejects_bad_args():
 # O1c -- scan and reduce under the other integer operators.
 # ---------------------------------------------------------------------------
 OP_IDENTITY = {"add": 0, "mul": 1, "and": 0xFFFFFFFF, "or": 0, "xor": 0, "min": 0xFFFFFFFF,
-               "max": 0}
+               "max": 0, "min_s": 0x7FFFFFFF, "max_s": 0x80000000}
 NP_ACCUMULATE = {"add": np.add, "mul": np.multiply, "and": np.bitwise_and, "or": np.bitwise_or,
-                 "xor": np.bitwise_xor, "min": np.minimum, "max": np.maximum}
+                 "xor": np.bitwise_xor, "min": np.minimum, "max": np.maximum,
+                 "min_s": np.minimum, "max_s": np.maximum}
+SIGNED = {"min_s", "max_s"}
+
+
+def np_accumulate(op, a):
+    """numpy's ufunc accumulate of the unsigned array a under op, comparing
+    as signed integers for min_s / max_s; returns the unsigned bits."""
+    if op in SIGNED:
+        s = a.view(np.int32 if a.dtype == np.uint32 else np.int64)
+        return NP_ACCUMULATE[op].accumulate(s).view(a.dtype)
+    return NP_ACCUMULATE[op].accumulate(a, dtype=a.dtype)
+
+
+def to_signed(x, bits):
+    return x - (1 << bits) if x >= 1 << (bits - 1) else x
 
 
 def test_op_scan_cairn_max_example():
@@ -372,7 +387,7 @@ def test_op_scan_matches_numpy_accumulate(op, n):
         a = (rng.integers(0, 2**32, n, dtype=np.uint32) | 1).astype(np.uint32)   # odd: no collapse to 0
     else:
         a = rng.integers(0, 2**32, n, dtype=np.uint32)
-    ref = NP_ACCUMULATE[op].accumulate(a, dtype=np.uint32)
+    ref = np_accumulate(op, a)
     inc, total = oracle.scan_op_u32(a, op, inclusive=True)
     assert np.array_equal(inc, ref)
     exc, total_e = oracle.scan_op_u32(a, op, inclusive=False)
@@ -386,7 +401,9 @@ def test_op_scan_brute_force_small(op):
     # Python integers, reduced mod 2^32 after every step, over small arrays.
     apply = {"add": lambda x, y: (x + y) % 2**32, "mul": lambda x, y: (x * y) % 2**32,
              "and": lambda x, y: x & y, "or": lambda x, y: x | y, "xor": lambda x, y: x ^ y,
-             "min": min, "max": max}[op]
+             "min": min, "max": max,
+             "min_s": lambda x, y: min(x, y, key=lambda v: to_signed(v, 32)),
+             "max_s": lambda x, y: max(x, y, key=lambda v: to_signed(v, 32))}[op]
     rng = np.random.default_rng(77)
     for n in range(0, 12):
         a = rng.choice(np.array([0, 1, 2, 3, 0x80000000, 0xFFFFFFFF, 0xDEADBEEF], dtype=np.uint32), n)
@@ -438,7 +455,8 @@ def test_op_scan_add_is_the_plain_scan_and_empty_is_identity():
 # O1d -- the same operators on u64 values, mod 2^64.
 # ---------------------------------------------------------------------------
 M64 = 1 << 64
-OP_IDENTITY64 = {"add": 0, "mul": 1, "and": M64 - 1, "or": 0, "xor": 0, "min": M64 - 1, "max": 0}
+OP_IDENTITY64 = {"add": 0, "mul": 1, "and": M64 - 1, "or": 0, "xor": 0, "min": M64 - 1, "max": 0,
+                 "min_s": 2**63 - 1, "max_s": 2**63}
 
 
 def test_op64_cairn_examples():
@@ -473,7 +491,7 @@ def test_op64_scan_matches_numpy_accumulate(op, n):
     a = rng.integers(0, 2**64, n, dtype=np.uint64)
     if op == "mul":
         a |= np.uint64(1)
-    ref = NP_ACCUMULATE[op].accumulate(a, dtype=np.uint64)
+    ref = np_accumulate(op, a)
     inc, total = oracle.scan_op_u64(a, op, inclusive=True)
     assert np.array_equal(inc, ref)
     exc, total_e = oracle.scan_op_u64(a, op, inclusive=False)
@@ -487,7 +505,9 @@ def test_op64_scan_brute_force_small(op):
     # Python integers reduced mod 2^64 after every step.
     apply = {"add": lambda x, y: (x + y) % M64, "mul": lambda x, y: (x * y) % M64,
              "and": lambda x, y: x & y, "or": lambda x, y: x | y, "xor": lambda x, y: x ^ y,
-             "min": min, "max": max}[op]
+             "min": min, "max": max,
+             "min_s": lambda x, y: min(x, y, key=lambda v: to_signed(v, 64)),
+             "max_s": lambda x, y: max(x, y, key=lambda v: to_signed(v, 64))}[op]
     vals = np.array([0, 1, 3, 2**31, 2**32 - 1, 2**32, 2**63, M64 - 1, 0xDEADBEEFCAFEF00D],
                     dtype=np.uint64)
     rng = np.random.default_rng(78)
@@ -523,8 +543,10 @@ def test_op64_carry_crosses_the_32_bit_boundary():
 @pytest.mark.parametrize("op", sorted(OP_IDENTITY64))
 def test_op64_agrees_with_u32_below_2_32(op):
     # On values below 2^32 every operator's u64 result, taken mod 2^32 (for
-    # add and mul) or as is (the others), is the u32 oracle's.
-    a = np.random.default_rng(9).integers(0, 2**32, 5000, dtype=np.uint32)
+    # add and mul) or as is (the others), is the u32 oracle's -- below 2^31
+    # for the signed comparisons, where both widths read the values alike.
+    a = np.random.default_rng(9).integers(0, 2**31 if op in SIGNED else 2**32, 5000,
+                                          dtype=np.uint32)
     if op == "mul":
         a |= np.uint32(1)
     r64, t64 = oracle.scan_op_u64(a.astype(np.uint64), op, inclusive=True)
@@ -684,3 +706,21 @@ def test_segflags_over_runs_gives_per_owner_totals():
     _, sums = oracle.segscan_flags_u32(vals, flags)
     per_owner = np.bincount(own, weights=vals, minlength=c.size).astype(np.uint64)
     assert np.array_equal(sums.astype(np.uint64), per_owner[c > 0])
+
+
+def test_signed_min_max_closed_forms():
+    # Signed and unsigned order differ exactly on the top bit: -1 is the
+    # largest unsigned word but the least signed one.
+    a = np.array([5, 0xFFFFFFFF, 3, 0x80000000, 7], dtype=np.uint32)
+    assert oracle.scan_op_u32(a, "min_s", inclusive=True)[0].tolist() == [5, 0xFFFFFFFF, 0xFFFFFFFF,
+                                                                           0x80000000, 0x80000000]
+    assert oracle.scan_op_u32(a, "max_s", inclusive=True)[0].tolist() == [5, 5, 5, 5, 7]
+    assert oracle.scan_op_u32(a, "min", inclusive=True)[0].tolist() == [5, 5, 3, 3, 3]
+    assert oracle.reduce_op_u32(a, "max") == 0xFFFFFFFF and oracle.reduce_op_u32(a, "max_s") == 7
+    b = np.array([2**63, 1, M64 - 1, 2**62], dtype=np.uint64)
+    assert oracle.reduce_op_u64(b, "min_s") == 2**63 and oracle.reduce_op_u64(b, "max_s") == 2**62
+    assert oracle.scan_op_u64(b, "max_s", inclusive=False)[0].tolist() == [2**63, 2**63, 1, 1]
+    # the other operators give the same bits whatever the signedness
+    x = np.random.default_rng(3).integers(0, 2**32, 1000, dtype=np.uint32)
+    assert np.array_equal(oracle.scan_op_u32(x, "add")[0],
+                          np.cumsum(x.view(np.int32), dtype=np.int32).view(np.uint32) - x)
