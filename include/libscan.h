@@ -155,11 +155,14 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
  * one value per index into a total, and its integer operators are add_wrap,
  * mul_wrap, &, |, ^, min and max; section "scan": a scan takes the same
  * operators, inclusive (out[i] = e(0) op .. op e(i)) or exclusive (what came
- * before i).  Values are unsigned 32-bit; min and max compare them as
- * unsigned; the exclusive output at index 0, and the result for n == 0, is
- * the operator's identity (0 for ADD, OR, XOR and MAX; 1 for MUL; 0xFFFFFFFF
- * for AND and MIN).  Every operator is associative and commutative, so the
- * bits do not depend on how the library groups the work.
+ * before i).  Values are 32-bit words; MIN and MAX compare them as
+ * unsigned, MIN_S and MAX_S as two's-complement signed (CAIRN's min and max
+ * are defined on integers, signed ones included; every other operator gives
+ * the same bits either way); the exclusive output at index 0, and the
+ * result for n == 0, is the operator's identity (0 for ADD, OR, XOR and MAX;
+ * 1 for MUL; 0xFFFFFFFF for AND and MIN; 0x7FFFFFFF for MIN_S; 0x80000000
+ * for MAX_S).  Every operator is associative and commutative, so the bits do
+ * not depend on how the library groups the work.
  */
 enum {
     LIBSCAN_OP_ADD = 0,     /* add_wrap (mod 2^32) */
@@ -168,7 +171,9 @@ enum {
     LIBSCAN_OP_OR = 3,
     LIBSCAN_OP_XOR = 4,
     LIBSCAN_OP_MIN = 5,
-    LIBSCAN_OP_MAX = 6
+    LIBSCAN_OP_MAX = 6,
+    LIBSCAN_OP_MIN_S = 7,   /* min as signed integers */
+    LIBSCAN_OP_MAX_S = 8    /* max as signed integers */
 };
 
 /*
@@ -176,7 +181,7 @@ enum {
  * *total_host and/or *total_dev as for scan_exclusive_u32.  Scratch: at least
  * scan_scratch_bytes(n).  Same layout, ownership and stream rules as
  * scan_exclusive_u32.  Errors: LIBSCAN_ERR_ARG for an op outside
- * LIBSCAN_OP_ADD..LIBSCAN_OP_MAX or inclusive not 0/1, plus those of
+ * LIBSCAN_OP_ADD..LIBSCAN_OP_MAX_S or inclusive not 0/1, plus those of
  * scan_exclusive_u32.  (op = LIBSCAN_OP_ADD is scan_exclusive_u32 /
  * scan_inclusive_u32.)
  */
@@ -201,7 +206,7 @@ int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host
  * total of 0..899 is 404550; "reduce and compact": u64 weights, a checksum
  * mixed with mul_wrap and ^; "scan": its scan is measured on u64 elements).
  * Operators and identities as above, with 2^64 - 1 the identity of AND and
- * MIN.  `data` and `total_dev` must be 8-byte aligned (LIBSCAN_ERR_ALIGN
+ * MIN, and 2^63 - 1 and 2^63 those of MIN_S and MAX_S (signed int64 order).  `data` and `total_dev` must be 8-byte aligned (LIBSCAN_ERR_ALIGN
  * otherwise); element i is at byte offset 8*i.  Scan scratch: at least
  * scan_op_u64_scratch_bytes(n); reduction scratch: reduce_scratch_bytes(n),
  * which covers both widths.  Ownership, stream, result and error rules as

@@ -239,7 +239,8 @@ def _scan(name, data, want_total, total_dev, stream):
 
 
 # LIBSCAN_OP_* of libscan.h.
-OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6}
+OPS = {"add": 0, "mul": 1, "and": 2, "or": 3, "xor": 4, "min": 5, "max": 6, "min_s": 7,
+       "max_s": 8}
 
 
 def _op(op):
@@ -250,8 +251,9 @@ def _op(op):
 
 def scan_op_u32(data, op, inclusive=False, want_total=True, total_dev=None, stream=None):
     """In-place scan of `data` under the operator named `op` ("add", "mul",
-    "and", "or", "xor", "min", "max"); returns the fold of all values (an
-    int, after waiting for the stream) when want_total, else None."""
+    "and", "or", "xor", "min", "max", or "min_s" / "max_s" comparing as
+    signed); returns the fold of all values (an int, after waiting for the
+    stream) when want_total, else None."""
     _dev_u32(data, "data")
     o = _op(op)
     sh, s = _stream_handle(data.device, stream)

@@ -90,8 +90,9 @@ __device__ __forceinline__ uint32_t wave_shr1(uint32_t x)
 // ---------------------------------------------------------------------------
 // The integer operators of a scan or reduction (CAIRN "Concurrency",
 // "reduce and compact"): add_wrap, mul_wrap, &, |, ^, min and max on
-// unsigned 32-bit values, each with its identity.  All are associative and
-// commutative, so any grouping gives the same bits.
+// 32-bit values, each with its identity; min and max compare as unsigned,
+// or as signed (MinS, MaxS).  All are associative and commutative, so any
+// grouping gives the same bits.
 // ---------------------------------------------------------------------------
 struct OpAdd {
     static constexpr uint32_t identity = 0u;
@@ -120,6 +121,21 @@ struct OpMin {
 struct OpMax {
     static constexpr uint32_t identity = 0u;
     __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b) { return a > b ? a : b; }
+};
+// min and max of the words read as two's-complement int32.
+struct OpMinS {
+    static constexpr uint32_t identity = 0x7FFFFFFFu;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b)
+    {
+        return (int32_t)a < (int32_t)b ? a : b;
+    }
+};
+struct OpMaxS {
+    static constexpr uint32_t identity = 0x80000000u;
+    __device__ static __forceinline__ uint32_t apply(uint32_t a, uint32_t b)
+    {
+        return (int32_t)a > (int32_t)b ? a : b;
+    }
 };
 
 // The same operators on unsigned 64-bit values (CAIRN writes its rows as
@@ -151,6 +167,20 @@ struct OpMin64 {
 struct OpMax64 {
     static constexpr uint64_t identity = 0u;
     __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b) { return a > b ? a : b; }
+};
+struct OpMinS64 {
+    static constexpr uint64_t identity = 0x7FFFFFFFFFFFFFFFull;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b)
+    {
+        return (int64_t)a < (int64_t)b ? a : b;
+    }
+};
+struct OpMaxS64 {
+    static constexpr uint64_t identity = 0x8000000000000000ull;
+    __device__ static __forceinline__ uint64_t apply(uint64_t a, uint64_t b)
+    {
+        return (int64_t)a > (int64_t)b ? a : b;
+    }
 };
 
 // DPP move whose disabled lanes (source outside the row, masked rows) read

@@ -204,13 +204,15 @@ int report_zero(uint32_t *host, uint32_t *dev, hipStream_t stream)
 // Identities of the LIBSCAN_OP_* operators.
 uint32_t op_identity(int op)
 {
-    static const uint32_t id[7] = {0u, 1u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu, 0u};
+    static const uint32_t id[9] = {0u, 1u, 0xFFFFFFFFu, 0u, 0u, 0xFFFFFFFFu, 0u, 0x7FFFFFFFu,
+                                   0x80000000u};
     return id[op];
 }
 
 uint64_t op_identity64(int op)
 {
-    static const uint64_t id[7] = {0u, 1u, ~0ull, 0u, 0u, ~0ull, 0u};
+    static const uint64_t id[9] = {0u, 1u, ~0ull, 0u, 0u, ~0ull, 0u, 0x7FFFFFFFFFFFFFFFull,
+                                   0x8000000000000000ull};
     return id[op];
 }
 
@@ -335,7 +337,7 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
 int scan_op_u32(uint32_t *data, uint64_t n, int op, int inclusive, uint32_t *total_host,
                 uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX || (inclusive != 0 && inclusive != 1))
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX_S || (inclusive != 0 && inclusive != 1))
         return LIBSCAN_ERR_ARG;
     if (n > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;
@@ -369,7 +371,7 @@ size_t reduce_scratch_bytes(uint64_t n)
 int reduce_op_u32(const uint32_t *data, uint64_t n, int op, uint32_t *total_host,
                   uint32_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX)
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX_S)
         return LIBSCAN_ERR_ARG;
     if (n > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;
@@ -401,7 +403,7 @@ size_t scan_op_u64_scratch_bytes(uint64_t n)
 int scan_op_u64(uint64_t *data, uint64_t n, int op, int inclusive, uint64_t *total_host,
                 uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX || (inclusive != 0 && inclusive != 1))
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX_S || (inclusive != 0 && inclusive != 1))
         return LIBSCAN_ERR_ARG;
     if (n > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;
@@ -428,7 +430,7 @@ int scan_op_u64(uint64_t *data, uint64_t n, int op, int inclusive, uint64_t *tot
 int reduce_op_u64(const uint64_t *data, uint64_t n, int op, uint64_t *total_host,
                   uint64_t *total_dev, void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX)
+    if (op < LIBSCAN_OP_ADD || op > LIBSCAN_OP_MAX_S)
         return LIBSCAN_ERR_ARG;
     if (n > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;

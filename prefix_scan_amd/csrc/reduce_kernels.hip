@@ -3,10 +3,11 @@
 //
 // CAIRN "Concurrency", section "reduce and compact": a reduction combines
 // one value per index into a total under add_wrap, mul_wrap, &, |, ^, min or
-// max; the integer operators give the same total in any order.  So a grid
-// that fills the GPU walks the tiles round-robin, each workgroup folds its
-// tiles into one partial (a thread's chunks, the wave, the workgroup), and
-// one workgroup folds the partials.  4 bytes read per element.
+// max (unsigned or signed); the integer operators give the same total in any
+// order.  So a grid that fills the GPU walks the tiles round-robin, each
+// workgroup folds its tiles into one partial (a thread's chunks, the wave,
+// the workgroup), and one workgroup folds the partials.  4 bytes read per
+// element.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -118,6 +119,8 @@ hipError_t launch_reduce_op(const uint32_t *data, uint64_t n, int op, const Scra
     case 4: return launch_reduce_m<OpXor>(data, n, s, total_out, stream);
     case 5: return launch_reduce_m<OpMin>(data, n, s, total_out, stream);
     case 6: return launch_reduce_m<OpMax>(data, n, s, total_out, stream);
+    case 7: return launch_reduce_m<OpMinS>(data, n, s, total_out, stream);
+    case 8: return launch_reduce_m<OpMaxS>(data, n, s, total_out, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -4,8 +4,8 @@
 // CAIRN "Concurrency" writes its rows as u64: "Tasks and leases" totals
 // 0..899 with add_wrap, "reduce and compact" reduces u64 weights and mixes a
 // checksum with mul_wrap and ^, and "scan" measures its pooled scan on u64
-// elements.  The operators (add_wrap, mul_wrap, &, |, ^, min, max) are those
-// of the u32 kernels, taken mod 2^64.
+// elements.  The operators (add_wrap, mul_wrap, &, |, ^, min, max, signed
+// min and max) are those of the u32 kernels, taken mod 2^64.
 //
 // The scan runs on the same grid-filling two-tile chained-carry driver as
 // the u32 scan (pipeline.hpp) with a two-word carry (Carry64): a tile of
@@ -221,6 +221,8 @@ hipError_t launch_scan_op64(uint64_t *data, uint64_t n, int op, bool inclusive, 
     case 4: return scan64_m<OpXor64>(data, n, inclusive, s, total_out, stream);
     case 5: return scan64_m<OpMin64>(data, n, inclusive, s, total_out, stream);
     case 6: return scan64_m<OpMax64>(data, n, inclusive, s, total_out, stream);
+    case 7: return scan64_m<OpMinS64>(data, n, inclusive, s, total_out, stream);
+    case 8: return scan64_m<OpMaxS64>(data, n, inclusive, s, total_out, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -326,6 +328,8 @@ hipError_t launch_reduce_op64(const uint64_t *data, uint64_t n, int op, const Sc
     case 4: return reduce64_m<OpXor64>(data, n, s, total_out, stream);
     case 5: return reduce64_m<OpMin64>(data, n, s, total_out, stream);
     case 6: return reduce64_m<OpMax64>(data, n, s, total_out, stream);
+    case 7: return reduce64_m<OpMinS64>(data, n, s, total_out, stream);
+    case 8: return reduce64_m<OpMaxS64>(data, n, s, total_out, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -416,6 +416,8 @@ hipError_t launch_scan_op(uint32_t *data, uint64_t n, int op, bool inclusive, co
     case 4: return scan_op_m<OpXor>(data, n, inclusive, s, total_out, stream);
     case 5: return scan_op_m<OpMin>(data, n, inclusive, s, total_out, stream);
     case 6: return scan_op_m<OpMax>(data, n, inclusive, s, total_out, stream);
+    case 7: return scan_op_m<OpMinS>(data, n, inclusive, s, total_out, stream);
+    case 8: return scan_op_m<OpMaxS>(data, n, inclusive, s, total_out, stream);
     default: return hipErrorInvalidValue;
     }
 }

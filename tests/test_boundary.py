@@ -161,7 +161,7 @@ def test_python_binding_rejects_cpu_tensors():
 def test_operator_scan_and_reduce_argument_errors():
     L = ps.lib()
     big = 1 << 20
-    for op in (-1, 7):
+    for op in (-1, 9):
         assert L.scan_op_u32(FAKE, 16, op, 0, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
         assert L.reduce_op_u32(FAKE, 16, op, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
     assert L.scan_op_u32(FAKE, 16, 6, 2, NOHOST, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
@@ -184,7 +184,7 @@ def test_u64_scan_and_reduce_argument_errors():
     L = ps.lib()
     big = 1 << 20
     NOHOST64 = ctypes.POINTER(ctypes.c_uint64)()
-    for op in (-1, 7):
+    for op in (-1, 9):
         assert L.scan_op_u64(FAKE, 16, op, 0, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
         assert L.reduce_op_u64(FAKE, 16, op, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG
     assert L.scan_op_u64(FAKE, 16, 0, 2, NOHOST64, NULLP, FAKE, big, NULLP) == ps.ERR_ARG

@@ -18,7 +18,7 @@ import prefix_scan_amd as ps
 from tests.gpu_util import first_mismatch, to_dev, to_host_u32
 
 pytestmark = pytest.mark.gpu
-OPS = ["add", "mul", "and", "or", "xor", "min", "max"]
+OPS = ["add", "mul", "and", "or", "xor", "min", "max", "min_s", "max_s"]
 
 
 def shaped(op, n, seed):
@@ -30,6 +30,12 @@ def shaped(op, n, seed):
         return (((i * 16) + rng.integers(0, 64, n, dtype=np.uint64)) % 2**32).astype(np.uint32)
     if op == "min":
         return (np.uint64(2**32 - 1) - ((i * 16) + rng.integers(0, 64, n, dtype=np.uint64)) % 2**32).astype(np.uint32)
+    if op in ("min_s", "max_s"):
+        # a signed trend through zero: the running extreme keeps changing and
+        # crosses the top bit, where signed and unsigned order disagree
+        t = (i.astype(np.int64) - n // 2) * 16 + rng.integers(0, 64, n)
+        t = t if op == "max_s" else -t
+        return (t % 2**32).astype(np.uint32)
     # one bit, whose position climbs through 0..31 along the array
     bit = (i * 32 // max(n, 1)).astype(np.uint64)
     if op == "or":
@@ -62,7 +68,7 @@ def test_scan_op_uniform(op):
     check_scan(a, op, True, 0)
 
 
-@pytest.mark.parametrize("op", ["xor", "max", "mul"])
+@pytest.mark.parametrize("op", ["xor", "max", "mul", "min_s"])
 def test_scan_op_headline_size(op):
     check_scan(shaped(op, 1 << 28, 29), op, False)
 

@@ -17,7 +17,7 @@ import prefix_scan_amd as ps
 from tests.gpu_util import first_mismatch, to_dev64, to_host_u64
 
 pytestmark = pytest.mark.gpu
-OPS = ["add", "mul", "and", "or", "xor", "min", "max"]
+OPS = ["add", "mul", "and", "or", "xor", "min", "max", "min_s", "max_s"]
 M64 = 1 << 64
 
 
@@ -30,6 +30,11 @@ def shaped(op, n, seed):
         return i * np.uint64(1 << 30) + rng.integers(0, 1 << 30, n, dtype=np.uint64)
     if op == "min":
         return np.uint64(M64 - 1) - (i * np.uint64(1 << 30) + rng.integers(0, 1 << 30, n, dtype=np.uint64))
+    if op in ("min_s", "max_s"):
+        # a signed trend through zero, crossing the top bit
+        t = (i.astype(np.int64) - n // 2) * (1 << 30) + rng.integers(0, 1 << 30, n)
+        t = t if op == "max_s" else -t
+        return t.astype(np.int64).view(np.uint64)
     bit = (i * np.uint64(64) // np.uint64(max(n, 1))).astype(np.uint64)
     if op == "or":
         return np.uint64(1) << bit
