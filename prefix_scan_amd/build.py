@@ -3,12 +3,17 @@
     python -m prefix_scan_amd.build        # or: python prefix_scan_amd/build.py
 
 The library is compiled for gfx950 only, with hipcc, into the package
-directory, where the Python binding loads it.
+directory, where the Python binding loads it.  Each source compiles to an
+object of its own, several at a time, and the objects are linked into one
+shared library.
 """
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -21,7 +26,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # No packed fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -31,24 +35,48 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(csrc=CSRC):
+    return sorted(glob.glob(os.path.join(csrc, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libscan.so; returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _jobs():
     try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16, int(os.environ.get("MAX_JOBS", n))))
+
+
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB, defines=()) -> str:
+    """Compile every *.hip of `csrc` into the shared library `out`; returns
+    its path.  `defines` are extra -D options for every source."""
+    tmp = out + ".tmp%d" % os.getpid()
+    objdir = tempfile.mkdtemp(prefix="libscan_obj")
+    extra = ["-D" + d for d in defines]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC] + FLAGS + extra + ["-I", INCLUDE, "-I", csrc, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    try:
+        with ThreadPoolExecutor(_jobs()) as pool:
+            objs = list(pool.map(compile_one, sources(csrc)))
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
     except BaseException:
         if os.path.exists(tmp):
             os.remove(tmp)
         raise
-    os.replace(tmp, LIB)
-    return LIB
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
