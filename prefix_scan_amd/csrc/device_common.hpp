@@ -298,6 +298,15 @@ __device__ __forceinline__ void wave_seg_incl(uint32_t &f, uint32_t &v)
     seg_step<kDppRowBcast31, 0xC>(f, v);
 }
 
+// Zero, computed by an instruction that reads v: whatever uses the result is
+// issued only after the load that wrote v has landed.
+__device__ __forceinline__ int32_t zero_after(uint32_t v)
+{
+    uint32_t z;
+    asm volatile("v_and_b32 %0, 0, %1" : "=v"(z) : "v"(v));
+    return (int32_t)z;
+}
+
 // ---------------------------------------------------------------------------
 // Chunk I/O.
 // ---------------------------------------------------------------------------

@@ -14,6 +14,15 @@
 // So a tile asks for its carry one full load latency after its own
 // aggregate went out, and its predecessors had the same time to publish.
 //
+// An Op that loads and reduces a tile in one call (load_local, below) has
+// the window read later: once the next tile's loads have landed, just
+// before that tile is reduced.  Read as the step starts, the window shows
+// the descriptors of a load latency earlier, when the tiles just before --
+// held by other workgroups at the same point of their own steps -- had not
+// published their prefixes yet, so the fold mostly needed a second, fresh
+// window: a round trip on the critical path.  Read late, it mostly holds a
+// prefix already.
+//
 // Tile numbers are drawn one at a time, so consecutive tiles go to different
 // workgroups that run side by side.  (Drawing several consecutive numbers
 // per atomic would relieve the one contended ticket word, but it hands runs
@@ -45,6 +54,13 @@
 //                                          may hold barriers of its own)
 //   void last(T carry, const TileInfoT<T> &);     thread 0, last tile only
 // where T is the carry's value type (u32 unless the Op names Carry64).
+// Optionally, in place of load + local for the tile after the current one:
+//   template <class R>
+//   void load_local(Regs &, Cells &, uint32_t tile, R &&ready);
+//                                          issue the loads, call ready(v) with
+//                                          v a register the last load writes
+//                                          (0 where there is none), then
+//                                          phase 1
 #pragma once
 
 #include "device_common.hpp"
@@ -123,6 +139,12 @@ struct carry_of<Op, std::void_t<typename Op::Carry>> {
 
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
+// Whether Op loads and reduces a tile in one call, with a hook between.
+template <class Op, class = void>
+struct has_load_local : std::false_type {};
+template <class Op>
+struct has_load_local<Op, std::void_t<decltype(Op::kLoadLocal)>> : std::true_type {};
+
 template <class Op>
 __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_t *ticket,
                                                 uint32_t *exits, uint64_t *desc)
@@ -195,15 +217,27 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
     auto step = [&](typename Op::Regs &X, typename Op::Regs &Y) {
         const int nb = cb == 2 ? 0 : cb + 1;
         const bool carry_needed = cur != 0 && info_cur.need_carry;     // wave 0
+        const bool have_next = nxt != kNoTile;
+        constexpr bool kLate = has_load_local<Op>::value;
         typename C::Window w0{};
-        if (threadIdx.x < kWave && carry_needed)
+        if (!kLate && threadIdx.x < kWave && carry_needed)
             w0 = C::load(desc, (int64_t)cur - 1);
         const bool drawing = threadIdx.x == kDrawer && nxt != kNoTile;
         const uint32_t nn_raw = drawing ? draw_num() : 0u;
-        const bool have_next = nxt != kNoTile;
         if (have_next) {
-            op.load(Y, nxt);
-            op.local(Y, s_cells[nb], nxt);
+            if constexpr (kLate) {
+                // The window is read after the load that writes `landed`
+                // (and so after every earlier load: loads land in order).
+                op.load_local(Y, s_cells[nb], nxt, [&](uint32_t landed) {
+                    if (threadIdx.x < kWave && carry_needed)
+                        w0 = C::load(desc, (int64_t)cur - 1 + zero_after(landed));
+                });
+            } else {
+                op.load(Y, nxt);
+                op.local(Y, s_cells[nb], nxt);
+            }
+        } else if (kLate && threadIdx.x < kWave && carry_needed) {
+            w0 = C::load(desc, (int64_t)cur - 1);
         }
         __syncthreads();
         Info info_next{C::identity, true, false};

@@ -69,6 +69,25 @@ struct ScanOp {
         TS::local(r.x, w, c.c);
     }
 
+    // Loads and reduces a tile in one call, so the driver reads the carry's
+    // first look-back window once the tile's loads have landed.  Whole and
+    // partial tiles take separate paths, so the waits of phase 1 in each
+    // follow that path's own loads.
+    static constexpr bool kLoadLocal = true;
+    template <class R>
+    __device__ __forceinline__ void load_local(Regs &r, Cells &c, uint32_t t, R &&ready) const
+    {
+        if (whole(t)) {
+            load_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
+            ready(r.x[V - 1].x);
+            local(r, c, t);
+        } else {
+            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
+            ready(0u);
+            local(r, c, t);
+        }
+    }
+
     __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t) const
     {
         return TileInfo{TS::cells(c.c), false, true};

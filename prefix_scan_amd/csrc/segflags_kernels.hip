@@ -69,12 +69,41 @@ struct SegFlagsOp {
         return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
     }
 
+    // Loads and reduces a tile in one call, so the driver reads the carry's
+    // first look-back window once the tile's loads have landed (the head
+    // bits are built from the flags, which load last).  Whole and partial
+    // tiles take separate paths.
+    static constexpr bool kLoadLocal = true;
+    template <class R>
+    __device__ __forceinline__ void load_local(Regs &r, Cells &c, uint32_t t, R &&ready) const
+    {
+        if (whole(t)) {
+            load_as<true>(r, t);
+            ready(r.hb);
+            local(r, c, t);
+        } else {
+            load_as<false>(r, t);
+            ready(r.hb);
+            local(r, c, t);
+        }
+    }
+
     __device__ __forceinline__ void load(Regs &r, uint32_t t) const
+    {
+        if (whole(t))
+            load_as<true>(r, t);
+        else
+            load_as<false>(r, t);
+    }
+
+    // WHOLE: the tile is known to lie wholly inside the array.
+    template <bool WHOLE>
+    __device__ __forceinline__ void load_as(Regs &r, uint32_t t) const
     {
         const uint64_t vstart = (uint64_t)t * T;
         const uint64_t q0 = vstart / 4 + threadIdx.x;
         u32x4 f[V];
-        if (whole(t)) {
+        if constexpr (WHOLE) {
             load_tile_full<BLOCK, V>(vbase, vstart, r.x);
             if constexpr (VEC_FLAGS) {
                 load_tile_full<BLOCK, V>(fbase, vstart, f);
