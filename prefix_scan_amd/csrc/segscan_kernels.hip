@@ -359,6 +359,263 @@ __global__ __launch_bounds__(BLOCK) void segscan_independent_kernel(
     op.finish(r, s_cells, t, 0u);
 }
 
+// ---------------------------------------------------------------------------
+// Short segments on a 16-byte-aligned array: L = 4G elements with G a power
+// of two up to 64.  Segment s is then G whole chunks, and in the chunk-major
+// layout those are held by G neighbouring lanes in one row of chunks of one
+// wave.  A segment's scan is each lane's in-chunk scan plus the exclusive
+// scan of its group's chunk totals -- log2 G DPP steps, each added only in
+// lanes at least that far into their group -- and its sum is the total the
+// group's last lane ends with.  No LDS, no barrier, no carry between
+// workgroups: the Small regime of Futhark's regularSegmentedRedomap with the
+// segment inside a wave.
+// ---------------------------------------------------------------------------
+template <int G, int CTRL, int ROW_MASK, int D>
+__device__ __forceinline__ void group_step(uint32_t &x, uint32_t lane)
+{
+    const uint32_t y = dpp<CTRL, ROW_MASK>(x);
+    if constexpr (G >= 16) {
+        x += y;     // groups of whole rows: every lane the move reaches is in the group
+    } else {
+        x += ((lane & (G - 1)) >= (uint32_t)D) ? y : 0u;
+    }
+}
+
+// Inclusive scan of x over groups of G neighbouring lanes.
+template <int G>
+__device__ __forceinline__ uint32_t group_incl(uint32_t x)
+{
+    const uint32_t lane = lane_id();
+    if constexpr (G >= 2) group_step<G, kDppRowShr1, 0xF, 1>(x, lane);
+    if constexpr (G >= 4) group_step<G, kDppRowShr2, 0xF, 2>(x, lane);
+    if constexpr (G >= 8) group_step<G, kDppRowShr4, 0xF, 4>(x, lane);
+    if constexpr (G >= 16) group_step<G, kDppRowShr8, 0xF, 8>(x, lane);
+    if constexpr (G >= 32) group_step<G, kDppRowBcast15, 0xA, 16>(x, lane);
+    if constexpr (G >= 64) group_step<G, kDppRowBcast31, 0xC, 32>(x, lane);
+    return x;
+}
+
+template <int BLOCK, int V, int G>
+__global__ __launch_bounds__(BLOCK) void segscan_lanes_kernel(const uint32_t *__restrict__ in,
+                                                              uint32_t *out, uint64_t n,
+                                                              uint32_t *__restrict__ sums)
+{
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    const uint64_t vstart = (uint64_t)blockIdx.x * T;
+    const bool whole = vstart + T <= n;
+    u32x4 x[V];
+    if (whole)
+        load_tile_full<BLOCK, V>(in, vstart, x);
+    else
+        load_tile<BLOCK, V>(in, vstart, 0, n, x);       // slots past the end read 0
+    const uint32_t lane = lane_id();
+    const uint64_t nseg = (n + 4 * G - 1) / (4 * G);
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        x[k].y += x[k].x;
+        x[k].z += x[k].y;
+        x[k].w += x[k].z;
+        const uint32_t incl = group_incl<G>(x[k].w);
+        const uint32_t before = incl - x[k].w;          // the group's chunks before this one
+        x[k].x += before;
+        x[k].y += before;
+        x[k].z += before;
+        x[k].w = incl;
+        if (sums && (lane & (G - 1)) == G - 1) {
+            // Zeros past the end leave a short last segment's total intact.
+            const uint64_t seg = (vstart / 4 + (uint64_t)k * BLOCK + threadIdx.x) / G;
+            if (seg < nseg)
+                sums[seg] = incl;
+        }
+    }
+    if (whole)
+        store_tile_full<BLOCK, V>(out, vstart, x);
+    else
+        store_tile<BLOCK, V>(out, vstart, 0, n, x);
+}
+
+// ---------------------------------------------------------------------------
+// Long segments, L >= the tile: a tile holds at most one head.  The tile is
+// scanned exactly as by the plain scan (ScanOp's registers and phases); the
+// head, at tile offset h, splits it into the part before h, which takes the
+// carry like any scan tile, and the part from h on, which restarts: its
+// outputs are the tile's local inclusive prefixes minus `pre`, the local
+// prefix before h.  A tile with a head publishes its sum since the head as
+// a final prefix at once (Futhark's Large regime, where a segment spans
+// several workgroups, with the partial sums chained instead of combined in
+// a second kernel).  Segment sums: the value just before a head inside a
+// tile (carry + pre) and the tile's last value when the next element opens
+// a segment or the array ends.
+// ---------------------------------------------------------------------------
+template <int BLOCK_, int V, bool VEC_OUT>
+struct SegLongOp {
+    static constexpr int BLOCK = BLOCK_;
+    using Monoid = OpAdd;
+    static constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    static constexpr int NW = BLOCK / kWave;
+    using TS = TileScan<BLOCK, V>;
+    struct Regs {
+        u32x4 x[V];
+    };
+    struct Cells {
+        uint32_t c[TS::NCELL];
+        uint32_t part;      // the head's prefix inside its (chunk row, wave) run
+        uint32_t pre;       // the tile's local prefix before the head
+    };
+
+    const uint32_t *ibase;  // virtual bases: address - head
+    uint32_t *obase;
+    uint64_t vlo, vhi, L;
+    uint32_t lg;            // log2 L when L is a power of two, else 64
+    uint32_t *sums;
+
+    // The head in tile t: its offset h (T when the tile holds none) and the
+    // segment it opens; elements before h belong to the segment before.
+    struct Head {
+        uint32_t h;
+        uint64_t seg;
+    };
+    __device__ __forceinline__ Head head(uint32_t t) const
+    {
+        const uint64_t vs = (uint64_t)t * T;
+        if (vs <= vlo)
+            return Head{(uint32_t)(vlo - vs), 0};       // element 0 opens segment 0
+        const uint64_t rel = vs - vlo;
+        const uint64_t s0 = lg < 64 ? rel >> lg : rel / L;
+        const uint64_t rem = rel - s0 * L;
+        if (rem == 0)
+            return Head{0, s0};
+        const uint64_t d = L - rem;                     // offset of the next head
+        return Head{d < T && vs + d < vhi ? (uint32_t)d : (uint32_t)T, s0 + 1};
+    }
+
+    __device__ __forceinline__ bool whole(uint32_t t) const
+    {
+        return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
+    }
+
+    __device__ __forceinline__ void load(Regs &r, uint32_t t) const
+    {
+        if (whole(t))
+            load_tile_full<BLOCK, V>(ibase, (uint64_t)t * T, r.x);
+        else
+            load_tile<BLOCK, V>(ibase, (uint64_t)t * T, vlo, vhi, r.x);
+    }
+
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
+    {
+        uint32_t w[V];
+        TS::local(r.x, w, c.c);
+        const uint32_t h = head(t).h;
+        if (h < T) {
+            const uint32_t q = h / 4, j = h % 4;
+            if (threadIdx.x == q % BLOCK) {
+                uint32_t part = 0;
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    if ((uint32_t)k == q / BLOCK) {
+                        const uint32_t in_chunk =
+                            j == 0 ? 0u : j == 1 ? r.x[k].x : j == 2 ? r.x[k].y : r.x[k].z;
+                        part = (w[k] - r.x[k].w) + in_chunk;
+                    }
+                }
+                c.part = part;
+            }
+        }
+    }
+
+    __device__ __forceinline__ TileInfo summary(Cells &c, uint32_t t) const
+    {
+        const uint32_t sum = TS::cells(c.c);
+        const uint32_t h = head(t).h;
+        if (h >= T)
+            return TileInfo{sum, false, true};
+        const uint32_t q = h / 4;
+        const uint32_t pre = c.c[(q / BLOCK) * NW + (q % BLOCK) / kWave] + c.part;
+        if (lane_id() == 0)
+            c.pre = pre;
+        return TileInfo{sum - pre, true, h > 0};
+    }
+
+    __device__ __forceinline__ void last(uint32_t, const TileInfo &) const {}
+
+    __device__ __forceinline__ void finish(Regs &r, Cells &c, uint32_t t, uint32_t carry) const
+    {
+        const Head hd = head(t);
+        const uint64_t vs = (uint64_t)t * T;
+        uint32_t w[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            w[k] = wave_incl_add(r.x[k].w);
+        if (hd.h >= T) {
+            TS::template apply<true>(r.x, w, c.c, carry);
+        } else {
+            const uint32_t pre = c.pre;
+            TS::template apply<true>(r.x, w, c.c, 0u);
+            const uint32_t restart = 0u - pre;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint32_t e0 = (uint32_t)(k * BLOCK + threadIdx.x) * 4;
+                r.x[k].x += e0 + 0 < hd.h ? carry : restart;
+                r.x[k].y += e0 + 1 < hd.h ? carry : restart;
+                r.x[k].z += e0 + 2 < hd.h ? carry : restart;
+                r.x[k].w += e0 + 3 < hd.h ? carry : restart;
+            }
+            // The segment before the head ends just before it.
+            if (sums && threadIdx.x == 0 && hd.h > 0 && hd.seg > 0)
+                sums[hd.seg - 1] = carry + pre;
+        }
+        if (sums) {
+            // The tile's last element ends its segment when the next element
+            // opens one or the array ends there.
+            const uint64_t end = vs + T < vhi ? vs + T : vhi;        // one past the last
+            const uint64_t rel = end - vlo;
+            const bool closes = end == vhi || (lg < 64 ? (rel & (L - 1)) == 0 : rel % L == 0);
+            const uint32_t e = (uint32_t)(end - vs - 1);
+            const uint32_t q = e / 4;
+            if (closes && threadIdx.x == q % BLOCK) {
+                const uint64_t seg = e >= hd.h ? hd.seg : hd.seg - 1;
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    if ((uint32_t)k == q / BLOCK) {
+                        const uint32_t j = e % 4;
+                        sums[seg] = j == 0 ? r.x[k].x : j == 1 ? r.x[k].y : j == 2 ? r.x[k].z : r.x[k].w;
+                    }
+                }
+            }
+        }
+        if (VEC_OUT) {
+            if (whole(t))
+                store_tile_full<BLOCK, V>(obase, vs, r.x);
+            else
+                store_tile<BLOCK, V>(obase, vs, vlo, vhi, r.x);
+        } else {
+            const uint64_t q0 = vs / 4 + threadIdx.x;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint64_t v0 = (q0 + (uint64_t)k * BLOCK) * 4;
+                const uint32_t vals[4] = {r.x[k].x, r.x[k].y, r.x[k].z, r.x[k].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (v0 + j >= vlo && v0 + j < vhi)
+                        obase[v0 + j] = vals[j];
+            }
+        }
+    }
+};
+
+template <int BLOCK, int V, bool VEC_OUT>
+__global__ __launch_bounds__(BLOCK) void segscan_long_kernel(const uint32_t *__restrict__ ibase,
+                                                             uint32_t *obase, uint64_t vlo,
+                                                             uint64_t vhi, uint64_t L, uint32_t lg,
+                                                             uint32_t ntiles, uint64_t *ticket,
+                                                             uint32_t *exits, uint64_t *desc,
+                                                             uint32_t *sums)
+{
+    SegLongOp<BLOCK, V, VEC_OUT> op{ibase, obase, vlo, vhi, L, lg, sums};
+    pipelined_chain(op, ntiles, ticket, exits, desc);
+}
+
 // Tile shape: 512 threads x 4 chunks, 8192 elements per tile (two tiles of
 // segmented-scan state fit in ~110 VGPRs, so two workgroups share a CU).
 // LIBSCAN_SEGSCAN_SHAPE=BxV picks another instantiated shape (a tuning knob;
@@ -408,6 +665,37 @@ static hipError_t launch_segscan_v(const uint32_t *in, uint32_t *out, uint64_t n
     div.shift = 18 + cl;
     div.mul = (uint32_t)(((1ull << div.shift) + l32 - 1) / l32);
     const bool small = seg_len < 4;
+    // Short power-of-two segments on 16-byte-aligned arrays: a segment is a
+    // group of lanes (256 x 8 = 8192 elements per workgroup).
+    if (head == 0 && vec_out && seg_len >= 4 && seg_len <= 256 && lg < 64) {
+        constexpr int LB = 256, LV = 8;
+        constexpr uint64_t TL = (uint64_t)LB * LV * 4;
+        const uint32_t grid = (uint32_t)((n + TL - 1) / TL);
+        auto lk = seg_len == 4 ? segscan_lanes_kernel<LB, LV, 1>
+                : seg_len == 8 ? segscan_lanes_kernel<LB, LV, 2>
+                : seg_len == 16 ? segscan_lanes_kernel<LB, LV, 4>
+                : seg_len == 32 ? segscan_lanes_kernel<LB, LV, 8>
+                : seg_len == 64 ? segscan_lanes_kernel<LB, LV, 16>
+                : seg_len == 128 ? segscan_lanes_kernel<LB, LV, 32>
+                                 : segscan_lanes_kernel<LB, LV, 64>;
+        hipLaunchKernelGGL(lk, dim3(grid), dim3(LB), 0, stream, in, out, n, seg_sums);
+        return hipGetLastError();
+    }
+    // Segments at least as long as the scan's tile (512 x 16 = 32768
+    // elements): at most one head per tile.
+    constexpr int SB = 512, SV = 16;
+    constexpr uint64_t TS = (uint64_t)SB * SV * 4;
+    if (seg_len >= TS) {
+        const uint64_t nts = tiles_for(n, head, TS);
+        auto sk = vec_out ? segscan_long_kernel<SB, SV, true> : segscan_long_kernel<SB, SV, false>;
+        uint64_t grid = (uint64_t)resident_grid((const void *)sk, SB);
+        if (grid > nts)
+            grid = nts;
+        hipLaunchKernelGGL(sk, dim3((uint32_t)grid), dim3(SB), 0, stream, ibase, obase,
+                           (uint64_t)head, n + head, seg_len, lg, (uint32_t)nts, s.ticket(),
+                           s.exits(), s.desc(), seg_sums);
+        return hipGetLastError();
+    }
     // Independent tiles (256 x 16 = 16384 elements each).
     constexpr uint64_t TI = 256 * 16 * 4;
     if (!small && TI % seg_len == 0 && head % seg_len == 0) {

@@ -102,3 +102,30 @@ def test_tile_boundaries_every_phase(offset, L):
     for n in (2 * 16384 - 1, 2 * 16384, 2 * 16384 + 3, 3 * 8192 + 1):
         a = workloads.small_random_u32(n, 41 + L + offset, high=1 << 16)
         check(a, L, offset=offset)
+
+
+# Short power-of-two segments on 16-byte-aligned arrays take the path where a
+# segment is a group of L/4 neighbouring lanes; every group size, ragged n
+# (a short last segment, a partial last workgroup of 8192 elements), in place.
+@pytest.mark.parametrize("L", [4, 8, 16, 32, 64, 128, 256])
+def test_lane_group_segments(L):
+    for n in (8192 * 3 + 5, 8192 * 2, 1000003, L - 1, 1):
+        a = workloads.small_random_u32(n, 500 + L, high=1 << 16)
+        check(a, L)
+    a = workloads.small_random_u32(65536 + 7, 600 + L)      # full-range values: sums wrap
+    check(a, L, in_place=True)
+
+
+# Segments at least as long as the 32768-element scan tile: at most one head
+# per tile.  Heads on tile boundaries (L a multiple of the tile), just past
+# them, inside tiles; the input in every 16-byte phase; an output in another
+# phase; in place.
+@pytest.mark.parametrize("L", [32768, 32769, 65536, 65535, 100003, 1 << 20])
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_long_segments(L, offset):
+    for n in (5 * 32768, 5 * 32768 + 3, 7 * 32768 - 1):
+        a = workloads.small_random_u32(n, 700 + L % 97 + offset, high=1 << 16)
+        check(a, L, offset=offset)
+    a = workloads.small_random_u32(4 * L + 12345, 800 + offset)
+    check(a, L, in_place=True, offset=offset)
+    check(a, L, offset=offset, out_offset=(offset + 2) % 4)
