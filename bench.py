@@ -160,17 +160,14 @@ def suite(args, torch, ps):
     every kernel runs at one size -- what the profile summaries group by."""
     out = []
 
-    def row(name, n, bytes_per_elem, fn, reps=20, warm=3, setup=None):
+    def row(name, n, bytes_per_elem, fn, reps=20, warm=3):
+        # Launches back to back, each bracketed by events on the stream: the
+        # host issues the next call while the GPU runs this one, so a launch's
+        # time is the GPU's, not the host's call overhead (except where a call
+        # is shorter than that overhead: the 2^16 rows are latencies).
         for _ in range(warm):
-            if setup:
-                setup()
             fn()
-        times = []
-        for _ in range(reps):
-            if setup:
-                setup()
-            t, _ = timed_launches(torch, fn, 1)
-            times.append(t[0])
+        times, _ = timed_launches(torch, fn, reps)
         med = float(np.median(times))
         rec = {"row": name, "n": n, "median_ms": round(med, 5), "min_ms": round(min(times), 5),
                "gelem_s": round(n / (med * 1e-3) / 1e9, 3),

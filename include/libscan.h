@@ -64,15 +64,16 @@ enum {
 
 /* Scan algorithms for scan_u32_ex. */
 enum {
-    LIBSCAN_ALGO_AUTO = 0,           /* LIBSCAN_ALGO_LOOKBACK */
+    LIBSCAN_ALGO_AUTO = 0,           /* LIBSCAN_ALGO_LOOKBACK_TILE up to 2^24 elements,
+                                        else LIBSCAN_ALGO_LOOKBACK (the faster of the
+                                        two at each size on MI355X) */
     LIBSCAN_ALGO_LOOKBACK = 1,       /* single pass, chained carry between tiles, on a
                                         grid-filling set of workgroups that hold two
                                         tiles each and take a tile's carry only after
                                         the next tile is loaded and published */
     LIBSCAN_ALGO_THREEPASS = 2,      /* reduce blocks / scan the sums / rescan blocks */
     LIBSCAN_ALGO_LOOKBACK_TILE = 3   /* single pass, one workgroup per tile that waits
-                                        for its carry right away (kept for
-                                        comparison) */
+                                        for its carry right away */
 };
 
 /* Text for a status code; for LIBSCAN_ERR_HIP, the text of the HIP error the
@@ -112,6 +113,7 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
  *              stream order; the call does not wait.
  * scratch      device scratch of at least scan_scratch_bytes(n) bytes.
  * stream       HIP stream.
+ * The algorithm is LIBSCAN_ALGO_AUTO's choice for n (see scan_u32_ex).
  * Errors: ERR_NULL (data NULL with n > 0, or scratch NULL with n > 0),
  * ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_SCRATCH, ERR_HIP.
  */

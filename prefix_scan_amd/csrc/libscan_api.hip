@@ -216,6 +216,8 @@ uint64_t op_identity64(int op)
     return id[op];
 }
 
+constexpr uint64_t kAutoTileMaxN = 1ull << 24;
+
 int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_depth,
                 uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
                 hipStream_t stream)
@@ -239,6 +241,12 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
                scan_ex_scratch_bytes(n, algo, fork_depth) - with_header(0), &s))
         return LIBSCAN_ERR_SCRATCH;
     uint32_t *tot = total_dev ? total_dev : s.total_slot();
+    // Automatic choice, from measurements on MI355X: up to 2^24 elements the
+    // grid that runs one tile per workgroup (512 x 32) finishes first -- too
+    // few tiles per workgroup for two in flight to pay (2^24: 27.7 against
+    // 31.3 us); from 2^25 on, the pipelined kernel (2^28: 342 against 407 us).
+    if (algo == LIBSCAN_ALGO_AUTO)
+        algo = n <= kAutoTileMaxN ? LIBSCAN_ALGO_LOOKBACK_TILE : LIBSCAN_ALGO_LOOKBACK;
     hipError_t e;
     if (algo == LIBSCAN_ALGO_THREEPASS) {
         const unsigned d = threepass_depth(n, fork_depth);
@@ -313,14 +321,14 @@ size_t scan_ex_scratch_bytes(uint64_t n, int algo, int fork_depth)
 int scan_exclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
                        void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    return scan_common(data, n, 0, LIBSCAN_ALGO_LOOKBACK, -1, total_host, total_dev, scratch,
+    return scan_common(data, n, 0, LIBSCAN_ALGO_AUTO, -1, total_host, total_dev, scratch,
                        scratch_bytes, stream);
 }
 
 int scan_inclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_t *total_dev,
                        void *scratch, size_t scratch_bytes, hipStream_t stream)
 {
-    return scan_common(data, n, 1, LIBSCAN_ALGO_LOOKBACK, -1, total_host, total_dev, scratch,
+    return scan_common(data, n, 1, LIBSCAN_ALGO_AUTO, -1, total_host, total_dev, scratch,
                        scratch_bytes, stream);
 }
 
