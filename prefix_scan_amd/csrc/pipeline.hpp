@@ -23,8 +23,9 @@
 // window: a round trip on the critical path.  Read late, it mostly holds a
 // prefix already.
 //
-// Tile numbers are drawn one at a time, so consecutive tiles go to different
-// workgroups that run side by side.  (Drawing several consecutive numbers
+// Tile numbers are drawn one at a time (but for each workgroup's first two,
+// drawn together), so consecutive tiles go to different workgroups that run
+// side by side.  (Drawing several consecutive numbers
 // per atomic would relieve the one contended ticket word, but it hands runs
 // of consecutive tiles to one workgroup, which then finishes them one after
 // another while the next workgroup waits on the last of them: the chain
@@ -177,11 +178,15 @@ __device__ __forceinline__ void pipelined_chain(Op &op, uint32_t ntiles, uint64_
     };
 
     if (threadIdx.x == kDrawer) {
+        // The first two tiles in one draw: every workgroup draws before its
+        // first load, and draws on the one ticket word are served one at a
+        // time (~14 ns each), so a second draw here would double the wait
+        // of the last workgroup to start (512 workgroups: ~14 against ~7 us).
         const uint64_t o1 =
-            __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(ticket, 2ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         epoch = (uint32_t)(o1 >> 32);
         const uint32_t c = tile_of((uint32_t)o1);
-        const uint32_t x = c != kNoTile ? tile_of(draw_num()) : kNoTile;
+        const uint32_t x = c != kNoTile ? tile_of((uint32_t)o1 + 1u) : kNoTile;
         s_cur = c;
         s_nxt = x;
         s_tag = (epoch & 0x3FFFFFFFu) << 2;
