@@ -236,9 +236,38 @@ __device__ __forceinline__ uint64_t dpp64_or(uint64_t x, uint64_t old)
 // Inclusive wave scan of u64 values under Op (the steps of wave_incl_add),
 // keeping operand order: lane l ends with x_0 op x_1 op .. op x_l, so Op
 // need not commute (the segmented pair of segflags_kernels.hip does not).
+// Inclusive wave scan of u64 values under wrapping add: each step one
+// carry-chained pair of DPP adds (low word, then high word with the carry).
+// Lanes whose source lies outside the row, or in a masked row, are disabled
+// for both instructions of the step and keep their value (x + 0).  Each step
+// starts with two wait states, which a DPP read of a VGPR written by the
+// instruction before it needs.
+#define LIBSCAN_DPP64_STEP(CTRL, RMASK)                                              \
+    "s_nop 1\n"                                                                      \
+    "v_add_co_u32_dpp %0, vcc, %0, %0 " CTRL " row_mask:" RMASK " bank_mask:0xf\n"    \
+    "v_addc_co_u32_dpp %1, vcc, %1, %1, vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
+__device__ __forceinline__ uint64_t wave_incl64_add(uint64_t x)
+{
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    asm volatile(LIBSCAN_DPP64_STEP("row_shr:1", "0xf")
+                 LIBSCAN_DPP64_STEP("row_shr:2", "0xf")
+                 LIBSCAN_DPP64_STEP("row_shr:4", "0xf")
+                 LIBSCAN_DPP64_STEP("row_shr:8", "0xf")
+                 LIBSCAN_DPP64_STEP("row_bcast:15", "0xa")
+                 LIBSCAN_DPP64_STEP("row_bcast:31", "0xc")
+                 "s_nop 1\n"
+                 : "+v"(lo), "+v"(hi)
+                 :
+                 : "vcc");
+    return ((uint64_t)hi << 32) | lo;
+}
+#undef LIBSCAN_DPP64_STEP
+
 template <class Op>
 __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
 {
+    if constexpr (__is_same(Op, OpAdd64))
+        return wave_incl64_add(x);
     constexpr uint64_t e = Op::identity;
     x = Op::apply(dpp64_or<kDppRowShr1, 0xF>(x, e), x);
     x = Op::apply(dpp64_or<kDppRowShr2, 0xF>(x, e), x);
