@@ -140,6 +140,27 @@ struct ScanOp64 {
         TS::local(r.x, w, c.c);
     }
 
+    // Loads and reduces a tile in one call, so the driver reads the carry's
+    // first look-back window once the tile's loads have landed.
+    static constexpr bool kLoadLocal = true;
+    template <class R>
+    __device__ __forceinline__ void load_local(Regs &r, Cells &c, uint32_t t, R &&ready) const
+    {
+        if (whole(t)) {
+            load_tile_full<BLOCK, V>(reinterpret_cast<const uint32_t *>(abase), (uint64_t)t * T * 2,
+                                     r.x);
+            ready(r.x[V - 1].x);
+            local(r, c, t);
+        } else {
+            const uint64_t q0 = (uint64_t)t * T / 2 + threadIdx.x;
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                r.x[k] = load2_guarded64(abase, q0 + (uint64_t)k * BLOCK, vlo, vhi, M::identity);
+            ready(0u);
+            local(r, c, t);
+        }
+    }
+
     __device__ __forceinline__ TileInfoT<uint64_t> summary(Cells &c, uint32_t) const
     {
         return TileInfoT<uint64_t>{TS::cells(c.c), false, true};
