@@ -39,6 +39,31 @@ __device__ __forceinline__ uint32_t pair_c(uint64_t p) { return (uint32_t)(p >> 
 __device__ __forceinline__ uint32_t pair_v(uint64_t p) { return (uint32_t)p; }
 __device__ __forceinline__ uint64_t make_pair(uint32_t c, uint32_t v) { return ((uint64_t)c << 32) | v; }
 
+// One step of the pairs' inclusive wave scan, in 32-bit halves: the counts
+// add (one DPP add), and a sum takes the piece before it only where its own
+// count is 0.  Lanes with no source lane read the identity (0, 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void pair_step(uint32_t &c, uint32_t &v)
+{
+    const uint32_t pv = dpp<CTRL, ROW_MASK>(v);
+    const uint32_t pc = dpp<CTRL, ROW_MASK>(c);
+    v = c ? v : v + pv;
+    c += pc;
+}
+
+// Inclusive wave scan of pairs under SegPair (the steps of wave_incl_add).
+__device__ __forceinline__ uint64_t wave_incl_pair(uint64_t x)
+{
+    uint32_t c = pair_c(x), v = pair_v(x);
+    pair_step<kDppRowShr1, 0xF>(c, v);
+    pair_step<kDppRowShr2, 0xF>(c, v);
+    pair_step<kDppRowShr4, 0xF>(c, v);
+    pair_step<kDppRowShr8, 0xF>(c, v);
+    pair_step<kDppRowBcast15, 0xA>(c, v);
+    pair_step<kDppRowBcast31, 0xC>(c, v);
+    return make_pair(c, v);
+}
+
 template <int BLOCK_, int V, bool VEC_FLAGS, bool VEC_OUT>
 struct SegFlagsOp {
     static constexpr int BLOCK = BLOCK_;
@@ -163,7 +188,7 @@ struct SegFlagsOp {
         uint64_t w[V];
 #pragma unroll
         for (int k = 0; k < V; ++k)
-            w[k] = wave_incl64<SegPair>(chunk_scan(r.x[k], (r.hb >> (4 * k)) & 15u));
+            w[k] = wave_incl_pair(chunk_scan(r.x[k], (r.hb >> (4 * k)) & 15u));
         if (lane_id() == kWave - 1) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
@@ -184,7 +209,7 @@ struct SegFlagsOp {
             v[j] = i < (uint32_t)NCELL ? c.c[i] : SegPair::identity;
             mine = SegPair::apply(mine, v[j]);
         }
-        const uint64_t incl = wave_incl64<SegPair>(mine);
+        const uint64_t incl = wave_incl_pair(mine);
         uint64_t run = wave_shr1_64<SegPair>(incl);
 #pragma unroll
         for (int j = 0; j < CELLS_PER_LANE; ++j) {
@@ -214,7 +239,7 @@ struct SegFlagsOp {
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             const uint32_t bits = (r.hb >> (4 * k)) & 15u;
-            const uint64_t w = wave_incl64<SegPair>(
+            const uint64_t w = wave_incl_pair(
                 make_pair((uint32_t)__builtin_popcount(bits), r.x[k].w));
             // Everything before this chunk: the tiles before, the runs of
             // chunks before in this tile, the lanes before in this wave.
