@@ -265,16 +265,21 @@ __global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__res
     const uint32_t tile = blockIdx.x;
     const uint64_t vstart = (uint64_t)tile * T;
     u32x4 x[V];
-    load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, x);
     // 16 counters as four words of four 8-bit fields.
     uint32_t c[4] = {0u, 0u, 0u, 0u};
+    // Whole tiles skip the per-key range checks.
+    const bool whole = vstart >= vlo && vstart + T <= vhi;
+    if (whole)
+        load_tile_full<BLOCK, V>(kbase, vstart, x);
+    else
+        load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, x);
 #pragma unroll
     for (int k = 0; k < V; ++k) {
         const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
         const uint32_t kk[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (v0 + j < vlo || v0 + j >= vhi)
+            if (!whole && (v0 + j < vlo || v0 + j >= vhi))
                 continue;
             const uint32_t d = (kk[j] >> shift) & 15u;
             const uint32_t inc = 1u << ((d & 3u) * 8u);
