@@ -151,9 +151,13 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(const uint32_t *__restri
     pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
-// Tile shape: 512 threads x 8 chunks, 16384 flags per tile (64 KiB of staged
-// indices).  LIBSCAN_COMPACT_SHAPE=BxV picks another instantiated shape (a
-// tuning knob; it never changes a result).
+// Tile shape: 1024 threads x 8 chunks, 32768 flags per tile (64 KiB of
+// staged indices), one workgroup per CU.  Two workgroups of 512 x 8 hold
+// the same registers and data in flight but draw twice as many tiles from
+// the one ticket word, whose draws are served one at a time: their first
+// draws alone keep the last workgroup waiting ~7 µs.
+// LIBSCAN_COMPACT_SHAPE=BxV picks another instantiated shape (a tuning knob;
+// it never changes a result).
 struct CompactShape {
     int block, chunks;
 };
@@ -161,10 +165,10 @@ struct CompactShape {
 static CompactShape compact_shape()
 {
     static CompactShape sh = [] {
-        CompactShape r{512, 8};
+        CompactShape r{1024, 8};
         if (const char *e = getenv("LIBSCAN_COMPACT_SHAPE"))
             if (sscanf(e, "%dx%d", &r.block, &r.chunks) != 2)
-                r = CompactShape{512, 8};
+                r = CompactShape{1024, 8};
         return r;
     }();
     return sh;
@@ -202,9 +206,11 @@ hipError_t launch_compact(const int32_t *flags, int32_t *out, uint64_t n, const 
         return launch_compact_v<256, 8>(flags, out, n, s, count_out, stream);
     if (sh.block == 256 && sh.chunks == 16)
         return launch_compact_v<256, 16>(flags, out, n, s, count_out, stream);
+    if (sh.block == 512 && sh.chunks == 8)
+        return launch_compact_v<512, 8>(flags, out, n, s, count_out, stream);
     if (sh.block == 512 && sh.chunks == 16)
         return launch_compact_v<512, 16>(flags, out, n, s, count_out, stream);
-    return launch_compact_v<512, 8>(flags, out, n, s, count_out, stream);
+    return launch_compact_v<1024, 8>(flags, out, n, s, count_out, stream);
 }
 
 }  // namespace libscan

@@ -33,9 +33,10 @@ namespace libscan {
 // Digit passes: 256 threads x 4 chunks, 4096 keys per tile.
 constexpr int kRadixChunks = 4;
 constexpr uint64_t kRadixTile = (uint64_t)kBlock * kRadixChunks * 4;
-// One-bit passes: 512 threads x 4 chunks, 8192 keys per tile (two tiles of
-// pairs in flight per workgroup).
-constexpr int kR1Block = 512;
+// One-bit passes: 1024 threads x 4 chunks, 16384 keys per tile (two tiles
+// of pairs in flight per workgroup, one workgroup per CU: two of 512 threads
+// hold as much but draw twice as many tiles from the one ticket word).
+constexpr int kR1Block = 1024;
 constexpr int kR1Chunks = 4;
 constexpr uint64_t kR1Tile = (uint64_t)kR1Block * kR1Chunks * 4;
 
@@ -235,7 +236,8 @@ struct Radix1Op {
     }
 };
 
-// Four waves per SIMD: two 512-thread workgroups per CU (128 VGPRs each).
+// Four waves per SIMD (128 VGPRs; two 8-byte values spill around the tile
+// loop).
 template <int BLOCK, int V, bool FIRST, bool LAST>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void radix1_pass_kernel(
     const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,

@@ -13,7 +13,7 @@
 // element, how many segments started up to it (so the segment's number) and
 // the sum since the last start.  It runs on the pipelined chained-carry
 // driver with the pair as a two-word carry (Carry64 keeps operand order).
-// Tiles of 512 threads x 8 chunks (16384 elements) hold the values and the
+// Tiles of 1024 threads x 8 chunks (32768 elements) hold the values and the
 // flags as 4 bits per chunk.  A segment's total is written where the next
 // segment starts (the pair just before the start) and, for the last
 // segment, by the last tile.  12 bytes per element (value, flag, output)
@@ -285,8 +285,8 @@ struct SegFlagsOp {
     }
 };
 
-// Four waves per SIMD: two 512-thread workgroups per CU (128 registers, a
-// few spilled), 2.7% faster than one workgroup per CU at 135.
+// Four waves per SIMD (128 registers, a few 8-byte values spilled around
+// the tile loop): 2.7% faster than 135 registers and two waves per SIMD.
 template <int BLOCK, int V, bool VEC_FLAGS, bool VEC_OUT>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void segflags_kernel(const uint32_t *vbase, const uint32_t *fbase,
                                                          uint32_t *obase, uint64_t vlo, uint64_t vhi,
@@ -298,7 +298,10 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     pipelined_chain(op, ntiles, ticket, exits, desc);
 }
 
-constexpr int kSegfBlock = 512;
+// 1024 threads x 8 chunks, 32768 elements per tile, one workgroup per CU
+// (as many registers and bytes in flight as two workgroups of 512, half the
+// tile draws from the one ticket word).
+constexpr int kSegfBlock = 1024;
 constexpr int kSegfChunks = 8;
 constexpr uint64_t kSegfTile = (uint64_t)kSegfBlock * kSegfChunks * 4;
 

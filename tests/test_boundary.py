@@ -249,6 +249,6 @@ def test_segscan_flags_argument_errors():
                                FAKE, big, NULLP) == ps.ERR_ALIGN
     assert L.segscan_flags_u32(FAKE, FAKE, FAKE, 1 << 26, NULLP, NOHOST, NULLP, FAKE,
                                L.segscan_flags_scratch_bytes(1 << 26) - 300, NULLP) == ps.ERR_SCRATCH
-    # two descriptor words per 16384-element tile
-    assert L.segscan_flags_scratch_bytes(1 << 26) >= ((1 << 26) // 16384) * 16
+    # two descriptor words per 32768-element tile
+    assert L.segscan_flags_scratch_bytes(1 << 26) >= ((1 << 26) // 32768) * 16
     assert L.segscan_flags_u32(NULLP, NULLP, NULLP, 0, NULLP, NOHOST, NULLP, NULLP, 0, NULLP) == ps.OK

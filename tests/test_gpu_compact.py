@@ -49,7 +49,8 @@ def test_workload_2p26(p):
     assert np.array_equal(to_host_i32(out)[:cref], kept.astype(np.int32))
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 5, 64, 1000, 8191, 8192, 8193, 16385, 100003, (1 << 20) + 3])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 64, 1000, 8191, 8192, 8193, 16385, 32767, 32768, 32769,
+                               100003, (1 << 20) + 3])
 @pytest.mark.parametrize("p", [0.3, 0.97])
 def test_ragged(n, p):
     check(workloads.bernoulli_flags(n, p, n + int(100 * p)))
@@ -94,7 +95,7 @@ def test_repeated_calls():
 @pytest.mark.parametrize("p", [0.5, 0.03, 0.97])
 def test_unaligned_output(out_offset, p):
     # Kept and -1 runs start at every 16-byte phase of the output, through
-    # tile boundaries (16384-flag tiles) and a ragged tail.
-    flags = workloads.bernoulli_flags(3 * 16384 + 77, p, 17 + out_offset)
+    # tile boundaries (32768-flag tiles) and a ragged tail.
+    flags = workloads.bernoulli_flags(3 * 32768 + 77, p, 17 + out_offset)
     check(flags, offset=0, out_offset=out_offset)
     check(flags, offset=(out_offset + 1) % 4, out_offset=out_offset)

@@ -38,7 +38,8 @@ def test_workload_2p25(kind):
     check(keys, 4, ref=ref)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 100, 4095, 4096, 4097, 12345, 65537, 300001])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 100, 4095, 4096, 4097, 12345, 16384, 16385, 65537,
+                               300001])
 def test_ragged(n):
     keys = workloads.small_random_u32(n, n)
     check(keys, 1)

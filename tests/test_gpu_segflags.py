@@ -37,7 +37,7 @@ def test_workload_full_size(mean):
     run(a, f)
 
 
-@pytest.mark.parametrize("n", [1, 2, 5, 4097, 16384, 16385, 3 * (1 << 18) + 5])
+@pytest.mark.parametrize("n", [1, 2, 5, 4097, 16384, 16385, 32768, 32769, 3 * (1 << 18) + 5])
 @pytest.mark.parametrize("p", [0.0, 0.03, 0.5, 1.0])
 def test_ragged_sizes_and_densities(n, p):
     a = workloads.small_random_u32(n, 100 + n)
