@@ -191,12 +191,64 @@ __device__ __forceinline__ uint32_t dpp_or(uint32_t x, uint32_t old)
     return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
 }
 
+// Operators whose identity is not 0 take their DPP steps as | or unsigned
+// max on the words XORed with a mask: a & b = ~(~a | ~b), min(a, b) =
+// ~max(~a, ~b), and flipping the sign bit maps signed order onto unsigned
+// order (flipping the other 31 bits too reverses it).  The mask maps 0 to
+// the operator's identity.  Under identity 0 each step is one DPP
+// instruction whose disabled lanes read 0 (bound_ctrl), with no register
+// holding the identity; & otherwise takes a DPP move and a separate and per
+// step, and the scans of &, min and signed min and max spilled.
+template <class Op>
+struct DppFlip {
+    using Base = Op;
+    static constexpr uint32_t mask = 0u;
+};
+template <>
+struct DppFlip<OpAnd> {
+    using Base = OpOr;
+    static constexpr uint32_t mask = 0xFFFFFFFFu;
+};
+template <>
+struct DppFlip<OpMin> {
+    using Base = OpMax;
+    static constexpr uint32_t mask = 0xFFFFFFFFu;
+};
+template <>
+struct DppFlip<OpMinS> {
+    using Base = OpMax;
+    static constexpr uint32_t mask = 0x7FFFFFFFu;
+};
+template <>
+struct DppFlip<OpMaxS> {
+    using Base = OpMax;
+    static constexpr uint32_t mask = 0x80000000u;
+};
+
+// x XOR Op's flip mask, opaque to the compiler: it would otherwise fold the
+// flips into the steps between them (& would turn back into & steps).
+template <class Op>
+__device__ __forceinline__ uint32_t dpp_flip(uint32_t x)
+{
+    constexpr uint32_t kMask = DppFlip<Op>::mask;
+    uint32_t y;
+    if constexpr (kMask == 0xFFFFFFFFu)
+        asm("v_not_b32 %0, %1" : "=v"(y) : "v"(x));
+    else
+        asm("v_xor_b32 %0, %2, %1" : "=v"(y) : "v"(x), "n"(kMask));
+    return y;
+}
+
 // Inclusive wave scan under Op (the same steps as wave_incl_add).
 template <class Op>
 __device__ __forceinline__ uint32_t wave_incl(uint32_t x)
 {
+    constexpr uint32_t kFlip = DppFlip<Op>::mask;
     if constexpr (__is_same(Op, OpAdd)) {
         return wave_incl_add(x);
+    } else if constexpr (kFlip != 0u) {
+        static_assert((kFlip ^ DppFlip<Op>::Base::identity) == Op::identity, "mask maps identities");
+        return dpp_flip<Op>(wave_incl<typename DppFlip<Op>::Base>(dpp_flip<Op>(x)));
     } else {
         constexpr uint32_t e = Op::identity;
         x = Op::apply(x, dpp_or<kDppRowShr1, 0xF>(x, e));
@@ -220,7 +272,11 @@ __device__ __forceinline__ uint32_t wave_fold(uint32_t x)
 template <class Op>
 __device__ __forceinline__ uint32_t wave_shr1_op(uint32_t x)
 {
-    return dpp_or<kDppWaveShr1, 0xF>(x, Op::identity);
+    constexpr uint32_t kFlip = DppFlip<Op>::mask;
+    if constexpr (kFlip != 0u)
+        return dpp_flip<Op>(dpp_or<kDppWaveShr1, 0xF>(dpp_flip<Op>(x), 0u));
+    else
+        return dpp_or<kDppWaveShr1, 0xF>(x, Op::identity);
 }
 
 // 64-bit lanes: each DPP step moves the two halves with the same control,
@@ -351,9 +407,9 @@ __device__ __forceinline__ void store4(uint32_t *abase, uint64_t q, u32x4 v)
 
 // Chunk q with every element outside [vlo, vhi) read as 0.
 __device__ __forceinline__ u32x4 load4_guarded(const uint32_t *abase, uint64_t q, uint64_t vlo,
-                                               uint64_t vhi)
+                                               uint64_t vhi, uint32_t fill = 0u)
 {
-    u32x4 r = {0u, 0u, 0u, 0u};
+    u32x4 r = {fill, fill, fill, fill};
     const uint64_t v0 = q * 4;
     if (v0 >= vlo && v0 + 4 <= vhi)
         return load4(abase, q);
@@ -430,7 +486,7 @@ __device__ __forceinline__ void load_tile_full_or(const uint32_t *abase, uint64_
 // Any tile: whole tiles take the plain path, partial ones per-element guards.
 template <int BLOCK, int V>
 __device__ __forceinline__ void load_tile(const uint32_t *abase, uint64_t vstart, uint64_t vlo,
-                                          uint64_t vhi, u32x4 (&x)[V])
+                                          uint64_t vhi, u32x4 (&x)[V], uint32_t fill = 0u)
 {
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     if (vstart >= vlo && vstart + T <= vhi) {
@@ -439,7 +495,7 @@ __device__ __forceinline__ void load_tile(const uint32_t *abase, uint64_t vstart
         const uint64_t q0 = vstart / 4 + threadIdx.x;
 #pragma unroll
         for (int k = 0; k < V; ++k)
-            x[k] = load4_guarded(abase, q0 + (uint64_t)k * BLOCK, vlo, vhi);
+            x[k] = load4_guarded(abase, q0 + (uint64_t)k * BLOCK, vlo, vhi, fill);
     }
 }
 
@@ -537,13 +593,16 @@ struct TileScan {
     // their exclusive scan; returns the tile's fold in every lane.
     __device__ static __forceinline__ uint32_t cells(uint32_t *s_cell)
     {
-        const uint32_t lane = lane_id();
+        // The mask tells the compiler lane < 64, so when the cells fill the
+        // wave exactly the range checks fold away (no divergent reads).
+        constexpr bool kExact = NCELL % kWave == 0;
+        const uint32_t lane = lane_id() & (kWave - 1u);
         uint32_t v[CELLS_PER_LANE];
         uint32_t mine = Op::identity;
 #pragma unroll
         for (int j = 0; j < CELLS_PER_LANE; ++j) {
             const uint32_t c = lane * CELLS_PER_LANE + j;
-            v[j] = c < (uint32_t)NCELL ? s_cell[c] : Op::identity;
+            v[j] = (kExact || c < (uint32_t)NCELL) ? s_cell[c] : Op::identity;
             mine = Op::apply(mine, v[j]);
         }
         const uint32_t incl = wave_incl<Op>(mine);
@@ -555,7 +614,7 @@ struct TileScan {
 #pragma unroll
         for (int j = 0; j < CELLS_PER_LANE; ++j) {
             const uint32_t c = lane * CELLS_PER_LANE + j;
-            if (c < (uint32_t)NCELL)
+            if (kExact || c < (uint32_t)NCELL)
                 s_cell[c] = run;
             run = Op::apply(run, v[j]);
         }

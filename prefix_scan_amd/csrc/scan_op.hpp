@@ -40,31 +40,17 @@ struct ScanOp {
         return (uint64_t)t * T >= vlo && (uint64_t)t * T + T <= vhi;
     }
 
+    // Slots outside the array read as the operator's identity.
     __device__ __forceinline__ void load(Regs &r, uint32_t t) const
     {
         if (whole(t))
             load_tile_full<BLOCK, V>(abase, (uint64_t)t * T, r.x);
         else
-            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
+            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x, M::identity);
     }
 
-    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
+    __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t) const
     {
-        if constexpr (M::identity != 0u) {
-            // The guarded loads read slots outside the array as 0; under an
-            // operator whose identity is not 0 they must hold the identity.
-            if (!whole(t)) {
-                const uint64_t vs = (uint64_t)t * T;
-#pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const uint64_t v0 = vs + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
-                    if (!(v0 + 0 >= vlo && v0 + 0 < vhi)) r.x[k].x = M::identity;
-                    if (!(v0 + 1 >= vlo && v0 + 1 < vhi)) r.x[k].y = M::identity;
-                    if (!(v0 + 2 >= vlo && v0 + 2 < vhi)) r.x[k].z = M::identity;
-                    if (!(v0 + 3 >= vlo && v0 + 3 < vhi)) r.x[k].w = M::identity;
-                }
-            }
-        }
         uint32_t w[V];
         TS::local(r.x, w, c.c);
     }
@@ -82,7 +68,7 @@ struct ScanOp {
             ready(r.x[V - 1].x);
             local(r, c, t);
         } else {
-            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x);
+            load_tile<BLOCK, V>(abase, (uint64_t)t * T, vlo, vhi, r.x, M::identity);
             ready(0u);
             local(r, c, t);
         }
