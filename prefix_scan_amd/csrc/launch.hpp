@@ -62,6 +62,8 @@ struct Scratch {
 // pipelined: the grid-filling two-tile kernel; else one workgroup per tile.
 hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
                                 const Scratch &s, uint32_t *total_out, hipStream_t stream);
+hipError_t launch_scan_table(uint32_t *data, uint64_t n, const Scratch &s, uint32_t *total_out,
+                             hipStream_t stream);
 int resident_grid(const void *kernel, int block);
 size_t scan_lookback_body_bytes(uint64_t n, uint32_t head);
 

@@ -323,6 +323,15 @@ hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool
                      : scan_lookback_v<512, 32>(data, n, inclusive, false, s, total_out, stream);
 }
 
+// An exclusive scan of a table of a few hundred thousand entries (the four-bit
+// sort's digit-major counts): one-tile kernel on 32 KiB tiles, so the 512
+// KiB table spreads over 16 workgroups rather than 2 (3.2% on the 2^25 sort).
+hipError_t launch_scan_table(uint32_t *data, uint64_t n, const Scratch &s, uint32_t *total_out,
+                             hipStream_t stream)
+{
+    return scan_lookback_v<256, 8>(data, n, false, false, s, total_out, stream);
+}
+
 // The three-pass scheme's own tile: 256 threads x 4 chunks.
 constexpr int kTpChunks = 4;
 
