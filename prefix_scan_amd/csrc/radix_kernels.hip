@@ -301,11 +301,16 @@ __global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__res
         }
     }
     const uint32_t wave = threadIdx.x / kWave;
+    // Two digits per wave sum, as 16-bit fields (at most 64 x 255 per field).
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-        const uint32_t t = wave_sum((c[d >> 2] >> ((d & 3) * 8)) & 0xFFu);
-        if (lane_id() == 0)
-            s_part[wave][d] = t;
+    for (int d = 0; d < 16; d += 2) {
+        const uint32_t lo = (c[d >> 2] >> ((d & 3) * 8)) & 0xFFu;
+        const uint32_t hi = (c[(d + 1) >> 2] >> (((d + 1) & 3) * 8)) & 0xFFu;
+        const uint32_t t = wave_sum(lo | (hi << 16));
+        if (lane_id() == 0) {
+            s_part[wave][d] = t & 0xFFFFu;
+            s_part[wave][d + 1] = t >> 16;
+        }
     }
     __syncthreads();
     if (threadIdx.x < 16) {
