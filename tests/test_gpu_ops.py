@@ -6,8 +6,8 @@ the carry between tiles is never trivially saturated: uniform values for
 xor; odd values for mul (even ones drive products to 0); a rising / falling
 trend for max / min; bits that first appear (or clear) slowly along the
 array for or / and.  Uniform values are run for every operator as well.
-Sizes: one tile, ragged multi-tile arrays with unaligned starts, 2^24 and
-the 2^28 headline size.
+Sizes: one tile, ragged multi-tile arrays with unaligned starts, 2^24, a
+ragged 2^25 + 4099 (the pipelined kernel) and the 2^28 headline size.
 """
 import numpy as np
 import pytest
@@ -66,6 +66,15 @@ def test_scan_op_uniform(op):
     a = np.random.default_rng(3).integers(0, 2**32, (1 << 20) + 333, dtype=np.uint32)
     check_scan(a, op, False, 3)
     check_scan(a, op, True, 0)
+
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_scan_op_pipelined(op, inclusive):
+    # Above 2^24 elements the scan runs the pipelined two-tile kernel: many
+    # tiles per workgroup, a ragged last tile and an unaligned start.
+    n = (1 << 25) + 4099
+    check_scan(shaped(op, n, 41), op, inclusive, 3 if inclusive else 1)
 
 
 @pytest.mark.parametrize("op", ["xor", "max", "mul", "min_s"])
