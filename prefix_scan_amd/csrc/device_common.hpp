@@ -305,7 +305,7 @@ __device__ __forceinline__ uint64_t dpp64_or(uint64_t x, uint64_t old)
 __device__ __forceinline__ uint64_t wave_incl64_add(uint64_t x)
 {
     uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-    asm volatile(LIBSCAN_DPP64_STEP("row_shr:1", "0xf")
+    asm(LIBSCAN_DPP64_STEP("row_shr:1", "0xf")
                  LIBSCAN_DPP64_STEP("row_shr:2", "0xf")
                  LIBSCAN_DPP64_STEP("row_shr:4", "0xf")
                  LIBSCAN_DPP64_STEP("row_shr:8", "0xf")
@@ -318,6 +318,35 @@ __device__ __forceinline__ uint64_t wave_incl64_add(uint64_t x)
     return ((uint64_t)hi << 32) | lo;
 }
 #undef LIBSCAN_DPP64_STEP
+
+// Two such scans interleaved step by step: each step's four instructions
+// put three others between every DPP read and the write of its register in
+// the step before, more than the two wait states it needs, so only the first
+// step waits.
+#define LIBSCAN_DPP64_STEP2(CTRL, RMASK)                                             \
+    "v_add_co_u32_dpp %0, vcc, %0, %0 " CTRL " row_mask:" RMASK " bank_mask:0xf\n"    \
+    "v_addc_co_u32_dpp %1, vcc, %1, %1, vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n" \
+    "v_add_co_u32_dpp %2, vcc, %2, %2 " CTRL " row_mask:" RMASK " bank_mask:0xf\n"    \
+    "v_addc_co_u32_dpp %3, vcc, %3, %3, vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
+__device__ __forceinline__ void wave_incl64_add2(uint64_t &a, uint64_t &b)
+{
+    uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32);
+    uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+    asm("s_nop 1\n"
+        LIBSCAN_DPP64_STEP2("row_shr:1", "0xf")
+        LIBSCAN_DPP64_STEP2("row_shr:2", "0xf")
+        LIBSCAN_DPP64_STEP2("row_shr:4", "0xf")
+        LIBSCAN_DPP64_STEP2("row_shr:8", "0xf")
+        LIBSCAN_DPP64_STEP2("row_bcast:15", "0xa")
+        LIBSCAN_DPP64_STEP2("row_bcast:31", "0xc")
+        "s_nop 1\n"
+        : "+v"(alo), "+v"(ahi), "+v"(blo), "+v"(bhi)
+        :
+        : "vcc");
+    a = ((uint64_t)ahi << 32) | alo;
+    b = ((uint64_t)bhi << 32) | blo;
+}
+#undef LIBSCAN_DPP64_STEP2
 
 template <class Op>
 __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
@@ -332,6 +361,25 @@ __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
     x = Op::apply(dpp64_or<kDppRowBcast15, 0xA>(x, e), x);
     x = Op::apply(dpp64_or<kDppRowBcast31, 0xC>(x, e), x);
     return x;
+}
+
+// Inclusive wave scans of V values under Op, two at a time for u64 add.
+template <class Op, int V>
+__device__ __forceinline__ void wave_incl64_n(const uint64_t (&e)[V], uint64_t (&w)[V])
+{
+    if constexpr (__is_same(Op, OpAdd64) && V % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < V; k += 2) {
+            uint64_t a = e[k], b = e[k + 1];
+            wave_incl64_add2(a, b);
+            w[k] = a;
+            w[k + 1] = b;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            w[k] = wave_incl64<Op>(e[k]);
+    }
 }
 
 // Op with its operands swapped.

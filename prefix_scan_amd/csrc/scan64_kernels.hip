@@ -38,13 +38,14 @@ struct TileScan64 {
                                                  uint64_t *s_cell)
     {
         const uint32_t wave = threadIdx.x / kWave;
+        uint64_t e[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            const uint64_t e1 = Op::apply(chunk_lo64(x[k]), chunk_hi64(x[k]));
-            x[k].z = (uint32_t)e1;
-            x[k].w = (uint32_t)(e1 >> 32);
-            w[k] = wave_incl64<Op>(e1);
+            e[k] = Op::apply(chunk_lo64(x[k]), chunk_hi64(x[k]));
+            x[k].z = (uint32_t)e[k];
+            x[k].w = (uint32_t)(e[k] >> 32);
         }
+        wave_incl64_n<Op, V>(e, w);
         if (lane_id() == kWave - 1) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
@@ -175,10 +176,11 @@ struct ScanOp64 {
     {
         // The wave prefix of the chunk folds is rebuilt rather than held
         // across the step (2 V registers less per tile).
-        uint64_t w[V];
+        uint64_t e[V], w[V];
 #pragma unroll
         for (int k = 0; k < V; ++k)
-            w[k] = wave_incl64<M>(chunk_hi64(r.x[k]));
+            e[k] = chunk_hi64(r.x[k]);
+        wave_incl64_n<M, V>(e, w);
         TS::template apply<INCL>(r.x, w, c.c, carry);
         if (whole(t)) {
             store_tile_full<BLOCK, V>(reinterpret_cast<uint32_t *>(abase), (uint64_t)t * T * 2, r.x);
