@@ -755,9 +755,22 @@ struct LookbackWindow {
     bool before_start;
 };
 
+// The lane number, computed afresh where it is used.  In a kernel at its
+// register limit, a loop-invariant copy (or a 64-bit value derived from it)
+// held across the tile loop is what the allocator spills first, and the
+// reload then waits for every load and store the wave has in flight (the
+// one-bit radix pass: +3.3%).
+__device__ __forceinline__ uint32_t lane_id_here()
+{
+    uint32_t l = lane_id();
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+template <bool FRESH_LANE = false>
 __device__ __forceinline__ LookbackWindow lookback_load(const uint64_t *desc, int64_t base)
 {
-    const int64_t pi = base - (int64_t)lane_id();
+    const int64_t pi = base - (int64_t)(FRESH_LANE ? lane_id_here() : lane_id());
     LookbackWindow w;
     w.before_start = pi < 0;
     w.d = __hip_atomic_load(desc + (pi < 0 ? 0 : pi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -792,7 +805,7 @@ __device__ __forceinline__ int lookback_fold(const LookbackWindow &w, uint32_t t
 // the window for base = tile - 1, which a caller may have loaded early.  The
 // first window is folded outside the retry loop, so waiting for it does not
 // wait for loads the caller issued after it.
-template <class Op = OpAdd>
+template <class Op = OpAdd, bool FRESH_LANE = false>
 __device__ __forceinline__ uint32_t lookback_from(const uint64_t *desc, uint32_t tile,
                                                   uint32_t tag, LookbackWindow w)
 {
@@ -804,7 +817,7 @@ __device__ __forceinline__ uint32_t lookback_from(const uint64_t *desc, uint32_t
             base -= kWave;
         else
             __builtin_amdgcn_s_sleep(1);
-        w = lookback_load(desc, base);
+        w = lookback_load<FRESH_LANE>(desc, base);
         r = lookback_fold<Op>(w, tag, excl);
     }
     return excl;

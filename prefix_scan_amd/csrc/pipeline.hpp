@@ -83,7 +83,7 @@ using TileInfo = TileInfoT<uint32_t>;
 // How a carry of the monoid M travels between tiles: a u32 value in one
 // descriptor word per tile (M must commute: the look-back folds nearer tiles
 // first), or a u64 value in two (operand order kept, any associative M).
-template <class M>
+template <class M, bool FRESH_LANE = false>
 struct Carry32 {
     using T = uint32_t;
     using Window = LookbackWindow;
@@ -96,12 +96,12 @@ struct Carry32 {
     }
     __device__ static __forceinline__ Window load(const uint64_t *desc, int64_t base)
     {
-        return lookback_load(desc, base);
+        return lookback_load<FRESH_LANE>(desc, base);
     }
     __device__ static __forceinline__ T from(const uint64_t *desc, uint32_t tile, uint32_t tag,
                                              const Window &w)
     {
-        return lookback_from<M>(desc, tile, tag, w);
+        return lookback_from<M, FRESH_LANE>(desc, tile, tag, w);
     }
 };
 

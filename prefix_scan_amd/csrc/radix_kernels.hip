@@ -103,6 +103,8 @@ template <int BLOCK_, int V, bool FIRST, bool LAST>
 struct Radix1Op {
     static constexpr int BLOCK = BLOCK_;
     using Monoid = OpAdd;
+    // The look-back computes its lane offsets afresh (see lane_id_here).
+    using Carry = Carry32<OpAdd, true>;
     static constexpr uint32_t T = (uint32_t)BLOCK * V * 4;
     using TS = TileScan<BLOCK, V>;
     // The zero flags and their scan inside each chunk are recomputed from
