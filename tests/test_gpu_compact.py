@@ -4,6 +4,10 @@ The workload: n = 2^26 int32 Bernoulli flags with keep probability 0.5, 0.01
 and 0.99; plus ragged sizes, unaligned flag pointers, the degenerate cases
 (nothing kept, everything kept, n = 1, negative flags) and the worked example
 of the CAIRN "Concurrency" page.
+
+Every output starts filled with -2 (no slot of a compaction holds it: kept
+indices are >= 0, the tail is -1) and every device count with a pattern the
+count cannot equal, so a slot or count the kernel never wrote fails.
 """
 import json
 import os
@@ -15,18 +19,17 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_i32, to_host_u32
+from tests.gpu_util import (first_mismatch, poison_value, poisoned, poisoned_index, to_dev,
+                            to_host_i32, to_host_u32)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def check(flags, offset=0, out_offset=None):
+def check(flags, offset=0, out_offset=0):
     ref, cref = oracle.compact_flags(flags)
     t = to_dev(flags.astype(np.int32), offset)
-    out = None
-    if out_offset is not None:
-        out = to_dev(np.full(flags.size, 12345, dtype=np.int32), out_offset)
+    out = poisoned_index(flags.size, out_offset)
     out, count = ps.compact_flags_u32(t, out=out)
     got = to_host_i32(out)
     msg = first_mismatch(got, ref)
@@ -39,8 +42,9 @@ def test_workload_2p26(p):
     flags = workloads.compact_flags(p)
     ref, cref = oracle.compact_flags(flags)
     t = torch.from_numpy(flags).to("cuda")
-    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out, none = ps.compact_flags_u32(t, want_count=False, count_dev=cnt)
+    cnt = poisoned(1, poison_value(np.array([cref], dtype=np.uint32)))
+    out, none = ps.compact_flags_u32(t, out=poisoned_index(flags.size), want_count=False,
+                                     count_dev=cnt)
     assert none is None
     assert first_mismatch(to_host_i32(out), ref) is None
     assert int(to_host_u32(cnt)[0]) == cref
@@ -74,7 +78,8 @@ def test_worked_example_cairn_keep_live():
     with open(os.path.join(GOLDEN, "cairn_compact_keep_live.json")) as f:
         g = json.load(f)
     flags = np.array(g["flags"], dtype=np.int32)
-    out, count = ps.compact_flags_u32(torch.from_numpy(flags).to("cuda"))
+    out, count = ps.compact_flags_u32(torch.from_numpy(flags).to("cuda"),
+                                      out=poisoned_index(flags.size))
     idx = to_host_i32(out)
     assert count == g["count"]
     assert flags[idx[:count]].tolist() == g["gathered_values"]

@@ -6,6 +6,8 @@ at the int32 index limit (n = 2^31 - 1).  Inputs have closed-form results -- all
 the scans (the exclusive scan of ones is j mod 2^32, the segmented scan is
 (j mod L) + 1), every third flag kept for compaction (kept index k is 3k) --
 so the whole output is checked, element by element, on the GPU in slices.
+Outputs that are not written in place start filled with -2 (indices) or
+0xDEADBEEF (values no output here holds), so an unwritten slot fails.
 Each case allocates 8-16 GiB of device memory.
 """
 import numpy as np
@@ -17,6 +19,7 @@ import prefix_scan_amd as ps
 pytestmark = pytest.mark.gpu
 SLICE = 1 << 27
 MASK32 = 0xFFFFFFFF
+POISON = 0xDEADBEEF - (1 << 32)      # the pattern 0xDEADBEEF as an int32
 
 
 def _u32(t):
@@ -74,7 +77,7 @@ def test_segscan_beyond_2p32(L):
     n = (1 << 32) + 777
     buf, t = _ones(n, 0)
     nseg = (n + L - 1) // L
-    sums = torch.empty(nseg, dtype=torch.int32, device="cuda")
+    sums = torch.full((nseg,), POISON, dtype=torch.int32, device="cuda")
     ps.segscan_u32(t, L, out=t, seg_sums=sums)
 
     def expected(start, stop):
@@ -89,7 +92,8 @@ def test_segscan_beyond_2p32(L):
 def test_compaction_at_int32_limit():
     n = (1 << 31) - 1
     flags = (torch.arange(n, dtype=torch.int64, device="cuda") % 3 == 0).to(torch.int32)
-    out, count = ps.compact_flags_u32(flags)
+    out = torch.full((n,), -2, dtype=torch.int32, device="cuda")
+    out, count = ps.compact_flags_u32(flags, out=out)
     kept = (n + 2) // 3
     assert count == kept
     del flags
@@ -113,7 +117,8 @@ def test_radix_at_int32_limit(bits):
     keys = ((i % 7) * step).to(torch.int32)   # wraps to the unsigned value's bits
     del i
     torch.cuda.empty_cache()
-    perm = ps.radix_perm_u32(keys, bits)
+    perm = ps.radix_perm_u32(keys, bits, perm=torch.full((n,), -2, dtype=torch.int32,
+                                                         device="cuda"))
     del keys
     torch.cuda.empty_cache()
     counts = [(n - r + 6) // 7 for r in range(7)]
@@ -154,7 +159,7 @@ def test_segscan_flags_at_u32_limit():
     flags = torch.zeros(n, dtype=torch.int32, device="cuda")
     flags[::L] = 1
     nseg = (n + L - 1) // L
-    sums = torch.empty(nseg, dtype=torch.int32, device="cuda")
+    sums = torch.full((nseg,), POISON, dtype=torch.int32, device="cuda")
     out, _, count = ps.segscan_flags_u32(vals, flags, out=vals, seg_sums=sums)
     assert count == nseg
     del flags
@@ -178,7 +183,8 @@ def test_runs_at_int32_limit():
     counts = (i % 5 != 4).to(torch.int32)            # owners 4, 9, 14, .. are empty
     del i
     torch.cuda.empty_cache()
-    ends, entries = ps.runs_layout_u32(counts)
+    ends = torch.full((n,), POISON, dtype=torch.int32, device="cuda")
+    ends, entries = ps.runs_layout_u32(counts, ends=ends)
     total = n - n // 5
     assert entries == total
     del counts
@@ -188,7 +194,8 @@ def test_runs_at_int32_limit():
         j = torch.arange(start, stop, dtype=torch.int64, device="cuda")
         return j + 1 - (j + 1) // 5
     _check_slices(ends, ends_of, "runs ends n=2^31-1")
-    owner = ps.runs_owner_all_u32(ends, total)
+    owner = ps.runs_owner_all_u32(ends, total, owner=torch.full((total,), -2, dtype=torch.int32,
+                                                                device="cuda"))
 
     def owner_of(start, stop):
         # entry e belongs to the owner skipping every 5th: 5 * (e // 4) + e % 4

@@ -95,7 +95,9 @@ def test_u64_empty_and_device_totals(op):
     assert ps.scan_op_u64(empty, op) == ident
     assert ps.reduce_op_u64(empty, op) == ident
     a = shaped(op, 70001, 12)
-    dev = torch.full((2,), 7, dtype=torch.int64, device="cuda")
+    want = oracle.reduce_op_u64(a, op)
+    # Start from a value the fold is not, so an unwritten total fails.
+    dev = torch.full((2,), 7 if want != 7 else 8, dtype=torch.int64, device="cuda")
     assert ps.scan_op_u64(to_dev64(a), op, want_total=False, total_dev=dev[0:1]) is None
     assert ps.reduce_op_u64(to_dev64(a), op, want_total=False, total_dev=dev[1:2]) is None
     got = to_host_u64(dev)

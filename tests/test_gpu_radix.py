@@ -5,6 +5,11 @@ distinct values, by 32 one-bit passes and by 8 four-bit passes; the stable
 permutation is unique, so both must equal the oracle bit for bit.  Plus
 ragged sizes, unaligned key and permutation pointers, and the degenerate
 orders (sorted, all equal, strictly decreasing).
+
+Every permutation is written into a buffer pre-filled with -2, an index no
+permutation holds, so a slot the sort never wrote fails; at the workload size
+the permutation is also checked to be a bijection (each place written by
+exactly one key, entelechy "parallel", sort_place).
 """
 import numpy as np
 import pytest
@@ -13,29 +18,30 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_i32
+from tests.gpu_util import (assert_bijection, first_mismatch, poisoned_index, to_dev,
+                            to_host_i32)
 
 pytestmark = pytest.mark.gpu
 
 
-def check(keys, bpp, offset=0, perm_offset=None, ref=None):
+def check(keys, bpp, offset=0, perm_offset=0, ref=None, bijection=False):
     if ref is None:
         ref = oracle.stable_argsort_u32(keys)
     t = to_dev(keys, offset)
-    perm = None
-    if perm_offset is not None:
-        perm = to_dev(np.zeros(keys.size, dtype=np.int32), perm_offset)
+    perm = poisoned_index(keys.size, perm_offset)
     got = to_host_i32(ps.radix_perm_u32(t, bpp, perm=perm))
     msg = first_mismatch(got, ref)
     assert msg is None, "%s n=%d bits_per_pass=%d" % (msg, keys.size, bpp)
+    if bijection:
+        assert_bijection(got, keys.size)
 
 
+@pytest.mark.parametrize("bpp", [1, 4])
 @pytest.mark.parametrize("kind", ["uniform", "distinct"])
-def test_workload_2p25(kind):
+def test_workload_2p25(kind, bpp):
     keys = workloads.radix_keys_uniform() if kind == "uniform" else workloads.radix_keys_distinct()
     ref = oracle.stable_argsort_u32(keys)
-    check(keys, 1, ref=ref)
-    check(keys, 4, ref=ref)
+    check(keys, bpp, ref=ref, bijection=True)
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 100, 4095, 4096, 4097, 12345, 16384, 16385, 65537,

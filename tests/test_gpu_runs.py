@@ -5,6 +5,10 @@ Workloads: 2^24 owners with counts uniform over [0, 8) and with nine owners
 in ten empty (long stretches of empty runs, the merge-path's hard case);
 ragged small sizes; outputs at every 16-byte phase relative to the counts;
 in place; all-zero counts; the owner of entries past the last run.
+
+Every output starts filled with a value it cannot hold (-2 for owners, a
+pattern absent from the expected run ends, entry count or slots), so
+anything the kernels never wrote fails.
 """
 import numpy as np
 import pytest
@@ -13,7 +17,8 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_i32, to_host_u32
+from tests.gpu_util import (first_mismatch, poison_value, poisoned, poisoned_index,
+                            poisoned_like_ref, to_dev, to_host_i32, to_host_u32)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +34,7 @@ def test_layout_matches_oracle(kind, n):
     ref, rent = oracle.runs_u32(c)
     for ci, ei in ((0, 0), (1, 3), (2, 2), (3, 0)):
         cd = to_dev(c, ci)
-        ed = to_dev(np.zeros(n, dtype=np.uint32), ei)
+        ed = poisoned_like_ref(ref, ei)
         _, ent = ps.runs_layout_u32(cd, ends=ed)
         msg = first_mismatch(to_host_u32(ed), ref)
         assert msg is None, "%s kind=%s n=%d offsets=%d,%d" % (msg, kind, n, ci, ei)
@@ -42,7 +47,7 @@ def test_layout_in_place_and_device_entries():
     c = counts_of("uniform", 1 << 22)
     ref, rent = oracle.runs_u32(c)
     t = to_dev(c, 1)
-    dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = poisoned(1, poison_value(np.array([rent], dtype=np.uint32)))
     ends, ent = ps.runs_layout_u32(t, ends=t, want_entries=False, entries_dev=dev)
     assert ent is None and int(to_host_u32(dev)[0]) == rent
     assert first_mismatch(to_host_u32(t), ref) is None
@@ -75,7 +80,7 @@ def test_owner_queries(kind):
     q = rng.integers(0, total + 1000, 1 << 20, dtype=np.uint32)
     q[:3] = [0, total - 1, total]
     want = np.where(q < total, every[np.minimum(q, total - 1)], -1).astype(np.int32)
-    got = ps.runs_owner_u32(to_dev(ends), to_dev(q, 1))
+    got = ps.runs_owner_u32(to_dev(ends), to_dev(q, 1), owner=poisoned_index(q.size, 2))
     assert first_mismatch(to_host_i32(got), want) is None
     # the oracle's own definition on a sample of queries
     for j in range(0, q.size, q.size // 37):
@@ -84,7 +89,8 @@ def test_owner_queries(kind):
 
 def test_owner_queries_without_runs():
     q = torch.arange(100, dtype=torch.int32, device="cuda")
-    got = ps.runs_owner_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), q)
+    got = ps.runs_owner_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), q,
+                            owner=poisoned_index(100))
     assert (to_host_i32(got) == -1).all()
 
 
@@ -96,7 +102,7 @@ def test_owner_all_matches_oracle(kind, n):
         c[-1] = 3
     ends, _ = oracle.runs_u32(c)
     want = oracle.runs_owner_all(c)
-    got = ps.runs_owner_all_u32(to_dev(ends), want.size)
+    got = ps.runs_owner_all_u32(to_dev(ends), want.size, owner=poisoned_index(want.size))
     msg = first_mismatch(to_host_i32(got), want)
     assert msg is None, "%s kind=%s n=%d" % (msg, kind, n)
 
@@ -108,9 +114,10 @@ def test_owner_all_short_and_long_totals():
     total = every.size
     e = to_dev(ends, 2)
     for t in (1, 4095, 4096, 4097, total // 3):          # a prefix of the entries
-        got = ps.runs_owner_all_u32(e, t)
+        got = ps.runs_owner_all_u32(e, t, owner=poisoned_index(t, t % 4))
         assert first_mismatch(to_host_i32(got), every[:t]) is None, t
-    got = ps.runs_owner_all_u32(e, total + 9000)           # entries past the last run: -1
+    got = ps.runs_owner_all_u32(e, total + 9000,          # entries past the last run: -1
+                                owner=poisoned_index(total + 9000))
     want = np.concatenate([every, np.full(9000, -1, dtype=np.int32)])
     assert first_mismatch(to_host_i32(got), want) is None
 
@@ -123,5 +130,5 @@ def test_owner_all_one_long_run_and_many_empty_runs():
     c[-1] = 5
     ends, _ = oracle.runs_u32(c)
     want = oracle.runs_owner_all(c)
-    got = ps.runs_owner_all_u32(to_dev(ends), want.size)
+    got = ps.runs_owner_all_u32(to_dev(ends), want.size, owner=poisoned_index(want.size))
     assert first_mismatch(to_host_i32(got), want) is None

@@ -13,7 +13,7 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_u32
+from tests.gpu_util import first_mismatch, poison_value, poisoned, to_dev, to_host_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +109,7 @@ def test_large_workload_uniform_exclusive_and_inclusive():
     for inclusive in (False, True):
         ref, tref = oracle.scan_u32(a, inclusive)
         t = to_dev(a)
-        tot_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+        tot_dev = poisoned(1, poison_value(np.array([tref], dtype=np.uint32)))
         f = ps.scan_inclusive_u32 if inclusive else ps.scan_exclusive_u32
         assert f(t, want_total=False, total_dev=tot_dev) is None
         got = to_host_u32(t)
@@ -127,7 +127,7 @@ def test_total_on_device_and_host_agree():
     a = workloads.small_random_u32(123457, 5)
     ref, tref = oracle.scan_exclusive_u32(a)
     t = to_dev(a)
-    tot_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tot_dev = poisoned(1, poison_value(np.array([tref], dtype=np.uint32)))
     tot = ps.scan_exclusive_u32(t, want_total=True, total_dev=tot_dev)
     assert tot == tref == int(to_host_u32(tot_dev)[0])
     assert np.array_equal(to_host_u32(t), ref)
@@ -173,10 +173,10 @@ def test_copy_kernel():
     for n in (1, 4097, (1 << 22) + 3):
         a = workloads.small_random_u32(n, 4)
         src = to_dev(a)
-        dst = torch.empty_like(src)
+        dst = poisoned(n, poison_value(a))
         ps.copy_u32(src, dst)
         assert np.array_equal(to_host_u32(dst), a)
     src = to_dev(a, 1)
-    dst = to_dev(np.zeros(a.size, dtype=np.uint32), 2)
+    dst = poisoned(a.size, poison_value(a), 2)
     ps.copy_u32(src, dst)
     assert np.array_equal(to_host_u32(dst), a)

@@ -13,7 +13,8 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_u32
+from tests.gpu_util import (first_mismatch, poison_value, poisoned, poisoned_like_ref, to_dev,
+                            to_host_u32)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +23,17 @@ def run(a, f, vo=0, fo=0, oo=None, in_place=False):
     ref, rsums = oracle.segscan_flags_u32(a, f)
     t = to_dev(a, vo)
     fl = to_dev(f, fo)
-    out = t if in_place else (to_dev(np.zeros_like(a), oo) if oo is not None else None)
-    got, sums, nsegs = ps.segscan_flags_u32(t, fl, out=out)
+    out = t if in_place else poisoned_like_ref(ref, oo or 0)
+    # Room for every possible segment, so the slots past the last one show
+    # that nothing is written beyond it.
+    sums_buf = poisoned(max(a.size, 1), poison_value(rsums))
+    got, sums, nsegs = ps.segscan_flags_u32(t, fl, out=out, seg_sums=sums_buf)
     msg = first_mismatch(to_host_u32(got), ref)
     assert msg is None, "%s n=%d offsets=%s" % (msg, a.size, (vo, fo, oo, in_place))
     assert nsegs == rsums.size
-    assert np.array_equal(to_host_u32(sums), rsums), (a.size, vo, fo, oo)
+    s_host = to_host_u32(sums)
+    assert np.array_equal(s_host[:nsegs], rsums), (a.size, vo, fo, oo)
+    assert (s_host[nsegs:] == poison_value(rsums)).all(), "a total written past the last segment"
 
 
 @pytest.mark.parametrize("mean", [16, 1 << 20])
@@ -72,9 +78,10 @@ def test_wrapping_sums_and_device_count():
     a = np.full(n, 0xFFFFFFFF, dtype=np.uint32)
     f = (np.arange(n) % 100000 == 0).astype(np.int32)
     run(a, f)
-    dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    want = int(np.count_nonzero(f))
+    dev = poisoned(1, poison_value(np.array([want], dtype=np.uint32)))
     _, _, none = ps.segscan_flags_u32(to_dev(a), to_dev(f), want_nsegs=False, nsegs_dev=dev)
-    assert none is None and int(to_host_u32(dev)[0]) == int(np.count_nonzero(f))
+    assert none is None and int(to_host_u32(dev)[0]) == want
 
 
 def test_empty():

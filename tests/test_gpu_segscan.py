@@ -5,6 +5,9 @@ length 16 (many per tile) and 2^20 (many tiles per segment; the sums wrap past
 2^32); plus ragged lengths that divide nothing, segment lengths 1, 2, 3 and
 >= n, in-place operation, unaligned pointers and an output whose 16-byte
 phase differs from the input's.
+
+Outputs and segment sums start filled with a 32-bit pattern the expected
+array does not contain, so a slot the kernel never wrote fails.
 """
 import numpy as np
 import pytest
@@ -13,7 +16,7 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_u32
+from tests.gpu_util import first_mismatch, poisoned_like_ref, to_dev, to_host_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -21,13 +24,9 @@ pytestmark = pytest.mark.gpu
 def check(a, L, in_place=False, offset=0, out_offset=None):
     ref, sref = oracle.segscan_u32(a, L)
     t = to_dev(a, offset)
-    if in_place:
-        out = t
-    elif out_offset is not None:
-        out = to_dev(np.zeros(a.size, dtype=np.uint32), out_offset)
-    else:
-        out = None
-    out, sums = ps.segscan_u32(t, L, out=out)
+    out = t if in_place else poisoned_like_ref(ref, out_offset or 0)
+    sums = poisoned_like_ref(sref)
+    out, sums = ps.segscan_u32(t, L, out=out, seg_sums=sums)
     got = to_host_u32(out)
     msg = first_mismatch(got, ref)
     assert msg is None, "%s n=%d L=%d" % (msg, a.size, L)
@@ -73,14 +72,14 @@ def test_wrapping_sums():
 def test_reduce_pin_cairn_weights():
     # CAIRN "Concurrency", reduce and compact: sum of i % 7 over 10000 is 29994.
     w = (np.arange(10000) % 7).astype(np.uint32)
-    _, sums = ps.segscan_u32(to_dev(w), 10000)
+    _, sums = ps.segscan_u32(to_dev(w), 10000, seg_sums=poisoned_like_ref(np.array([29994], dtype=np.uint32)))
     assert int(to_host_u32(sums)[0]) == 29994
 
 
 def test_no_sums_and_empty():
     a = workloads.small_random_u32(5000, 2)
-    out, sums = ps.segscan_u32(to_dev(a), 64, seg_sums=None)
     ref, _ = oracle.segscan_u32(a, 64)
+    out, sums = ps.segscan_u32(to_dev(a), 64, out=poisoned_like_ref(ref), seg_sums=None)
     assert sums is None and np.array_equal(to_host_u32(out), ref)
     out, sums = ps.segscan_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), 5)
     assert out.numel() == 0

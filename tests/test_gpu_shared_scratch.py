@@ -6,7 +6,9 @@ chained-carry state.  The library clears the state it cannot trust before a
 call whose layout differs from the buffer's last one; these tests interleave
 all entry points on one buffer -- including a one-bit radix call followed by
 a four-bit one, whose rows overlap the four-bit histogram scan's state -- and
-check every result against the oracle.
+check every result against the oracle.  Every output starts poisoned (-2
+for indices, a pattern absent from the expected values otherwise), so a
+call cannot pass on the answer an earlier call left in recycled memory.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,8 @@ import torch
 import oracle
 import prefix_scan_amd as ps
 import workloads
-from tests.gpu_util import first_mismatch, to_dev, to_host_i32, to_host_u32
+from tests.gpu_util import (assert_bijection, first_mismatch, poisoned_index,
+                            poisoned_like_ref, to_dev, to_host_i32, to_host_u32)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,19 +32,21 @@ def scan_ok(a, algo, inclusive):
 
 def radix_ok(keys, bpp):
     ref = oracle.stable_argsort_u32(keys)
-    got = to_host_i32(ps.radix_perm_u32(to_dev(keys), bpp))
+    got = to_host_i32(ps.radix_perm_u32(to_dev(keys), bpp, perm=poisoned_index(keys.size)))
     assert first_mismatch(got, ref) is None, (bpp, keys.size)
+    assert_bijection(got, keys.size)
 
 
 def compact_ok(flags):
     ref, c = oracle.compact_flags(flags)
-    out, count = ps.compact_flags_u32(to_dev(flags))
+    out, count = ps.compact_flags_u32(to_dev(flags), out=poisoned_index(flags.size))
     assert first_mismatch(to_host_i32(out), ref) is None and count == c
 
 
 def segscan_ok(a, L):
     ref, sref = oracle.segscan_u32(a, L)
-    out, sums = ps.segscan_u32(to_dev(a), L)
+    out, sums = ps.segscan_u32(to_dev(a), L, out=poisoned_like_ref(ref),
+                               seg_sums=poisoned_like_ref(sref))
     assert first_mismatch(to_host_u32(out), ref) is None
     assert first_mismatch(to_host_u32(sums), sref) is None
 
