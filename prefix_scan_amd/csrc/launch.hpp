@@ -27,8 +27,8 @@ constexpr int kBlock = 256;
 // data (block sums, radix ping-pong rows).  Tickets and descriptors carry the
 // epoch of the launch that wrote them, so they stay valid from launch to
 // launch without clearing -- as long as no data of another layout has been
-// written over them.  The C ABI tracks that (state.cpp) and clears a state
-// region before a call whenever the buffer's previous layout could have
+// written over them.  The C ABI tracks that (scratch_state.hpp) and clears a
+// state region before a call whenever the buffer's previous layout could have
 // overwritten it.
 constexpr size_t kScratchAlign = 256;
 constexpr size_t kHeaderBytes = 256;

@@ -3,12 +3,12 @@
 // total or count.  All GPU work is enqueued on the caller's stream.
 #include "../../include/libscan.h"
 #include "launch.hpp"
+#include "scratch_state.hpp"
 
 #include <stdio.h>
 #include <string.h>
 
 #include <mutex>
-#include <unordered_map>
 
 using namespace libscan;
 
@@ -46,83 +46,38 @@ bool carve(void *scratch, size_t scratch_bytes, size_t body, Scratch *out)
 }
 
 // ---------------------------------------------------------------------------
-// Scratch state tracking.
-//
-// Tickets (header) and tile descriptors (front of the body) stay valid from
-// launch to launch because every word carries the epoch of the launch that
-// wrote it.  Two things break that: data of another layout written over a
-// descriptor region (the three-pass sums, the radix rows), and a buffer whose
-// contents the library has never seen.  The library therefore remembers,
-// per scratch buffer, what its last call left there, and before each call
-// clears (with a fill kernel on the call's stream) whatever state the call
-// will read that it cannot vouch for:
-//   ZERO  -- libscan_scratch_init zeroed the buffer: every state is valid.
-//   DESC  -- descriptors of the look-back scan, segmented scan or
-//            compaction in the first `state` body bytes: valid for any of
-//            those three, a larger call clears only the extra range.
-//   RADIX -- the radix layout for one (n, bits_per_pass): valid only for the
-//            same pair.
-//   DATA  -- the three-pass scan's block sums over the body: nothing valid.
-// An unknown buffer is cleared.  Forgetting a buffer is therefore always
-// safe, so the table is simply emptied if it grows large.  After 2^29
-// launches on one buffer the state is cleared too, long before the 30-bit
-// epoch in the descriptors could repeat.
+// Scratch state tracking (scratch_state.hpp): before each call, clear with a
+// fill kernel on the call's stream whatever state the call will read that it
+// cannot vouch for.
 // ---------------------------------------------------------------------------
-enum StateKind { kKindZero = 1, kKindDesc = 2, kKindRadix = 3, kKindData = 4 };
+StateTable g_states;
 
-struct StateRecord {
-    int kind;
-    uint64_t sig;
-    size_t state;          // body bytes of valid state from the front
-    uint64_t launches;     // launches since the last full clear
-};
+// Whether `stream` is recording a HIP graph right now.
+bool stream_capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess)
+        return false;
+    return st == hipStreamCaptureStatusActive;
+}
 
-std::mutex g_state_mu;
-std::unordered_map<uintptr_t, StateRecord> g_state;
-constexpr uint64_t kMaxLaunchesBetweenClears = 1ull << 29;
-constexpr size_t kMaxTrackedBuffers = 4096;
+hipError_t apply_plan(const Scratch &s, const ClearPlan &p, size_t state, hipStream_t stream)
+{
+    if (p.header)
+        return launch_fill_zero(s.base, kHeaderBytes + state, stream);
+    if (p.bytes)
+        return launch_fill_zero(s.body() + p.from, p.bytes, stream);
+    return hipSuccess;
+}
 
 hipError_t prepare_state(const Scratch &s, int kind, uint64_t sig, size_t state,
                          uint64_t launches, hipStream_t stream)
 {
-    std::lock_guard<std::mutex> lock(g_state_mu);
-    if (g_state.size() > kMaxTrackedBuffers)
-        g_state.clear();
     const uintptr_t key = (uintptr_t)s.base;
-    StateRecord prev{0, 0, 0, 0};
-    auto it = g_state.find(key);
-    if (it != g_state.end())
-        prev = it->second;
-    if (kind == kKindData) {
-        g_state[key] = StateRecord{kKindData, 0, 0, prev.launches};
-        return hipSuccess;
-    }
-    const bool fresh_epochs = prev.kind != 0 && prev.launches + launches < kMaxLaunchesBetweenClears;
-    size_t valid = 0;              // body bytes this call may trust as they are
-    bool header_ok = false;
-    if (fresh_epochs) {
-        if (prev.kind == kKindZero || (prev.kind == kKindDesc && kind == kKindDesc)) {
-            header_ok = true;
-            valid = prev.state;
-        } else if (prev.kind == kKindRadix && kind == kKindRadix && prev.sig == sig) {
-            header_ok = true;
-            valid = state;
-        }
-    }
-    hipError_t e = hipSuccess;
-    StateRecord next{kind, sig, state, prev.launches + launches};
-    if (!header_ok) {
-        e = launch_fill_zero(s.base, kHeaderBytes + state, stream);
-        next.launches = launches;
-    } else if (valid < state) {
-        e = launch_fill_zero(s.body() + valid, state - valid, stream);
-    } else if (kind == kKindDesc) {
-        next.state = valid;        // the larger valid range stays valid
-    }
-    if (e == hipSuccess)
-        g_state[key] = next;
-    else
-        g_state.erase(key);
+    const ClearPlan p = g_states.prepare(key, kind, sig, state, launches, stream_capturing(stream));
+    const hipError_t e = apply_plan(s, p, state, stream);
+    if (e != hipSuccess)
+        g_states.forget(key);
     return e;
 }
 
@@ -299,8 +254,7 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
     hipError_t e = launch_fill_zero(s.base, kHeaderBytes, stream);
     if (e != hipSuccess)
         return hip_status(e);
-    std::lock_guard<std::mutex> lock(g_state_mu);
-    g_state[(uintptr_t)s.base] = StateRecord{kKindZero, 0, 0, 0};
+    g_states.zeroed((uintptr_t)s.base);
     return LIBSCAN_OK;
 }
 
