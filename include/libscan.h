@@ -148,6 +148,37 @@ int scan_u32_ex(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
                 uint32_t *total_host, uint32_t *total_dev, void *scratch, size_t scratch_bytes,
                 hipStream_t stream);
 
+/*
+ * The scan for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no scratch argument; its chained-carry state lives in a static
+ * device array inside the library, LIBSCAN_NOALLOC_SCRATCH_BYTES (about
+ * 1 MiB) on each device it runs on, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the caller passes the data and, optionally, where the total goes.
+ *
+ * data         device, n u32, in place, exactly as scan_exclusive_u32 /
+ *              scan_inclusive_u32 (same results, same kernels).
+ * n            0 .. LIBSCAN_NOALLOC_MAX_N (2^32); larger is ERR_SIZE.
+ * inclusive    0 exclusive, 1 inclusive.
+ * total_dev    device u32 or NULL; the total in stream order.  There is no
+ *              host total: a graph cannot wait for the host.
+ * stream       HIP stream; the device it belongs to runs the scan.
+ * Every call on one device shares that device's array, and the array keeps
+ * what the last call left: calls on one device that may overlap (different
+ * streams, or graphs replayed concurrently) race and give wrong results.
+ * Before each call the library clears (with a fill kernel, never a memset
+ * node) whatever part of the array the call cannot trust; once the entry
+ * point has been captured into a graph on a device, every later call there
+ * clears all the state it reads.
+ * Errors: ERR_ARG (inclusive not 0/1), ERR_SIZE, ERR_ALIGN, ERR_NULL (data
+ * NULL with n > 0), ERR_HIP.
+ */
+#define LIBSCAN_NOALLOC_MAX_N ((uint64_t)1 << 32)
+#define LIBSCAN_NOALLOC_SCRATCH_BYTES ((size_t)1049088)
+int scan_u32_noalloc(uint32_t *data, uint64_t n, int inclusive, uint32_t *total_dev,
+                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Scan and reduction under the other integer operators                     */
 /* ------------------------------------------------------------------------ */

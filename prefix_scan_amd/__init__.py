@@ -22,7 +22,7 @@ __all__ = [
     "scan_op_u32", "reduce_op_u32", "scan_op_u64", "reduce_op_u64",
     "runs_layout_u32", "runs_slots_i32", "runs_owner_u32", "runs_owner_all_u32",
     "segscan_flags_u32",
-    "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32",
+    "segscan_u32", "compact_flags_u32", "radix_perm_u32", "copy_u32", "scan_u32_noalloc",
     "scan_scratch_bytes", "scan_ex_scratch_bytes", "segscan_scratch_bytes",
     "compact_scratch_bytes", "radix_scratch_bytes",
     "ALGO_AUTO", "ALGO_LOOKBACK", "ALGO_THREEPASS", "ALGO_LOOKBACK_TILE",
@@ -119,6 +119,8 @@ def lib():
         L.radix_perm_u32.restype = i32
         L.copy_u32.argtypes = [vp, vp, u64, vp]
         L.copy_u32.restype = i32
+        L.scan_u32_noalloc.argtypes = [vp, u64, i32, vp, vp]
+        L.scan_u32_noalloc.restype = i32
         _lib = L
     return _lib
 
@@ -491,6 +493,24 @@ def radix_perm_u32(keys, bits_per_pass=1, perm=None, stream=None):
     _check(lib().radix_perm_u32(_ptr(keys), _ptr(perm), n, bits_per_pass, _ptr(scr), scr.numel(),
                                 sh), "radix_perm_u32")
     return perm
+
+
+# Largest n of scan_u32_noalloc (LIBSCAN_NOALLOC_MAX_N of libscan.h).
+NOALLOC_MAX_N = 1 << 32
+
+
+def scan_u32_noalloc(data, inclusive=False, total_dev=None, stream=None):
+    """In-place scan of `data` (as scan_exclusive_u32 / scan_inclusive_u32)
+    whose scratch is the library's own static device array: nothing is
+    allocated, here or in the library.  The total goes to the device u32
+    `total_dev` when given; nothing waits."""
+    _dev_u32(data, "data")
+    if total_dev is not None:
+        _dev_u32(total_dev, "total_dev")
+    sh, _ = _stream_handle(data.device, stream)
+    _check(lib().scan_u32_noalloc(_ptr(data), data.numel(), 1 if inclusive else 0,
+                                  _ptr(total_dev), sh), "scan_u32_noalloc")
+    return None
 
 
 def copy_u32(src, dst, stream=None):

@@ -62,6 +62,11 @@ struct Scratch {
 // pipelined: the grid-filling two-tile kernel; else one workgroup per tile.
 hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
                                 const Scratch &s, uint32_t *total_out, hipStream_t stream);
+// The same with the default tile shapes only (never the tuning override);
+// its tiles hold at least kDefaultScanTile elements.
+constexpr uint64_t kDefaultScanTile = (uint64_t)512 * 16 * 4;
+hipError_t launch_scan_lookback_default(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
+                                        const Scratch &s, uint32_t *total_out, hipStream_t stream);
 hipError_t launch_scan_table(uint32_t *data, uint64_t n, const Scratch &s, uint32_t *total_out,
                              hipStream_t stream);
 int resident_grid(const void *kernel, int block);

@@ -222,6 +222,82 @@ int scan_common(uint32_t *data, uint64_t n, int inclusive, int algo, int fork_de
     return LIBSCAN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// scan_u32_noalloc: the scan with its scratch in a static device array, for
+// callers that cannot allocate.  Each device holds its own copy of the
+// array, at its own address; host code reaches it only through the address
+// hipGetSymbolAddress returns for the device (the array's name is a host-side
+// stand-in, not a device address).  The array keeps the chained carry's
+// header and the descriptors of the default tile shapes: up to
+// kNoallocTiles tiles of at least kDefaultScanTile elements, so n up to
+// LIBSCAN_NOALLOC_MAX_N whatever the array's 16-byte phase.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kNoallocTiles = (LIBSCAN_NOALLOC_MAX_N + 3 + kDefaultScanTile - 1) / kDefaultScanTile;
+constexpr size_t kNoallocBody = (kNoallocTiles * sizeof(uint64_t) + kScratchAlign - 1) /
+                                kScratchAlign * kScratchAlign;
+constexpr size_t kNoallocBytes = kHeaderBytes + kNoallocBody;
+static_assert(kNoallocBytes == LIBSCAN_NOALLOC_SCRATCH_BYTES, "the header states the array's size");
+
+constexpr int kNoallocMaxDevices = 64;
+
+// Per device: the array's address and what the last call left in it.  A
+// fixed table (no heap), guarded by a mutex.
+struct NoallocDevice {
+    void *ptr;             // device address of the array, or null before set-up
+    StateRecord rec;
+    bool captured;         // used under graph capture: never trust its state again
+};
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[kNoallocMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t noalloc_scratch[kNoallocBytes];
+
+namespace {
+
+// The device `stream` runs on.
+hipError_t device_of(hipStream_t stream, int *dev)
+{
+    if (stream == nullptr)
+        return hipGetDevice(dev);
+    hipDevice_t d = 0;
+    const hipError_t e = hipStreamGetDevice(stream, &d);
+    *dev = (int)d;
+    return e;
+}
+
+// The array's address on `dev`, looked up once per device with that device
+// current (the caller holds g_noalloc_mu).
+hipError_t noalloc_ptr(int dev, void **out)
+{
+    NoallocDevice &d = g_noalloc[dev];
+    if (!d.ptr) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr || ((uintptr_t)p & (kScratchAlign - 1)) != 0)
+            return hipErrorInvalidSymbol;
+        d.ptr = p;
+        d.rec = StateRecord{kKindNone, 0, 0, 0};
+        d.captured = false;
+    }
+    *out = d.ptr;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,6 +706,49 @@ int radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per
     if (e != hipSuccess)
         return hip_status(e);
     return hip_status(launch_radix(keys, perm, n, bits_per_pass, s, stream));
+}
+
+int scan_u32_noalloc(uint32_t *data, uint64_t n, int inclusive, uint32_t *total_dev,
+                     hipStream_t stream)
+{
+    if (inclusive != 0 && inclusive != 1)
+        return LIBSCAN_ERR_ARG;
+    if (n > LIBSCAN_NOALLOC_MAX_N)
+        return LIBSCAN_ERR_SIZE;
+    if (misaligned4(data) || misaligned4(total_dev))
+        return LIBSCAN_ERR_ALIGN;
+    if (n == 0)
+        return report_zero(nullptr, total_dev, stream);
+    if (!data)
+        return LIBSCAN_ERR_NULL;
+    int dev = 0;
+    hipError_t e = device_of(stream, &dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= kNoallocMaxDevices)
+        return LIBSCAN_ERR_ARG;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    void *ptr = nullptr;
+    if ((e = noalloc_ptr(dev, &ptr)) != hipSuccess)
+        return hip_status(e);
+    const size_t state = (size_t)tiles_for(n, head_of(data), kDefaultScanTile) * sizeof(uint64_t);
+    Scratch s;
+    if (!carve(ptr, kNoallocBytes, state, &s))      // cannot fail below the limit
+        return LIBSCAN_ERR_SIZE;
+    NoallocDevice &d = g_noalloc[dev];
+    if (stream_capturing(stream))
+        d.captured = true;
+    StateRecord next;
+    const ClearPlan p = plan_call(d.rec, d.captured, kKindDesc, 0, state, 1, &next);
+    e = apply_plan(s, p, state, stream);
+    if (e != hipSuccess) {
+        d.rec = StateRecord{kKindNone, 0, 0, 0};
+        return hip_status(e);
+    }
+    d.rec = next;
+    uint32_t *tot = total_dev ? total_dev : s.total_slot();
+    e = launch_scan_lookback_default(data, n, inclusive != 0, n > kAutoTileMaxN, s, tot, stream);
+    return hip_status(e);
 }
 
 int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream)

@@ -327,6 +327,17 @@ hipError_t launch_scan_lookback(uint32_t *data, uint64_t n, bool inclusive, bool
                      : scan_lookback_v<512, 32>(data, n, inclusive, false, s, total_out, stream);
 }
 
+// The default shapes only, whatever LIBSCAN_SCAN_BLOCK / LIBSCAN_SCAN_CHUNKS
+// say: a caller whose descriptor space is fixed (scan_u32_noalloc) sizes it
+// for these tiles, none smaller than kDefaultScanTile elements.
+hipError_t launch_scan_lookback_default(uint32_t *data, uint64_t n, bool inclusive, bool pipelined,
+                                        const Scratch &s, uint32_t *total_out, hipStream_t stream)
+{
+    if (pipelined || n <= (1ull << 22))
+        return scan_lookback_v<512, 16>(data, n, inclusive, pipelined, s, total_out, stream);
+    return scan_lookback_v<512, 32>(data, n, inclusive, false, s, total_out, stream);
+}
+
 // An exclusive scan of a table of a few hundred thousand entries (the four-bit
 // sort's digit-major counts): one-tile kernel on 32 KiB tiles, so the 512
 // KiB table spreads over 16 workgroups rather than 2 (3.2% on the 2^25 sort).

@@ -147,6 +147,17 @@ def test_copy_argument_errors():
     assert L.copy_u32(NULLP, NULLP, 0, NULLP) == ps.OK
 
 
+def test_noalloc_scan_argument_errors():
+    L = ps.lib()
+    assert L.scan_u32_noalloc(FAKE, (1 << 32) + 1, 0, NULLP, NULLP) == ps.ERR_SIZE
+    assert L.scan_u32_noalloc(FAKE, 16, 2, NULLP, NULLP) == ps.ERR_ARG
+    assert L.scan_u32_noalloc(ctypes.c_void_p(0x100002), 16, 0, NULLP, NULLP) == ps.ERR_ALIGN
+    assert L.scan_u32_noalloc(FAKE, 16, 0, ctypes.c_void_p(0x100001), NULLP) == ps.ERR_ALIGN
+    assert L.scan_u32_noalloc(NULLP, 16, 1, NULLP, NULLP) == ps.ERR_NULL
+    assert L.scan_u32_noalloc(NULLP, 0, 0, NULLP, NULLP) == ps.OK
+    assert ps.NOALLOC_MAX_N == 1 << 32
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     t = torch.zeros(8, dtype=torch.int32)
