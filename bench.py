@@ -2,15 +2,27 @@
 
 Default: the U32 exclusive scan, in place, of n = 2^28 values uniform over
 [0, 2^32) (seed 202), through scan_exclusive_u32 with the total left on the
-device.  Prints ONE JSON line:  GElem/s over the timed steps, the kernel's
-roofline (algorithmic bytes = 8 per element: 4 read + 4 written, over the
-average launch duration from HIP events on the launch stream), and the CPU
-oracle timed on this host beside it.
+device.  W untimed steps, then K steps back to back, bracketed by a device
+synchronisation on both sides; prints ONE JSON line:
+  value           GElem/s over the timed steps (host wall clock);
+  roofline        the scan kernel's algorithmic bytes (8 per element: 4 read
+                  + 4 written) over its average launch time, from HIP events
+                  recorded on the launch stream at the two ends of the timed
+                  region; the ceiling -- the library's streaming copy over the
+                  same 1 GiB, in place (the scan's traffic and memory pattern
+                  with none of its work) and out of place -- timed before the
+                  timed region; the HBM traffic from the committed rocprofv3
+                  counter summary;
+  cpu_baseline    the oracle's three-pass scan on all of this host's affinity
+                  threads, its sequential scan on one, and numpy's cumsum, on
+                  the same array, whose first passes are checked against the
+                  GPU's result bit for bit.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite [--hbm-rows]]
 
 --suite additionally prints one JSON line per primitive workload (the other
-scan variants, compaction, segmented scan, radix permutation) for the tables.
+scan variants, compaction, segmented scan, radix permutation, ...), each the
+median of per-launch event times, every launch on the pristine workload.
 """
 import argparse
 import hashlib
@@ -55,39 +67,114 @@ def measured_traffic(n):
     return rec.get("hbm_bytes_per_launch")
 
 
-def timed_launches(torch, fn, reps):
+def timed_launches(torch, fn, reps, before=None):
     """Run fn() reps times on the current stream, each bracketed by HIP
-    events; returns (per-launch ms list, wall ms for all reps)."""
+    events (before(), when given, runs first, outside the events); returns
+    the per-launch ms list."""
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for a, b in evs:
+        if before is not None:
+            before()
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def timed_region(torch, fn, reps):
+    """Run fn() reps times back to back; returns (wall ms, event ms) for the
+    whole region, the events recorded on the launch stream at its two ends."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    return [a.elapsed_time(b) for a, b in evs], wall
+    return wall, e0.elapsed_time(e1)
 
 
-def cpu_baseline_scan(a, gpu_out, budget_s=10.0):
-    """The oracle's sequential scan of the same array on this host; also
-    checks the GPU result of the same input bit for bit."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_scan(a, gpu_out, budget_s=4.0):
+    """The oracle's scans of the same 2^28 array on this host: bendlib's three
+    passes with passes 1 and 3 on all T affinity threads (fork depth
+    ceil(log2 T) + 2), the sequential definition on one thread, and numpy's
+    wrapping cumsum as a library reference.  Each repeats for about budget_s
+    on buffers allocated once; the first pass of each oracle is also checked
+    against the GPU's result, bit for bit."""
+    import ctypes
     import oracle
-    reps, elapsed, ok = 0, 0.0, None
-    while elapsed < budget_s or reps == 0:
-        t0 = time.perf_counter()
-        out, _ = oracle.scan_exclusive_u32(a)
-        elapsed += time.perf_counter() - t0
-        if ok is None:
-            ok = bool(np.array_equal(out, gpu_out))
-        reps += 1
-    return {"value": round(reps * a.size / elapsed / 1e9, 4), "unit": "GElem/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "the whole n=2^28 workload, %d sequential passes of the C oracle "
-                      "(%.1f s), one host thread" % (reps, elapsed)}, ok
+    L = oracle.load()
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    T = len(os.sched_getaffinity(0))
+    b = (T - 1).bit_length() + 2
+    n = a.size
+
+    def rate(fn, check=None):
+        reps, elapsed = 0, 0.0
+        while elapsed < budget_s or reps == 0:
+            t0 = time.perf_counter()
+            r = fn()
+            elapsed += time.perf_counter() - t0
+            if reps == 0 and check is not None:
+                check(r)
+            reps += 1
+        return n * reps / elapsed / 1e9, reps, elapsed
+
+    ok = []
+    buf = a.copy()
+    tot = ctypes.c_uint32(0)
+
+    def threaded():
+        # In place: the first pass scans the workload (and is checked); later
+        # passes scan their predecessor's output, which costs the same.
+        rc = L.oracle_scan_blocked_threads_u32(buf.ctypes.data_as(u32p), n, b, 0, T,
+                                               ctypes.byref(tot))
+        assert rc == 0
+        return buf
+    thr, thr_reps, thr_s = rate(threaded, lambda r: ok.append(bool(np.array_equal(r, gpu_out))))
+    out = np.empty_like(a)
+
+    def sequential():
+        L.oracle_scan_u32(a.ctypes.data_as(u32p), out.ctypes.data_as(u32p), n, 0)
+        return out
+    seq, seq_reps, seq_s = rate(sequential, lambda r: ok.append(bool(np.array_equal(r, gpu_out))))
+    cs = np.empty_like(a)
+
+    def numpy_cumsum():
+        np.cumsum(a, dtype=np.uint32, out=cs)
+        return cs
+    npy, npy_reps, npy_s = rate(numpy_cumsum)
+    rec = {"value": round(thr, 4), "unit": "GElem/s", "cores": T, "kind": "oracle",
+           "sample": "the whole n=2^28 workload, %d passes (%.1f s) of the oracle's three-pass "
+                     "scan at fork depth %d with passes 1 and 3 on %d host threads" % (
+                         thr_reps, thr_s, b, T),
+           "cpu_model": cpu_model(),
+           "sequential_1core": {"value": round(seq, 4), "unit": "GElem/s", "cores": 1,
+                                "sample": "%d sequential passes of the oracle (%.1f s)" % (
+                                    seq_reps, seq_s)},
+           "numpy_cumsum_uint32": {"value": round(npy, 4), "unit": "GElem/s", "cores": 1,
+                                   "sample": "%d passes of numpy.cumsum(dtype=uint32) "
+                                             "(%.1f s)" % (npy_reps, npy_s)}}
+    return rec, all(ok)
 
 
 def headline(args, torch, ps):
@@ -106,20 +193,28 @@ def headline(args, torch, ps):
     def step():
         ps.scan_exclusive_u32(dev, want_total=False, total_dev=tot)
 
+    # The ceiling, before the timed region: the library's streaming copy in
+    # place over the same 1 GiB (the scan's traffic and memory pattern with
+    # none of its work), and out of place.  Median of per-launch events.
+    scratch_copy = torch.empty_like(dev)
+    for _ in range(3):
+        ps.copy_u32(scratch_copy, scratch_copy)
+    ceil_in = float(np.median(timed_launches(torch, lambda: ps.copy_u32(scratch_copy, scratch_copy),
+                                             20)))
+    ceil_out = float(np.median(timed_launches(torch, lambda: ps.copy_u32(dev, scratch_copy), 20)))
+    del scratch_copy
+    ceiling_gbs = 8.0 * n / (min(ceil_in, ceil_out) * 1e-3) / 1e9
+    # The scan's launches one at a time (an event pair around each), for
+    # comparison with the profiler's per-kernel durations.
+    isolated = timed_launches(torch, step, max(10, args.steps))
+
     for _ in range(args.warmup):
         step()
-    per_launch, wall = timed_launches(torch, step, args.steps)
+    wall, region = timed_region(torch, step, args.steps)
     ms_step = wall / args.steps
-    avg_launch = float(np.mean(per_launch))
+    avg_launch = region / args.steps
     achieved = 8.0 * n / (avg_launch * 1e-3) / 1e9
-
-    # The copy ceiling: the same 8 bytes per element, no scan.
-    dst = torch.empty_like(dev)
-    for _ in range(3):
-        ps.copy_u32(dev, dst)
-    cp, _ = timed_launches(torch, lambda: ps.copy_u32(dev, dst), max(10, args.steps // 2))
-    copy_gbs = 8.0 * n / (float(np.mean(cp)) * 1e-3) / 1e9
-    del dst, dev
+    del dev
 
     traffic = measured_traffic(n)
     cpu, ok = cpu_baseline_scan(a, check_host) if not args.no_cpu else (None, None)
@@ -144,10 +239,17 @@ def headline(args, torch, ps):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "scan_pipelined_kernel" + SCAN_SHAPE, "avg_launch_ms": round(avg_launch, 5),
+                     "kernel": "scan_pipelined_kernel" + SCAN_SHAPE,
+                     "avg_launch_ms": round(avg_launch, 5),
+                     "avg_launch_source": "HIP events at the two ends of the timed region on the "
+                                          "launch stream, divided by the steps",
+                     "avg_launch_ms_isolated": round(float(np.mean(isolated)), 5),
+                     "median_launch_ms_isolated": round(float(np.median(isolated)), 5),
                      "algorithmic_bytes_per_launch": 8 * n,
-                     "copy_kernel_gbs": round(copy_gbs, 1),
-                     "frac_of_copy": round(achieved / copy_gbs, 4)},
+                     "ceiling_gbs": round(ceiling_gbs, 1),
+                     "ceiling_kernel": "ceiling_copy_kernel<512, 16> (copy_u32), median launch: "
+                                       "in place %.4f ms, out of place %.4f ms" % (ceil_in, ceil_out),
+                     "frac_of_ceiling": round(achieved / ceiling_gbs, 4)},
         "cpu_baseline": cpu,
         "bit_exact_vs_oracle": ok,
     }
@@ -159,15 +261,23 @@ def suite(args, torch, ps):
     With --hbm-rows only the HBM-sized rows run (no 2^24 / 2^16 scans), so
     every kernel runs at one size -- what the profile summaries group by."""
     out = []
+    # Writing 768 MiB pushes the last call's lines out of the L2s and of
+    # the 256 MB Infinity Cache, so no timed launch starts on cached data.
+    flush_buf = torch.empty(3 << 26, dtype=torch.int32, device="cuda")
 
-    def row(name, n, bytes_per_elem, fn, reps=20, warm=3):
-        # Launches back to back, each bracketed by events on the stream: the
-        # host issues the next call while the GPU runs this one, so a launch's
-        # time is the GPU's, not the host's call overhead (except where a call
-        # is shorter than that overhead: the 2^16 rows are latencies).
+    def flush():
+        flush_buf.zero_()
+
+    def row(name, n, bytes_per_elem, fn, reps=20, warm=3, before=None):
+        # Each launch bracketed by events on the stream.  Rows that scan in
+        # place pass `before`, which puts the pristine input back (and
+        # flushes the caches) outside the events, so every timed launch
+        # works on the workload itself, never on an earlier launch's output.
         for _ in range(warm):
+            if before is not None:
+                before()
             fn()
-        times, _ = timed_launches(torch, fn, reps)
+        times = timed_launches(torch, fn, reps, before=before)
         med = float(np.median(times))
         rec = {"row": name, "n": n, "median_ms": round(med, 5), "min_ms": round(min(times), 5),
                "gelem_s": round(n / (med * 1e-3) / 1e9, 3),
@@ -181,46 +291,74 @@ def suite(args, torch, ps):
     if not args.hbm_rows:
         sizes += [(workloads.N_SCAN_MID, "2^24 (cache-resident)"), (workloads.N_SCAN_SMALL, "2^16")]
     for n, label in sizes:
-        d = torch.from_numpy(workloads.uniform_u32(n, 202).view(np.int32)).to("cuda")
-        row("scan exclusive lookback n=" + label, n, 8, lambda: ps.scan_exclusive_u32(d, want_total=False))
-        row("scan inclusive lookback n=" + label, n, 8, lambda: ps.scan_inclusive_u32(d, want_total=False))
+        pristine = torch.from_numpy(workloads.uniform_u32(n, 202).view(np.int32)).to("cuda")
+        d = torch.empty_like(pristine)
+        dst = torch.empty_like(pristine)
+        tot = torch.empty(1, dtype=torch.int32, device="cuda")
+        big = n >= workloads.N_SCAN_LARGE
+
+        def restore():
+            d.copy_(pristine)
+            if big:
+                flush()
+
+        def restore_cached():
+            d.copy_(pristine)     # cache-resident rows: the copy leaves d in cache
+
+        rs = restore if big else restore_cached
+        row("scan exclusive lookback n=" + label, n, 8,
+            lambda: ps.scan_exclusive_u32(d, want_total=False, total_dev=tot), before=rs)
+        row("scan inclusive lookback n=" + label, n, 8,
+            lambda: ps.scan_inclusive_u32(d, want_total=False, total_dev=tot), before=rs)
         row("scan exclusive lookback_tile n=" + label, n, 8,
-            lambda: ps.scan_u32_ex(d, algo="lookback_tile", want_total=False))
+            lambda: ps.scan_u32_ex(d, algo="lookback_tile", want_total=False, total_dev=tot),
+            before=rs)
         row("scan exclusive threepass n=" + label, n, 12,
-            lambda: ps.scan_u32_ex(d, algo="threepass", want_total=False))
-        dst = torch.empty_like(d)
-        row("copy n=" + label, n, 8, lambda: ps.copy_u32(d, dst))
-        if n == workloads.N_SCAN_LARGE:
+            lambda: ps.scan_u32_ex(d, algo="threepass", want_total=False, total_dev=tot),
+            before=rs)
+        row("copy in place n=" + label, n, 8, lambda: ps.copy_u32(d, d), before=rs)
+        row("copy n=" + label, n, 8, lambda: ps.copy_u32(pristine, dst),
+            before=flush if big else None)
+        if big:
             # The other integer operators (scan 8 B/element, reduction 4).
             for op in ("mul", "and", "or", "xor", "min", "max"):
                 row("scan exclusive %s n=%s" % (op, label), n, 8,
-                    lambda: ps.scan_op_u32(d, op, want_total=False))
+                    lambda: ps.scan_op_u32(d, op, want_total=False, total_dev=tot), before=rs)
             for op in ("add", "max"):
                 row("reduce %s n=%s" % (op, label), n, 4,
-                    lambda: ps.reduce_op_u32(d, op, want_total=False, total_dev=dst[:1]))
-        del d, dst
+                    lambda: ps.reduce_op_u32(pristine, op, want_total=False, total_dev=tot),
+                    before=flush)
+        del d, dst, pristine
     # u64 values at the same byte size (scan 16 B/element, reduction 8).
-    d = torch.from_numpy(workloads.uniform_u64(workloads.N_SCAN_U64, workloads.SEED_SCAN_U64)
-                         .view(np.int64)).to("cuda")
+    pristine64 = torch.from_numpy(workloads.uniform_u64(workloads.N_SCAN_U64, workloads.SEED_SCAN_U64)
+                                  .view(np.int64)).to("cuda")
+    d = torch.empty_like(pristine64)
     tot = torch.empty(1, dtype=torch.int64, device="cuda")
+
+    def restore64():
+        d.copy_(pristine64)
+        flush()
     for op in ("add", "max"):
         row("scan exclusive u64 %s n=2^27" % op, d.numel(), 16,
-            lambda: ps.scan_op_u64(d, op, want_total=False))
+            lambda: ps.scan_op_u64(d, op, want_total=False, total_dev=tot), before=restore64)
     row("reduce u64 add n=2^27", d.numel(), 8,
-        lambda: ps.reduce_op_u64(d, "add", want_total=False, total_dev=tot))
-    del d, tot
+        lambda: ps.reduce_op_u64(pristine64, "add", want_total=False, total_dev=tot),
+        before=flush)
+    del d, tot, pristine64
+    # The rows below read inputs they never write; `flush` keeps each timed
+    # launch from finding them in the caches.
     for p in (0.5, 0.01, 0.99):
         f = torch.from_numpy(workloads.compact_flags(p)).to("cuda")
         o = torch.empty_like(f)
         row("compact p=%g n=2^26" % p, f.numel(), 8,
-            lambda: ps.compact_flags_u32(f, out=o, want_count=False))
+            lambda: ps.compact_flags_u32(f, out=o, want_count=False), before=flush)
         del f, o
     v = torch.from_numpy(workloads.seg_values().view(np.int32)).to("cuda")
     o = torch.empty_like(v)
     for L in workloads.SEG_LENS:
         sums = torch.empty((v.numel() + L - 1) // L, dtype=torch.int32, device="cuda")
         row("segscan L=%d n=2^26" % L, v.numel(), 8 + 4.0 / L,
-            lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums))
+            lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums), before=flush)
     # Irregular segments from head flags: value + flag read, output written
     # (12 B per element) and one 4-byte total per segment.
     f_means = (16, 1 << 20)
@@ -229,7 +367,8 @@ def suite(args, torch, ps):
         nseg = int(fl.count_nonzero().item())
         sums = torch.empty(v.numel(), dtype=torch.int32, device="cuda")
         row("segscan flags mean=%d n=2^26" % mean, v.numel(), 12 + 4.0 * nseg / v.numel(),
-            lambda: ps.segscan_flags_u32(v, fl, out=o, seg_sums=sums, want_nsegs=False))
+            lambda: ps.segscan_flags_u32(v, fl, out=o, seg_sums=sums, want_nsegs=False),
+            before=flush)
         del fl, sums
     del v, o
     # Runs laid out by owner: the ends (8 B per owner), the -1 slots (4 B per
@@ -260,10 +399,11 @@ def suite(args, torch, ps):
         k = torch.from_numpy(gen().view(np.int32)).to("cuda")
         perm = torch.empty_like(k)
         row("radix 1-bit x32 %s n=2^25" % kind, k.numel(), 508,
-            lambda: ps.radix_perm_u32(k, 1, perm=perm), reps=5, warm=1)
+            lambda: ps.radix_perm_u32(k, 1, perm=perm), reps=5, warm=1, before=flush)
         row("radix 4-bit x8 %s n=2^25" % kind, k.numel(), 152,
-            lambda: ps.radix_perm_u32(k, 4, perm=perm), reps=5, warm=1)
+            lambda: ps.radix_perm_u32(k, 4, perm=perm), reps=5, warm=1, before=flush)
         del k, perm
+    del flush_buf
     return out
 
 
@@ -291,7 +431,7 @@ def algorithmic_bytes(name, grid):
     big = grid >= (1 << 16)            # threads: a data pass, not a table scan
     n28, n27, n26, n25 = 1 << 28, 1 << 27, 1 << 26, 1 << 25
     table = [
-        ("scan_pipelined_kernel", 8 * n28), ("copy_kernel", 8 * n28),
+        ("scan_pipelined_kernel", 8 * n28), ("ceiling_copy_kernel", 8 * n28),
         ("reduce_blocks_kernel", 4 * n28), ("compact_kernel", 8 * n26),
         ("segscan_independent_kernel", 8 * n26 + 4 * (n26 // 16)),
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
@@ -317,7 +457,7 @@ def algorithmic_bytes(name, grid):
         last = ", false, true>" in name
         return (12 if first or last else 16) * n25
     return None
-COPY_KERNEL = "libscan::copy_kernel"
+COPY_KERNEL = "libscan::ceiling_copy_kernel"
 SCAN_KERNEL = "libscan::scan_pipelined_kernel"
 SCAN_SHAPE = "<512, 16, false, libscan::OpAdd>"    # the exclusive add scan's default shape
 
@@ -365,7 +505,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
             _short(name), grid, calls, tot / 1e3, avg / 1e3, 100.0 * tot / total, gbs))
         if SCAN_KERNEL in name and SCAN_SHAPE in name:
             scan_us = avg / 1e3
-        if COPY_KERNEL in name and grid >= (1 << 20):
+        if COPY_KERNEL in name:
             copy_us = avg / 1e3
     lines.append("")
     if scan_us:
@@ -374,7 +514,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
                      % (scan_us, 8.0 * n / (scan_us * 1e-6) / 1e9,
                         100.0 * 8.0 * n / (scan_us * 1e-6) / 8e12))
     if copy_us:
-        lines.append("Copy kernel over the same 1 GiB: average %.2f us = %.1f GB/s." %
+        lines.append("Streaming copy (the ceiling, in place and out of place) over the same "
+                     "1 GiB: average %.2f us = %.1f GB/s." %
                      (copy_us, 8.0 * n / (copy_us * 1e-6) / 1e9))
     with open(os.path.join(prof, "%s_kernel_trace.md" % tag), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -389,7 +530,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
         return {(r[0], r[1]): (r[2], r[3]) for r in rs}
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
-    copies = [k for k in fetch if COPY_KERNEL in k[0] and "<256, 8>" in k[0]]
+    # Every dispatch of the copy in these runs moves 2^28 u32 (1 GiB read,
+    # 1 GiB written), in place or out of place.
+    copies = [k for k in fetch if COPY_KERNEL in k[0]]
     if not copies:
         raise SystemExit("the copy kernel is missing from the counter runs")
     cal = max(copies, key=lambda k: k[1])               # the 2^28 copy: the largest grid
@@ -400,7 +543,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
         "the HBM-sized rows of bench.py --suite" if suite else "U32 exclusive scan, n = 2^28"), "",
         "Commands (each counter in a run of its own):", ""]
     lines += ["    " + c for c in cmds[1:]] + [""]
-    lines += ["Calibration on `copy_kernel<256, 8>` over 2^28 u32 (1 GiB read and 1 GiB "
+    lines += ["Calibration on `ceiling_copy_kernel<512, 16>` over 2^28 u32 (1 GiB read and 1 GiB "
               "written per dispatch): FETCH_SIZE reads %.1f KiB, WRITE_SIZE %.1f KiB, so the "
               "scale factors are %.4f (fetch) and %.4f (write)." %
               (fetch[cal][1], write[cal][1], f_fetch, f_write), "",

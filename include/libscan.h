@@ -396,13 +396,26 @@ int radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int bits_per
 /* ------------------------------------------------------------------------ */
 
 /*
- * dst[i] = src[i] for i < n with the same 16-byte loads and stores the scans
- * use: the practical bandwidth ceiling a streaming kernel reaches, timed
- * beside the scans, and the known-size kernel that calibrates the HBM byte
- * counters.  src and dst must not overlap.
- * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_HIP.
+ * dst[i] = src[i] for i < n: a measurement aid, not part of the pages'
+ * method.  It moves memory the way the pipelined scan does -- tiles taken in
+ * order from the scratch header's ticket, two per workgroup on a grid that
+ * fills the GPU once, each tile's loads landed before the previous tile's
+ * stores go out -- with none of the scan's arithmetic or carry, and with
+ * write-through stores.  So it is the read + write ceiling the scan is
+ * measured against (in place, dst == src, it is the scan's exact traffic),
+ * and the known-size kernel that calibrates the HBM byte counters.
+ *
+ * src, dst     device, n u32; dst == src (in place) or no overlap at all.
+ *              16-byte aligned arrays with n a multiple of 4 take the
+ *              streaming kernel; anything else a plain element copy.
+ * scratch      device scratch of at least copy_scratch_bytes(n) bytes (the
+ *              256-byte header); it may be shared with the scans.
+ * Errors: ERR_NULL, ERR_ALIGN, ERR_SIZE (n > LIBSCAN_MAX_N), ERR_SCRATCH,
+ * ERR_HIP.
  */
-int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream);
+size_t copy_scratch_bytes(uint64_t n);
+int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, void *scratch, size_t scratch_bytes,
+             hipStream_t stream);
 
 #ifdef __cplusplus
 }

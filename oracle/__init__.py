@@ -50,6 +50,9 @@ def load():
     lib.oracle_segscan_flags_u32.restype = ctypes.c_uint64
     lib.oracle_scan_blocked_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint, ctypes.c_int, u32p]
     lib.oracle_scan_blocked_u32.restype = ctypes.c_int
+    lib.oracle_scan_blocked_threads_u32.argtypes = [u32p, ctypes.c_uint64, ctypes.c_uint,
+                                                     ctypes.c_int, ctypes.c_uint, u32p]
+    lib.oracle_scan_blocked_threads_u32.restype = ctypes.c_int
     lib.oracle_segscan_u32.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint64, u32p]
     lib.oracle_segscan_u32.restype = ctypes.c_uint64
     lib.oracle_compact_flags.argtypes = [i32p, i32p, ctypes.c_uint64]
@@ -144,6 +147,19 @@ def scan_blocked_u32(a, b, inclusive=False):
                                         1 if inclusive else 0, ctypes.byref(total))
     if rc != 0:
         raise ValueError("blocked scan needs a power-of-two length, got %d" % out.size)
+    return out, int(total.value)
+
+
+def scan_blocked_threads_u32(a, b, threads, inclusive=False):
+    """The blocked three-pass scan at fork depth b with passes 1 and 3 on
+    `threads` host threads (n must be a power of two); returns (out, total)."""
+    out = _u32(a).copy()
+    total = ctypes.c_uint32(0)
+    rc = load().oracle_scan_blocked_threads_u32(_ptr(out, ctypes.c_uint32), out.size, int(b),
+                                                1 if inclusive else 0, int(threads),
+                                                ctypes.byref(total))
+    if rc != 0:
+        raise ValueError("threaded blocked scan: n must be a power of two and threads >= 1")
     return out, int(total.value)
 
 

@@ -16,8 +16,8 @@ LIB = os.path.join(HERE, "liboracle.so")
 def build(verbose: bool = False) -> str:
     """Build liboracle.so from oracle.c; returns its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
-           "-o", tmp, SRC]
+    cmd = ["gcc", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-O2", "-Wall", "-Wextra", "-Werror",
+           "-fPIC", "-shared", "-pthread", "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

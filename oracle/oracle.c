@@ -33,6 +33,7 @@
  * pages, closed forms, numpy library routines, brute force); none is
  * "parity unpinned".
  */
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -312,6 +313,103 @@ int oracle_scan_blocked_u32(uint32_t *a, uint64_t n, unsigned b, int inclusive, 
         return -1;
     *total = blocked_scan(a, n, b, inclusive, 1);
     return 0;
+}
+
+/*
+ * The same three passes with passes 1 and 3 spread over `threads` host
+ * threads, the blocks dealt out in contiguous runs; pass 2 stays one lane
+ * (d < 12) or the nested scheme, exactly as in blocked_scan.  [cairn] "scan":
+ * a parallel scan runs as two passes over the lane pool with a sequential
+ * step between; every grouping of an integer sum gives the same bits.  Used
+ * as the CPU figure beside the GPU, and checked against O1 at every depth.
+ */
+struct blocked_job {
+    uint32_t *a;
+    uint32_t *s;
+    uint64_t first, last;     /* blocks [first, last) */
+    uint64_t bsize;
+    int inclusive;
+    int pass;                 /* 1: block sums, 3: rescans */
+};
+
+static void *blocked_worker(void *arg)
+{
+    struct blocked_job *j = (struct blocked_job *)arg;
+    for (uint64_t i = j->first; i < j->last; ++i) {
+        if (j->pass == 1) {
+            uint32_t acc = 0;
+            for (uint64_t k = i * j->bsize; k < (i + 1) * j->bsize; ++k)
+                acc += j->a[k];
+            j->s[i] = acc;
+        } else {
+            (void)one_lane_walk(j->a, i * j->bsize, j->bsize, j->s[i], j->inclusive);
+        }
+    }
+    return NULL;
+}
+
+/* Runs one pass over all blocks on `threads` threads; 0 on success. */
+static int blocked_pass(struct blocked_job *jobs, pthread_t *tid, unsigned threads, int pass)
+{
+    unsigned started = 0;
+    int rc = 0;
+    for (unsigned t = 0; t < threads; ++t) {
+        jobs[t].pass = pass;
+        if (t == 0)
+            continue;                       /* the calling thread runs job 0 */
+        if (pthread_create(&tid[t], NULL, blocked_worker, &jobs[t]) != 0) {
+            rc = -1;
+            break;
+        }
+        started = t;
+    }
+    if (rc == 0)
+        blocked_worker(&jobs[0]);
+    for (unsigned t = 1; t <= started; ++t)
+        pthread_join(tid[t], NULL);
+    return rc;
+}
+
+/*
+ * Returns 0 and sets *total on success; -1 when n is zero or not a power of
+ * two, or threads is 0, or a thread cannot be started.
+ */
+int oracle_scan_blocked_threads_u32(uint32_t *a, uint64_t n, unsigned b, int inclusive,
+                                    unsigned threads, uint32_t *total)
+{
+    if (n == 0 || (n & (n - 1)) != 0 || threads == 0)
+        return -1;
+    unsigned lg = floor_log2_u64(n);
+    unsigned d = b < lg ? b : lg;
+    uint64_t blocks = (uint64_t)1 << d;
+    uint64_t bsize = (uint64_t)1 << (lg - d);
+    if (threads > blocks)
+        threads = (unsigned)blocks;
+    uint32_t *s = (uint32_t *)calloc((size_t)blocks, sizeof(uint32_t));
+    struct blocked_job *jobs = (struct blocked_job *)calloc(threads, sizeof(struct blocked_job));
+    pthread_t *tid = (pthread_t *)calloc(threads, sizeof(pthread_t));
+    if (!s || !jobs || !tid)
+        abort();
+    for (unsigned t = 0; t < threads; ++t) {
+        jobs[t].a = a;
+        jobs[t].s = s;
+        jobs[t].first = blocks * t / threads;
+        jobs[t].last = blocks * (t + 1) / threads;
+        jobs[t].bsize = bsize;
+        jobs[t].inclusive = inclusive;
+    }
+    int rc = blocked_pass(jobs, tid, threads, 1);
+    if (rc == 0) {
+        if (d < 12)
+            *total = one_lane_walk(s, 0, blocks, 0, 0);
+        else
+            *total = blocked_scan(s, blocks, d / 2, 0, 0);
+        rc = blocked_pass(jobs, tid, threads, 3);
+    }
+    free(tid);
+    free(jobs);
+    free(s);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------- */

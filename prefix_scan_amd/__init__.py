@@ -117,7 +117,9 @@ def lib():
         L.radix_scratch_bytes.restype = sz
         L.radix_perm_u32.argtypes = [vp, vp, u64, i32, vp, sz, vp]
         L.radix_perm_u32.restype = i32
-        L.copy_u32.argtypes = [vp, vp, u64, vp]
+        L.copy_scratch_bytes.argtypes = [u64]
+        L.copy_scratch_bytes.restype = sz
+        L.copy_u32.argtypes = [vp, vp, u64, vp, sz, vp]
         L.copy_u32.restype = i32
         L.scan_u32_noalloc.argtypes = [vp, u64, i32, vp, vp]
         L.scan_u32_noalloc.restype = i32
@@ -514,11 +516,14 @@ def scan_u32_noalloc(data, inclusive=False, total_dev=None, stream=None):
 
 
 def copy_u32(src, dst, stream=None):
-    """dst <- src with the library's streaming copy kernel."""
+    """dst <- src with the library's streaming copy (dst may be src: an
+    in-place pass with the scan's memory traffic and none of its work)."""
     _dev_u32(src, "src")
     _dev_u32(dst, "dst")
     if dst.numel() != src.numel():
         raise ValueError("src and dst differ in size")
-    sh, _ = _stream_handle(src.device, stream)
-    _check(lib().copy_u32(_ptr(src), _ptr(dst), src.numel(), sh), "copy_u32")
+    sh, s = _stream_handle(src.device, stream)
+    scr = _scratch_for(src.device, s, lib().copy_scratch_bytes(src.numel()))
+    _check(lib().copy_u32(_ptr(src), _ptr(dst), src.numel(), _ptr(scr), scr.numel(), sh),
+           "copy_u32")
     return dst

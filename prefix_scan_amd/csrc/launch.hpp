@@ -79,7 +79,8 @@ size_t scan_threepass_body_bytes(unsigned d);
 unsigned threepass_auto_depth(uint64_t n);
 unsigned floor_log2(uint64_t n);
 
-hipError_t launch_copy(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream);
+hipError_t launch_copy(const uint32_t *src, uint32_t *dst, uint64_t n, const Scratch &s,
+                       hipStream_t stream);
 
 // Scan under operator `op` (0 add_wrap, 1 mul_wrap, 2 and, 3 or, 4 xor,
 // 5 min, 6 max), pipelined; and one u32 written on the stream.

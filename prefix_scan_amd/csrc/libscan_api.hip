@@ -751,7 +751,14 @@ int scan_u32_noalloc(uint32_t *data, uint64_t n, int inclusive, uint32_t *total_
     return hip_status(e);
 }
 
-int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream)
+size_t copy_scratch_bytes(uint64_t n)
+{
+    (void)n;
+    return with_header(0);
+}
+
+int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, void *scratch, size_t scratch_bytes,
+             hipStream_t stream)
 {
     if (n > LIBSCAN_MAX_N)
         return LIBSCAN_ERR_SIZE;
@@ -759,9 +766,16 @@ int copy_u32(const uint32_t *src, uint32_t *dst, uint64_t n, hipStream_t stream)
         return LIBSCAN_ERR_ALIGN;
     if (n == 0)
         return LIBSCAN_OK;
-    if (!src || !dst)
+    if (!src || !dst || !scratch)
         return LIBSCAN_ERR_NULL;
-    return hip_status(launch_copy(src, dst, n, stream));
+    Scratch s;
+    if (!carve(scratch, scratch_bytes, 0, &s))
+        return LIBSCAN_ERR_SCRATCH;
+    // The copy draws tiles from the header's ticket exactly as the scans do.
+    hipError_t e = prepare_state(s, kKindDesc, 0, 0, 1, stream);
+    if (e == hipSuccess)
+        e = launch_copy(src, dst, n, s, stream);
+    return hip_status(e);
 }
 
 }  // extern "C"

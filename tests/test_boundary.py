@@ -142,9 +142,14 @@ def test_radix_argument_errors():
 
 def test_copy_argument_errors():
     L = ps.lib()
-    assert L.copy_u32(NULLP, FAKE, 16, NULLP) == ps.ERR_NULL
-    assert L.copy_u32(FAKE, ctypes.c_void_p(0x100001), 16, NULLP) == ps.ERR_ALIGN
-    assert L.copy_u32(NULLP, NULLP, 0, NULLP) == ps.OK
+    big = 1 << 16
+    assert L.copy_scratch_bytes(1 << 28) >= 256
+    assert L.copy_u32(NULLP, FAKE, 16, FAKE, big, NULLP) == ps.ERR_NULL
+    assert L.copy_u32(FAKE, FAKE, 16, NULLP, big, NULLP) == ps.ERR_NULL
+    assert L.copy_u32(FAKE, ctypes.c_void_p(0x100001), 16, FAKE, big, NULLP) == ps.ERR_ALIGN
+    assert L.copy_u32(FAKE, FAKE, 16, FAKE, 100, NULLP) == ps.ERR_SCRATCH
+    assert L.copy_u32(FAKE, FAKE, (1 << 36) + 1, FAKE, big, NULLP) == ps.ERR_SIZE
+    assert L.copy_u32(NULLP, NULLP, 0, NULLP, 0, NULLP) == ps.OK
 
 
 def test_noalloc_scan_argument_errors():

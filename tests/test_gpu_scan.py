@@ -170,13 +170,32 @@ def test_empty():
 
 
 def test_copy_kernel():
-    for n in (1, 4097, (1 << 22) + 3):
+    # The streaming copy (16-byte aligned, n a multiple of 4: whole tiles
+    # and a cut last tile) and the plain copy (everything else), out of
+    # place and in place, on poisoned destinations.
+    for n in (4, 4096, 32768, 32772, (1 << 22) + 12, 1, 4097, (1 << 22) + 3):
         a = workloads.small_random_u32(n, 4)
         src = to_dev(a)
         dst = poisoned(n, poison_value(a))
         ps.copy_u32(src, dst)
-        assert np.array_equal(to_host_u32(dst), a)
+        assert np.array_equal(to_host_u32(dst), a), n
+        ps.copy_u32(src, src)
+        assert np.array_equal(to_host_u32(src), a), n
     src = to_dev(a, 1)
     dst = poisoned(a.size, poison_value(a), 2)
     ps.copy_u32(src, dst)
     assert np.array_equal(to_host_u32(dst), a)
+
+
+def test_copy_shares_scratch_with_the_scans():
+    # The copy draws from the same header ticket as the pipelined scan.
+    a = workloads.small_random_u32((1 << 22) + 4, 5)
+    b = workloads.small_random_u32(1 << 23, 6)
+    ref, _ = oracle.scan_exclusive_u32(b)
+    for _ in range(3):
+        src, dst = to_dev(a), poisoned(a.size, poison_value(a))
+        ps.copy_u32(src, dst)
+        t = to_dev(b)
+        ps.scan_u32_ex(t, algo="lookback")
+        assert np.array_equal(to_host_u32(dst), a)
+        assert first_mismatch(to_host_u32(t), ref) is None

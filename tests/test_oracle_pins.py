@@ -166,6 +166,41 @@ def test_blocked_rejects_non_power_of_two():
         oracle.scan_blocked_u32(np.ones(3, dtype=np.uint32), 1)
 
 
+# The three passes with passes 1 and 3 on host threads (the CPU baseline):
+# the same bits as numpy's wrapping cumsum at every depth and thread count,
+# including more threads than blocks and the nested pass 2 (d >= 12).
+@pytest.mark.parametrize("lg", [0, 1, 5, 10, 14])
+def test_blocked_threads_every_b_and_thread_count(lg):
+    n = 1 << lg
+    a = workloads.small_random_u32(n, 700 + lg)
+    for inclusive in (False, True):
+        incl = np.cumsum(a, dtype=np.uint32)
+        ref = incl if inclusive else np.concatenate([[0], incl[:-1]]).astype(np.uint32)
+        tref = int(incl[-1])
+        for b in sorted({0, 1, 2, lg // 2, lg, lg + 2, 12, 13}):
+            for threads in (1, 2, 3, 8, 33):
+                out, t = oracle.scan_blocked_threads_u32(a, b, threads, inclusive)
+                assert t == tref, (lg, b, threads)
+                assert np.array_equal(out, ref), (lg, b, threads, inclusive)
+
+
+def test_blocked_threads_workload_depth_of_the_baseline():
+    # The depth the benchmark uses: ceil(log2 T) + 2 for T host threads.
+    a = workloads.uniform_u32(1 << 20, 31)
+    ref, tref = oracle.scan_exclusive_u32(a)
+    for T in (1, 4, 8, 16, 64):
+        b = (T - 1).bit_length() + 2
+        out, t = oracle.scan_blocked_threads_u32(a, b, T)
+        assert t == tref and np.array_equal(out, ref), T
+
+
+def test_blocked_threads_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.scan_blocked_threads_u32(np.ones(3, dtype=np.uint32), 1, 2)
+    with pytest.raises(ValueError):
+        oracle.scan_blocked_threads_u32(np.ones(4, dtype=np.uint32), 1, 0)
+
+
 # --------------------------------------------------------------------------
 # O2 segmented scan and sums
 # --------------------------------------------------------------------------
