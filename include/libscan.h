@@ -102,8 +102,9 @@ int libscan_scratch_init(void *scratch, size_t scratch_bytes, hipStream_t stream
  *   bendlib "scan.bend source", header comment and API: exclusive makes a[j]
  *   the sum a[0] + .. + a[j-1] (a[0] becomes 0), inclusive makes a[j] the sum
  *   a[0] + .. + a[j]; both return the total a[0] + .. + a[n-1]; sums wrap at
- *   2^32.  CAIRN "Concurrency", section "scan": a device scan whose total
- *   nobody binds leaves its prefixes in device memory and nothing waits.
+ *   2^32.  CAIRN "Concurrency", section "scan": if no one takes a device
+ *   scan's total, the prefixes stay on the device and the host never
+ *   blocks on them.
  *
  * data         device, n u32, read then overwritten in place.
  * n            element count; 0 is a no-op with total 0.
@@ -184,8 +185,8 @@ int scan_u32_noalloc(uint32_t *data, uint64_t n, int inclusive, uint32_t *total_
 /* ------------------------------------------------------------------------ */
 
 /*
- * CAIRN "Concurrency", section "reduce and compact": a reduction combines
- * one value per index into a total, and its integer operators are add_wrap,
+ * CAIRN "Concurrency", section "reduce and compact": a reduction folds the
+ * values of all indices into one result; on integers it may use add_wrap,
  * mul_wrap, &, |, ^, min and max; section "scan": a scan takes the same
  * operators, inclusive (out[i] = e(0) op .. op e(i)) or exclusive (what came
  * before i).  Values are 32-bit words; MIN and MAX compare them as
@@ -279,11 +280,11 @@ int segscan_flags_u32(const uint32_t *in, const int32_t *flags, uint32_t *out, u
 
 /*
  * entelechy "parallel" package, kernels runs_ends, runs_entries, runs_slots
- * and the function owner (interface "runs").  From each owner's count of
- * entries: where each owner's run ends, an inclusive prefix sum of the
- * counts, so owner i's run is [ends[i] - counts[i], ends[i]); how many
- * entries the runs hold, at least one so the row they are laid in is never
- * empty; that row, every slot -1; and the owner of an entry.
+ * and the function owner (interface "runs").  Given how many entries each
+ * owner has: the end of every owner's run (the counts' inclusive prefix
+ * sums; owner i then holds slots ends[i] - counts[i] .. ends[i] - 1); the
+ * number of entries, never below one, so the row of slots always exists;
+ * that row with every slot -1; and which owner an entry belongs to.
  *
  * runs_layout_u32: ends[i] = counts[0] + .. + counts[i] (mod 2^32, as the
  *   scan) for n u32 counts into a separate array `ends` (or ends == counts,

@@ -527,7 +527,7 @@ int oracle_stable_argsort_u32(const uint32_t *keys, int32_t *perm, uint64_t n)
  *     sort_place -- a zero lands at its rank among the zeros, zeros[i] - 1;
  *                   a one lands behind all Z zeros at its rank among the
  *                   ones, Z + (i + 1 - zeros[i]) - 1;
- *                   each place is written by exactly one element.
+ *                   no two elements share a place.
  * Keys are full 32-bit unsigned values, so 32 one-bit passes run (the page
  * allows 1..31 bits of non-negative keys; the unsigned widening is this
  * build's reading).
@@ -609,10 +609,10 @@ int oracle_radix_perm_u32(const uint32_t *keys, int32_t *perm, uint64_t n, int b
 /* ------------------------------------------------------------------------- */
 
 /*
- * [ent] runs_ends: where each owner's run ends -- an inclusive prefix sum of
- * the counts, so owner i's run is [ends[i] - counts[i], ends[i]).
- * [ent] runs_entries: how many entries the runs hold, at least one, so the
- * row they are laid in is never empty.
+ * [ent] runs_ends: the end of every owner's run, the counts' inclusive
+ * prefix sums; owner i then holds slots ends[i] - counts[i] .. ends[i] - 1.
+ * [ent] runs_entries: the number of entries, never below one, so the row of
+ * slots always exists.
  * Readings: counts are unsigned 32-bit and the sums wrap at 2^32 as the scan's
  * do; for n == 0 the runs hold nothing and entries is 1.
  * Writes ends[0..n) and returns entries = max(ends[n-1], 1).

@@ -1,10 +1,10 @@
 // reduce_kernels.hip -- reduction of n u32 values under one integer operator
 // on gfx950.
 //
-// CAIRN "Concurrency", section "reduce and compact": a reduction combines
-// one value per index into a total under add_wrap, mul_wrap, &, |, ^, min or
-// max (unsigned or signed); the integer operators give the same total in any
-// order.  So a grid that fills the GPU walks the tiles round-robin, each
+// CAIRN "Concurrency", section "reduce and compact": a reduction folds the
+// values of all indices into one result under add_wrap, mul_wrap, &, |, ^,
+// min or max (here unsigned or signed); for these integer operators the
+// result does not depend on the order of the fold.  So a grid that fills the GPU walks the tiles round-robin, each
 // workgroup folds its tiles into one partial (a thread's chunks, the wave,
 // the workgroup), and one workgroup folds the partials.  4 bytes read per
 // element.

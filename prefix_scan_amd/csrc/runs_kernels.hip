@@ -1,11 +1,11 @@
 // runs_kernels.hip -- entries laid out in runs by owner, on gfx950.
 //
 // entelechy "parallel" package, kernels runs_ends, runs_entries, runs_slots
-// and the function owner (interface "runs"): from each owner's count of
-// entries, where each owner's run ends (an inclusive prefix sum of the
-// counts, so owner i's run is [ends[i] - counts[i], ends[i])), how many
-// entries there are (at least one), the row of -1 they are laid in, and the
-// owner of an entry.
+// and the function owner (interface "runs"): given how many entries each
+// owner has, the end of every owner's run (the counts' inclusive prefix
+// sums; owner i holds slots ends[i] - counts[i] .. ends[i] - 1), the number
+// of entries (never below one), the row of slots set to -1, and which owner
+// an entry belongs to.
 //
 //  * runs_ends_kernel: the out-of-place inclusive scan of the counts on the
 //    pipelined chained-carry driver (scan_op.hpp); its last tile writes

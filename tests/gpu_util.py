@@ -89,7 +89,7 @@ def poisoned_like_ref(ref, offset=0):
 
 
 def assert_bijection(perm, n):
-    """Every index 0..n-1 appears exactly once: each place written once."""
+    """Every index 0..n-1 appears once and only once."""
     p = np.asarray(perm).astype(np.int64)
     assert p.size == n and p.min(initial=0) >= 0 and p.max(initial=-1) < n, "indices out of range"
     counts = np.bincount(p, minlength=n)

@@ -8,8 +8,8 @@ orders (sorted, all equal, strictly decreasing).
 
 Every permutation is written into a buffer pre-filled with -2, an index no
 permutation holds, so a slot the sort never wrote fails; at the workload size
-the permutation is also checked to be a bijection (each place written by
-exactly one key, entelechy "parallel", sort_place).
+the permutation is also checked to be a bijection (no two keys land in one
+place, entelechy "parallel", sort_place).
 """
 import numpy as np
 import pytest
