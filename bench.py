@@ -482,6 +482,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, suite):
     tag = "suite" if suite else "scan_lookback_u32_n2p28"
     cmds = [c.replace(" [--suite --hbm-rows]", " --suite --hbm-rows" if suite else "")
              .replace(" [--suite]", " --suite" if suite else "") for c in PROFILE_COMMANDS]
+    if suite:
+        cmds = [c.replace("rocprof_out/", "rocprof_out/suite_") for c in cmds]
     n = 1 << 28
 
     # Kernel trace statistics, per kernel and grid (one workload each).
