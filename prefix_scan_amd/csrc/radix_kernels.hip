@@ -59,21 +59,64 @@ __global__ __launch_bounds__(BLOCK) void bit_ones_kernel(const uint32_t *__restr
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     constexpr int NW = BLOCK / kWave;
     __shared__ uint32_t s_part[NW][32];
-    uint32_t c[32];
+    // Bit counts in fields of a word, a few operations per key instead of
+    // one shift-and-add per bit.  Nibble stage: field j (bits 4j..4j+3) of
+    // nib[k] counts bit 4j + k over at most 15 keys.  Byte stage: byte i of
+    // lo[k] / hi[k] counts bit 8i + k / 8i + 4 + k over at most 255 keys.
+    // Totals: c[b].  Every thread takes 4 keys per chunk (zeros outside the
+    // array), so the stage counters are the same in every lane.
+    constexpr uint32_t kNibMask = 0x11111111u, kByteMask = 0x0F0F0F0Fu;
+    uint32_t nib[4], lo[4], hi[4], c[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        nib[k] = lo[k] = hi[k] = 0;
 #pragma unroll
     for (int b = 0; b < 32; ++b)
         c[b] = 0;
+    uint32_t in_nib = 0, in_byte = 0;       // keys held by each stage
+    auto byte_flush = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[8 * i + k] += (lo[k] >> (8 * i)) & 0xFFu;
+                c[8 * i + 4 + k] += (hi[k] >> (8 * i)) & 0xFFu;
+            }
+            lo[k] = hi[k] = 0;
+        }
+        in_byte = 0;
+    };
+    auto nib_flush = [&]() {
+        if (in_byte + in_nib > 255u)
+            byte_flush();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo[k] += nib[k] & kByteMask;
+            hi[k] += (nib[k] >> 4) & kByteMask;
+            nib[k] = 0;
+        }
+        in_byte += in_nib;
+        in_nib = 0;
+    };
     for (uint64_t vs = (uint64_t)blockIdx.x * T; vs < vhi; vs += (uint64_t)gridDim.x * T) {
         u32x4 x[V];
         load_tile<BLOCK, V>(kbase, vs, vlo, vhi, x);    // outside the array: key 0
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
+        for (int q = 0; q < V; ++q) {
+            if (in_nib + 4u > 15u)
+                nib_flush();
+            const uint32_t kv[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
 #pragma unroll
-            for (int b = 0; b < 32; ++b)
-                c[b] += ((x[k].x >> b) & 1u) + ((x[k].y >> b) & 1u) + ((x[k].z >> b) & 1u) +
-                        ((x[k].w >> b) & 1u);
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    nib[k] += (kv[j] >> k) & kNibMask;
+            }
+            in_nib += 4u;
         }
     }
+    nib_flush();
+    byte_flush();
     const uint32_t wave = threadIdx.x / kWave;
 #pragma unroll
     for (int b = 0; b < 32; ++b) {
@@ -658,11 +701,13 @@ hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bit
         hipError_t e = launch_fill_zero(ones, 32 * sizeof(uint32_t), stream);
         if (e != hipSuccess)
             return e;
-        uint64_t grid = (n + head + kRadixTile - 1) / kRadixTile;
-        if (grid > 2048)
-            grid = 2048;
-        hipLaunchKernelGGL((bit_ones_kernel<kBlock, kRadixChunks>), dim3((uint32_t)grid), blk, 0,
-                           stream, kuser, (uint64_t)head, n + head, ones);
+        // One round of resident workgroups walking the tiles.
+        auto ok = bit_ones_kernel<kBlock, kRadixChunks>;
+        uint64_t grid = (uint64_t)resident_grid((const void *)ok, kBlock);
+        if (grid > ntiles_user)
+            grid = ntiles_user;
+        hipLaunchKernelGGL(ok, dim3((uint32_t)grid), blk, 0, stream, kuser, (uint64_t)head, n + head,
+                           ones);
         const uint64_t nt_user = tiles_for(n, head, kR1Tile);
         const uint64_t nt_own = tiles_for(n, 0, kR1Tile);
         auto k_first = radix1_pass_kernel<kR1Block, kR1Chunks, true, false>;
