@@ -414,7 +414,9 @@ __device__ __forceinline__ void bucket_onehot(uint32_t b, bool valid, uint32_t &
     w1 = b < 2 ? 0u : one;
 }
 
-template <int BLOCK, int V, bool FIRST, bool LAST>
+// OFF32: every output offset in bytes fits 32 bits (n * 4 < 2^32), so the
+// stores address the outputs as a scalar base plus a 32-bit offset.
+template <int BLOCK, int V, bool FIRST, bool LAST, bool OFF32>
 __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
     const uint32_t *__restrict__ kbase, uint64_t vlo, uint64_t vhi,
     const uint32_t *__restrict__ iin, uint32_t *__restrict__ kout, uint32_t *__restrict__ iout,
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
     static_assert(T < (1u << 16), "bucket counts are 16-bit fields");
     __shared__ uint32_t s_c0[TS::NCELL], s_c1[TS::NCELL];
     __shared__ uint32_t s_key[T], s_idx[T];
-    __shared__ uint32_t s_tot[2], s_base[16], s_start[16];
+    __shared__ uint32_t s_tot[2], s_move[16];
     const uint64_t n = vhi - vlo;
 
     // One two-bit split of `valid` pairs held in (kk, ii), element order
@@ -460,9 +462,13 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
         __syncthreads();
         const uint32_t t0 = s_tot[0], t1 = s_tot[1];
         const uint32_t n0 = t0 & 0xFFFFu, n1 = t0 >> 16, n2 = t1 & 0xFFFFu;
-        const uint32_t start[4] = {0u, n0, n0 + n1, n0 + n1 + n2};
-        TS::template apply<false>(c0, w0, s_c0, 0u);
-        TS::template apply<false>(c1, w1, s_c1, 0u);
+        // Each bucket's start in the split order (0, n0, n0 + n1, n0 + n1 +
+        // n2), packed like the counters and added as the scans' carry, so
+        // each field of c0 / c1 becomes its bucket's start plus the rank
+        // inside the bucket: a key's slot is one field of one word.  No
+        // field exceeds 2T < 2^16.
+        TS::template apply<false>(c0, w0, s_c0, n0 << 16);
+        TS::template apply<false>(c1, w1, s_c1, (n0 + n1) | ((n0 + n1 + n2) << 16));
         __syncthreads();                        // every read of the previous order is done
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -475,8 +481,7 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
                     continue;
                 const uint32_t bkt = (kk[k][j] >> bit) & 3u;
                 const uint32_t word = bkt < 2 ? r0[j] : r1[j];
-                const uint32_t rank = (bkt & 1u) ? (word >> 16) : (word & 0xFFFFu);
-                const uint32_t p = start[bkt] + rank;
+                const uint32_t p = __builtin_amdgcn_ubfe(word, (bkt & 1u) << 4, 16);
                 s_key[p] = kk[k][j];
                 s_idx[p] = ii[k][j];
             }
@@ -562,15 +567,14 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
             }
         }
         split(kk, ii, shift + 2, valid);
-        // Where each digit's run starts in the tile and in the output.
+        // How far each digit's run moves: from where it starts in the
+        // sorted tile to its base in the output (mod 2^32).
         if (threadIdx.x < kWave) {
             const uint32_t d = lane_id();
             const uint32_t cnt = d < 16 ? b1 - b0 : 0u;
             const uint32_t incl = wave_incl_add(cnt);
-            if (d < 16) {
-                s_base[d] = b0;
-                s_start[d] = incl - cnt;
-            }
+            if (d < 16)
+                s_move[d] = b0 - (incl - cnt);
         }
         __syncthreads();
 #pragma unroll
@@ -579,10 +583,17 @@ __global__ __launch_bounds__(BLOCK) void digit_scatter_kernel(
             if (p < valid) {
                 const uint32_t kv = s_key[p];
                 const uint32_t d = (kv >> shift) & 15u;
-                const uint32_t dest = s_base[d] + (p - s_start[d]);
-                if (!LAST)
-                    kout[dest] = kv;
-                iout[dest] = s_idx[p];
+                const uint32_t dest = p + s_move[d];
+                if constexpr (OFF32) {
+                    const uint32_t off = dest * 4u;
+                    if (!LAST)
+                        *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(kout) + off) = kv;
+                    *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(iout) + off) = s_idx[p];
+                } else {
+                    if (!LAST)
+                        kout[dest] = kv;
+                    iout[dest] = s_idx[p];
+                }
             }
         }
         __syncthreads();                        // LDS is free for the next tile
@@ -748,9 +759,15 @@ hipError_t launch_radix(const uint32_t *keys, int32_t *perm, uint64_t n, int bit
         hipError_t e = launch_scan_table(hist, 16 * nt, spine, spine.total_slot(), stream);
         if (e != hipSuccess)
             return e;
-        auto sk = first ? digit_scatter_kernel<kScatterBlock, kScatterChunks, true, false>
-                        : (p == 7 ? digit_scatter_kernel<kScatterBlock, kScatterChunks, false, true>
-                                  : digit_scatter_kernel<kScatterBlock, kScatterChunks, false, false>);
+        // Outputs are the library's own key and index sides and the caller's
+        // permutation, each n entries from its start.
+        const bool off32 = n * 4 < (1ull << 32);
+        auto sk = off32 ? (first ? digit_scatter_kernel<kScatterBlock, kScatterChunks, true, false, true>
+                                 : (p == 7 ? digit_scatter_kernel<kScatterBlock, kScatterChunks, false, true, true>
+                                           : digit_scatter_kernel<kScatterBlock, kScatterChunks, false, false, true>))
+                        : (first ? digit_scatter_kernel<kScatterBlock, kScatterChunks, true, false, false>
+                                 : (p == 7 ? digit_scatter_kernel<kScatterBlock, kScatterChunks, false, true, false>
+                                           : digit_scatter_kernel<kScatterBlock, kScatterChunks, false, false, false>));
         uint64_t grid = (uint64_t)resident_grid((const void *)sk, kScatterBlock);
         if (grid > nt)
             grid = nt;
