@@ -320,14 +320,21 @@ __global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__res
     const uint32_t tile = blockIdx.x;
     const uint64_t vstart = (uint64_t)tile * T;
     u32x4 x[V];
-    // 16 counters as four words of four 8-bit fields.
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
     // Whole tiles skip the per-key range checks.
     const bool whole = vstart >= vlo && vstart + T <= vhi;
     if (whole)
         load_tile_full<BLOCK, V>(kbase, vstart, x);
     else
         load_tile<BLOCK, V>(kbase, vstart, vlo, vhi, x);
+    // Digit d adds 1 << 4(d mod 8) to lo (d < 8) or hi (d >= 8): 16 counters
+    // as nibbles of two words, a separate pair for every 8 keys so no nibble
+    // passes 8.
+    static_assert(V % 2 == 0, "two chunks (8 keys) per pair of nibble words");
+    constexpr int NP = V / 2;
+    uint32_t lo[NP], hi[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+        lo[q] = hi[q] = 0;
 #pragma unroll
     for (int k = 0; k < V; ++k) {
         const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
@@ -337,24 +344,36 @@ __global__ __launch_bounds__(BLOCK) void digit_hist_kernel(const uint32_t *__res
             if (!whole && (v0 + j < vlo || v0 + j >= vhi))
                 continue;
             const uint32_t d = (kk[j] >> shift) & 15u;
-            const uint32_t inc = 1u << ((d & 3u) * 8u);
-            const uint32_t sel = d >> 2;
-            c[0] += sel == 0 ? inc : 0u;
-            c[1] += sel == 1 ? inc : 0u;
-            c[2] += sel == 2 ? inc : 0u;
-            c[3] += sel == 3 ? inc : 0u;
+            const uint32_t one = 1u << ((d << 2) & 31u);
+            lo[k / 2] += d < 8 ? one : 0u;
+            hi[k / 2] += d < 8 ? 0u : one;
         }
     }
-    const uint32_t wave = threadIdx.x / kWave;
-    // Two digits per wave sum, as 16-bit fields (at most 64 x 255 per field).
+    // Nibbles to bytes (at most 8 * NP per byte): digits 2i and 2i + 1 of
+    // each half in byte i of ev / od.
+    uint32_t ev_lo = 0, od_lo = 0, ev_hi = 0, od_hi = 0;
 #pragma unroll
-    for (int d = 0; d < 16; d += 2) {
-        const uint32_t lo = (c[d >> 2] >> ((d & 3) * 8)) & 0xFFu;
-        const uint32_t hi = (c[(d + 1) >> 2] >> (((d + 1) & 3) * 8)) & 0xFFu;
-        const uint32_t t = wave_sum(lo | (hi << 16));
-        if (lane_id() == 0) {
-            s_part[wave][d] = t & 0xFFFFu;
-            s_part[wave][d + 1] = t >> 16;
+    for (int q = 0; q < NP; ++q) {
+        ev_lo += lo[q] & 0x0F0F0F0Fu;
+        od_lo += (lo[q] >> 4) & 0x0F0F0F0Fu;
+        ev_hi += hi[q] & 0x0F0F0F0Fu;
+        od_hi += (hi[q] >> 4) & 0x0F0F0F0Fu;
+    }
+    const uint32_t wave = threadIdx.x / kWave;
+    // Two digits per wave sum, as 16-bit fields (at most 64 x 16 per field):
+    // digits (2i, 2i + 1) from byte i of ev and od.
+    const uint32_t evw[2] = {ev_lo, ev_hi}, odw[2] = {od_lo, od_hi};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t pair = ((evw[h] >> (8 * i)) & 0xFFu) | (((odw[h] >> (8 * i)) & 0xFFu) << 16);
+            const uint32_t t = wave_sum(pair);
+            if (lane_id() == 0) {
+                const int d = 8 * h + 2 * i;
+                s_part[wave][d] = t & 0xFFFFu;
+                s_part[wave][d + 1] = t >> 16;
+            }
         }
     }
     __syncthreads();
