@@ -363,22 +363,67 @@ __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
     return x;
 }
 
-// Inclusive wave scans of V values under Op, two at a time for u64 add.
+// One DPP move of a u64 lane value whose identity under Op is the source
+// of lanes outside the row (or in a row not written).  When the identity is
+// 0 and every row is written, bound_ctrl makes out-of-row lanes read 0
+// directly, so the move needs no copy of the identity in its destination.
+template <int CTRL, int ROW_MASK, uint64_t ID>
+__device__ __forceinline__ uint64_t dpp64_id(uint64_t x)
+{
+    if constexpr (ID == 0 && ROW_MASK == 0xF) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+        const uint32_t hi =
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        return dpp64_or<CTRL, ROW_MASK>(x, ID);
+    }
+}
+
+// Two inclusive wave scans of u64 values under Op, step by step together:
+// each step's DPP reads of one scan follow the other scan's writes, so
+// neither waits for the register it reads (the steps of wave_incl64).
+template <class Op>
+__device__ __forceinline__ void wave_incl64_pair(uint64_t &a, uint64_t &b)
+{
+    constexpr uint64_t e = Op::identity;
+#define LIBSCAN_PAIR_STEP(CTRL, RMASK)                                                             \
+    {                                                                                              \
+        const uint64_t pa = dpp64_id<CTRL, RMASK, e>(a);                                           \
+        const uint64_t pb = dpp64_id<CTRL, RMASK, e>(b);                                           \
+        a = Op::apply(pa, a);                                                                      \
+        b = Op::apply(pb, b);                                                                      \
+    }
+    LIBSCAN_PAIR_STEP(kDppRowShr1, 0xF)
+    LIBSCAN_PAIR_STEP(kDppRowShr2, 0xF)
+    LIBSCAN_PAIR_STEP(kDppRowShr4, 0xF)
+    LIBSCAN_PAIR_STEP(kDppRowShr8, 0xF)
+    LIBSCAN_PAIR_STEP(kDppRowBcast15, 0xA)
+    LIBSCAN_PAIR_STEP(kDppRowBcast31, 0xC)
+#undef LIBSCAN_PAIR_STEP
+}
+
+// Inclusive wave scans of V values under Op, two at a time -- but for the
+// 64-bit multiply, whose steps are long enough to need no partner and whose
+// pairs only add register pressure (5.7% slower paired).
 template <class Op, int V>
 __device__ __forceinline__ void wave_incl64_n(const uint64_t (&e)[V], uint64_t (&w)[V])
 {
-    if constexpr (__is_same(Op, OpAdd64) && V % 2 == 0) {
-#pragma unroll
-        for (int k = 0; k < V; k += 2) {
-            uint64_t a = e[k], b = e[k + 1];
-            wave_incl64_add2(a, b);
-            w[k] = a;
-            w[k + 1] = b;
-        }
-    } else {
+    if constexpr (__is_same(Op, OpMul64) || V % 2 != 0) {
 #pragma unroll
         for (int k = 0; k < V; ++k)
             w[k] = wave_incl64<Op>(e[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; k += 2) {
+            uint64_t a = e[k], b = e[k + 1];
+            if constexpr (__is_same(Op, OpAdd64))
+                wave_incl64_add2(a, b);
+            else
+                wave_incl64_pair<Op>(a, b);
+            w[k] = a;
+            w[k + 1] = b;
+        }
     }
 }
 
