@@ -241,40 +241,56 @@ constexpr int kMpBlock = 256;
 constexpr int kMpItems = 16;
 constexpr uint64_t kMpTile = (uint64_t)kMpBlock * kMpItems;    // merged items per workgroup
 
-__device__ __forceinline__ uint64_t merge_split(const uint32_t *ends, uint64_t n, uint64_t total,
-                                                uint64_t d)
-{
-    uint64_t lo = d > total ? d - total : 0;
-    uint64_t hi = d < n ? d : n;
-    while (lo < hi) {
-        const uint64_t mid = (lo + hi + 1) / 2;
-        const uint64_t em = ends[mid - 1];
-        if ((em < total ? em : total) + mid <= d)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
+// The split at merged position d: the number of run ends among the first d
+// items, i.e. the largest i in [lo, hi] (lo = max(0, d - total), hi =
+// min(d, n)) with i == lo or min(ends[i - 1], total) + i <= d.  The test is
+// monotone in i for non-decreasing ends.  One wave per split: each round
+// tests 64 points spread over the open range at once, so a range shrinks
+// 64-fold per dependent load (about five loads for 2^24 owners instead of
+// a binary search's 25).
 __global__ __launch_bounds__(256) void runs_partition_kernel(const uint32_t *__restrict__ ends,
                                                              uint64_t n, uint64_t total,
                                                              uint64_t nparts,
                                                              uint32_t *__restrict__ splits)
 {
-    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t b = (uint64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
     if (b > nparts)
-        return;
+        return;                                 // the whole wave
+    const uint32_t lane = lane_id();
     const uint64_t d = b * kMpTile < n + total ? b * kMpTile : n + total;
-    splits[b] = (uint32_t)merge_split(ends, n, total, d);
+    uint64_t lo = d > total ? d - total : 0;
+    uint64_t hi = d < n ? d : n;
+    while (lo < hi) {
+        const uint64_t span = hi - lo;
+        // Probes in increasing order, the last at hi when span >= 64.
+        const uint64_t m = span >= kWave ? lo + ((span * (lane + 1)) >> 6) : lo + lane + 1;
+        bool ok = false;
+        if (m <= hi) {
+            const uint64_t em = ends[m - 1];
+            ok = (em < total ? em : total) + m <= d;
+        }
+        const uint32_t c = (uint32_t)__builtin_popcountll(ballot(ok));   // probes that pass
+        const uint64_t m_lo = __shfl(m, c == 0 ? 0 : c - 1);
+        const uint64_t m_hi = __shfl(m, c < kWave ? c : kWave - 1);
+        const uint32_t nprobe = span >= kWave ? (uint32_t)kWave : (uint32_t)span;
+        const uint64_t new_lo = c == 0 ? lo : m_lo;
+        const uint64_t new_hi = c >= nprobe ? new_lo : m_hi - 1;
+        lo = new_lo;
+        hi = new_hi > lo ? new_hi : lo;
+    }
+    if (lane == 0)
+        splits[b] = (uint32_t)lo;
 }
 
 __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
     const uint32_t *__restrict__ ends, uint64_t n, uint64_t total,
     const uint32_t *__restrict__ splits, int32_t *__restrict__ owner)
 {
-    // The workgroup's run ends at [0, ni), its owners from ni: together
-    // exactly its merged items, at most kMpTile.
+    // The workgroup's share: merged items [d0, d1), runs [i0, i1), entries
+    // [e0, e1).  Inside it every position is a 32-bit offset from those
+    // starts: the share's run ends, as offsets from e0 (capped at total, and
+    // at kMpTile: no end of a run in the share lies further), at [0, ni) of
+    // s_buf, its owners from ni.
     __shared__ uint32_t s_buf[kMpTile];
     const uint64_t b = blockIdx.x;
     const uint64_t d0 = b * kMpTile;
@@ -286,34 +302,38 @@ __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
     // access inside the workgroup's share even then.
     if (i1 < i0 || i1 - i0 > d1 - d0)
         i1 = i0;
-    const uint64_t e0 = d0 - i0, e1 = d1 - i1;
+    const uint64_t e0 = d0 - i0;
     const uint32_t ni = (uint32_t)(i1 - i0);
-    const uint32_t ne = (uint32_t)(e1 - e0);
-    for (uint32_t j = threadIdx.x; j < ni; j += kMpBlock)
-        s_buf[j] = ends[i0 + j];
+    const uint32_t nd = (uint32_t)(d1 - d0);
+    const uint32_t ne = nd - ni;
+    for (uint32_t j = threadIdx.x; j < ni; j += kMpBlock) {
+        const uint64_t em = ends[i0 + j] < total ? ends[i0 + j] : total;
+        const uint64_t rel = em > e0 ? em - e0 : 0;
+        s_buf[j] = rel < kMpTile ? (uint32_t)rel : (uint32_t)kMpTile;
+    }
     __syncthreads();
-    const uint64_t da = d0 + (uint64_t)threadIdx.x * kMpItems;
-    if (da < d1) {
-        // This thread's split inside the workgroup's share.
-        uint64_t lo = da > e1 + i0 ? da - e1 : i0;
-        uint64_t hi = da - e0 < i1 ? da - e0 : i1;
+    const uint32_t da = threadIdx.x * kMpItems;
+    if (da < nd) {
+        // This thread's split inside the share: the largest j in
+        // [max(0, da - ne), min(da, ni)] with j == lo or s_buf[j-1] + j <= da.
+        uint32_t lo = da > ne ? da - ne : 0;
+        uint32_t hi = da < ni ? da : ni;
         while (lo < hi) {
-            const uint64_t mid = (lo + hi + 1) / 2;
-            const uint64_t em = s_buf[mid - 1 - i0];
-            if ((em < total ? em : total) + mid <= da)
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (s_buf[mid - 1] + mid <= da)
                 lo = mid;
             else
                 hi = mid - 1;
         }
-        uint64_t i = lo, e = da - lo;
-        const uint64_t db = da + kMpItems < d1 ? da + kMpItems : d1;
-        for (uint64_t d = da; d < db; ++d) {
-            if (i < i1 && (s_buf[i - i0] <= e || e >= total)) {
-                ++i;                                // run i ended at or before entry e
+        uint32_t li = lo, le = da - lo;
+        const uint32_t db = da + kMpItems < nd ? da + kMpItems : nd;
+        for (uint32_t dd = da; dd < db; ++dd) {
+            if (li < ni && s_buf[li] <= le) {
+                ++li;                               // run li ended at or before entry le
             } else {
-                if (e - e0 < ne)
-                    s_buf[ni + (e - e0)] = i < n ? (uint32_t)i : 0xFFFFFFFFu;
-                ++e;
+                if (le < ne)
+                    s_buf[ni + le] = i0 + li < n ? (uint32_t)(i0 + li) : 0xFFFFFFFFu;
+                ++le;
             }
         }
     }
@@ -332,7 +352,7 @@ hipError_t launch_runs_owner_all(const uint32_t *ends, uint64_t n, int32_t *owne
 {
     const uint64_t nparts = runs_owner_all_parts(n, total);
     uint32_t *splits = reinterpret_cast<uint32_t *>(s.body());
-    const uint64_t pgrid = (nparts + 1 + 255) / 256;
+    const uint64_t pgrid = (nparts + 1 + 256 / kWave - 1) / (256 / kWave);    // a wave per split
     hipLaunchKernelGGL(runs_partition_kernel, dim3((uint32_t)pgrid), dim3(256), 0, stream, ends, n,
                        total, nparts, splits);
     hipLaunchKernelGGL(runs_owner_all_kernel, dim3((uint32_t)nparts), dim3(kMpBlock), 0, stream,
