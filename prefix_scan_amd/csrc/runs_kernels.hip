@@ -243,43 +243,37 @@ constexpr uint64_t kMpTile = (uint64_t)kMpBlock * kMpItems;    // merged items p
 
 // The split at merged position d: the number of run ends among the first d
 // items, i.e. the largest i in [lo, hi] (lo = max(0, d - total), hi =
-// min(d, n)) with i == lo or min(ends[i - 1], total) + i <= d.  The test is
-// monotone in i for non-decreasing ends.  One wave per split: each round
-// tests 64 points spread over the open range at once, so a range shrinks
-// 64-fold per dependent load (about five loads for 2^24 owners instead of
-// a binary search's 25).
+// min(d, n)) with i == lo or min(ends[i - 1], total) + i <= d (monotone in i
+// for non-decreasing ends), by binary search.  One thread per split: the
+// first levels of every search read the same few ends, which the caches
+// keep.  (A wave per split testing 64 points per round took twice as long:
+// 64 times the loads for five rounds instead of 25 levels.)
+__device__ __forceinline__ uint64_t merge_split(const uint32_t *ends, uint64_t n, uint64_t total,
+                                                uint64_t d)
+{
+    uint64_t lo = d > total ? d - total : 0;
+    uint64_t hi = d < n ? d : n;
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi + 1) / 2;
+        const uint64_t em = ends[mid - 1];
+        if ((em < total ? em : total) + mid <= d)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 __global__ __launch_bounds__(256) void runs_partition_kernel(const uint32_t *__restrict__ ends,
                                                              uint64_t n, uint64_t total,
                                                              uint64_t nparts,
                                                              uint32_t *__restrict__ splits)
 {
-    const uint64_t b = (uint64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b > nparts)
-        return;                                 // the whole wave
-    const uint32_t lane = lane_id();
+        return;
     const uint64_t d = b * kMpTile < n + total ? b * kMpTile : n + total;
-    uint64_t lo = d > total ? d - total : 0;
-    uint64_t hi = d < n ? d : n;
-    while (lo < hi) {
-        const uint64_t span = hi - lo;
-        // Probes in increasing order, the last at hi when span >= 64.
-        const uint64_t m = span >= kWave ? lo + ((span * (lane + 1)) >> 6) : lo + lane + 1;
-        bool ok = false;
-        if (m <= hi) {
-            const uint64_t em = ends[m - 1];
-            ok = (em < total ? em : total) + m <= d;
-        }
-        const uint32_t c = (uint32_t)__builtin_popcountll(ballot(ok));   // probes that pass
-        const uint64_t m_lo = __shfl(m, c == 0 ? 0 : c - 1);
-        const uint64_t m_hi = __shfl(m, c < kWave ? c : kWave - 1);
-        const uint32_t nprobe = span >= kWave ? (uint32_t)kWave : (uint32_t)span;
-        const uint64_t new_lo = c == 0 ? lo : m_lo;
-        const uint64_t new_hi = c >= nprobe ? new_lo : m_hi - 1;
-        lo = new_lo;
-        hi = new_hi > lo ? new_hi : lo;
-    }
-    if (lane == 0)
-        splits[b] = (uint32_t)lo;
+    splits[b] = (uint32_t)merge_split(ends, n, total, d);
 }
 
 __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
@@ -352,7 +346,7 @@ hipError_t launch_runs_owner_all(const uint32_t *ends, uint64_t n, int32_t *owne
 {
     const uint64_t nparts = runs_owner_all_parts(n, total);
     uint32_t *splits = reinterpret_cast<uint32_t *>(s.body());
-    const uint64_t pgrid = (nparts + 1 + 256 / kWave - 1) / (256 / kWave);    // a wave per split
+    const uint64_t pgrid = (nparts + 1 + 255) / 256;
     hipLaunchKernelGGL(runs_partition_kernel, dim3((uint32_t)pgrid), dim3(256), 0, stream, ends, n,
                        total, nparts, splits);
     hipLaunchKernelGGL(runs_owner_all_kernel, dim3((uint32_t)nparts), dim3(kMpBlock), 0, stream,
