@@ -16,13 +16,20 @@ synchronisation on both sides; prints ONE JSON line:
   cpu_baseline    the oracle's three-pass scan on all of this host's affinity
                   threads, its sequential scan on one, and numpy's cumsum, on
                   the same array, whose first passes are checked against the
-                  GPU's result bit for bit.
+                  GPU's result bit for bit;
+  device          the GPU's name, memory and compute units, the HBM peak the
+                  fractions use, and the memory as `amd-smi static --vram`
+                  reports it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--suite [--hbm-rows]]
 
 --suite additionally prints one JSON line per primitive workload (the other
 scan variants, compaction, segmented scan, radix permutation, ...), each the
-median of per-launch event times, every launch on the pristine workload.
+median of per-launch event times, every launch on the pristine workload;
+unless --no-cpu, each row whose result the oracle computes also carries the
+oracle's time for it on one host thread (std::stable_sort for the radix
+rows), and the 2^28 scan has a row with the total returned to the host,
+timed by the host clock, with the latency the wait adds.
 """
 import argparse
 import hashlib
@@ -99,6 +106,30 @@ def timed_region(torch, fn, reps):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     return wall, e0.elapsed_time(e1)
+
+
+def amd_smi_vram():
+    """The board's memory as amd-smi reports it (type, width, size ...), one
+    line, or None; queried as a child process before this process touches
+    the GPU."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "static", "-g", "0", "--vram"], capture_output=True,
+                           text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    text = " ".join(r.stdout.split())
+    return text[:400] if r.returncode == 0 and text else None
+
+
+def device_record(torch, vram):
+    props = torch.cuda.get_device_properties(0)
+    rec = {"name": props.name, "memory_gib": round(props.total_memory / 2**30, 1),
+           "compute_units": props.multi_processor_count,
+           "hbm_peak_gbs": HBM_PEAK_GBS, "hbm_peak_source": "AMD's published MI355X HBM3E figure"}
+    if vram:
+        rec["amd_smi_vram"] = vram
+    return rec
 
 
 def cpu_model():
@@ -256,6 +287,20 @@ def headline(args, torch, ps):
     return rec
 
 
+def oracle_call(name, *a):
+    """One call of the oracle's function `name` (CPU baseline only)."""
+    import oracle
+    return getattr(oracle, name)(*a)
+
+
+def cpu_baseline_row(kind, fn):
+    """The oracle computing a suite row's result on one host thread, timed
+    once by the host clock: the CPU baseline beside each GPU row."""
+    t0 = time.perf_counter()
+    fn()
+    return {"cpu_baseline_1core_ms": round((time.perf_counter() - t0) * 1e3, 2), "cpu_baseline_kind": kind}
+
+
 def suite(args, torch, ps):
     """One line per primitive workload (parity is the tests' job; this times).
     With --hbm-rows only the HBM-sized rows run (no 2^24 / 2^16 scans), so
@@ -268,11 +313,16 @@ def suite(args, torch, ps):
     def flush():
         flush_buf.zero_()
 
-    def row(name, n, bytes_per_elem, fn, reps=20, warm=3, before=None):
+    def row(name, n, bytes_per_elem, fn, reps=20, warm=3, before=None, cpu=None):
         # Each launch bracketed by events on the stream.  Rows that scan in
         # place pass `before`, which puts the pristine input back (and
         # flushes the caches) outside the events, so every timed launch
         # works on the workload itself, never on an earlier launch's output.
+        # `cpu`, when CPU baselines are on, is the oracle's computation of
+        # the same result on one host thread (see cpu_baseline_row); it runs
+        # first, so the warm-up launches bring the GPU back from the idle
+        # seconds it leaves.
+        base = cpu_baseline_row(*cpu) if cpu is not None and not args.no_cpu else {}
         for _ in range(warm):
             if before is not None:
                 before()
@@ -284,6 +334,27 @@ def suite(args, torch, ps):
                "bytes_per_elem": bytes_per_elem,
                "gb_s": round(bytes_per_elem * n / (med * 1e-3) / 1e9, 1),
                "frac_hbm_peak": round(bytes_per_elem * n / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        rec.update(base)
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+
+    def host_total_row(n, label, fn, before, reps=10):
+        # The same scan with the total returned to the host: the call copies
+        # the total back and waits for the stream, so it is timed by the host
+        # clock from a drained stream; `added_ms` is what the wait costs over
+        # the device-total call's median launch (the row timed just before).
+        times = []
+        for _ in range(reps + 2):
+            before()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            times.append((time.perf_counter() - t0) * 1e3)
+        times = times[2:]
+        med = float(np.median(times))
+        rec = {"row": "scan exclusive lookback n=%s, total to host (host clock, includes the wait)"
+                      % label, "n": n, "median_ms": round(med, 5), "min_ms": round(min(times), 5),
+               "added_ms": round(med - out[-1]["median_ms"], 5)}
         print(json.dumps(rec), flush=True)
         out.append(rec)
 
@@ -291,7 +362,8 @@ def suite(args, torch, ps):
     if not args.hbm_rows:
         sizes += [(workloads.N_SCAN_MID, "2^24 (cache-resident)"), (workloads.N_SCAN_SMALL, "2^16")]
     for n, label in sizes:
-        pristine = torch.from_numpy(workloads.uniform_u32(n, 202).view(np.int32)).to("cuda")
+        host = workloads.uniform_u32(n, 202)
+        pristine = torch.from_numpy(host.view(np.int32)).to("cuda")
         d = torch.empty_like(pristine)
         dst = torch.empty_like(pristine)
         tot = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -307,7 +379,10 @@ def suite(args, torch, ps):
 
         rs = restore if big else restore_cached
         row("scan exclusive lookback n=" + label, n, 8,
-            lambda: ps.scan_exclusive_u32(d, want_total=False, total_dev=tot), before=rs)
+            lambda: ps.scan_exclusive_u32(d, want_total=False, total_dev=tot), before=rs,
+            cpu=("sequential scan", lambda: oracle_call("scan_u32", host)))
+        if big:
+            host_total_row(n, label, lambda: ps.scan_exclusive_u32(d), rs)
         row("scan inclusive lookback n=" + label, n, 8,
             lambda: ps.scan_inclusive_u32(d, want_total=False, total_dev=tot), before=rs)
         row("scan exclusive lookback_tile n=" + label, n, 8,
@@ -348,27 +423,33 @@ def suite(args, torch, ps):
     # The rows below read inputs they never write; `flush` keeps each timed
     # launch from finding them in the caches.
     for p in (0.5, 0.01, 0.99):
-        f = torch.from_numpy(workloads.compact_flags(p)).to("cuda")
+        fh = workloads.compact_flags(p)
+        f = torch.from_numpy(fh).to("cuda")
         o = torch.empty_like(f)
         row("compact p=%g n=2^26" % p, f.numel(), 8,
-            lambda: ps.compact_flags_u32(f, out=o, want_count=False), before=flush)
+            lambda: ps.compact_flags_u32(f, out=o, want_count=False), before=flush,
+            cpu=("compaction", lambda: oracle_call("compact_flags", fh)))
         del f, o
-    v = torch.from_numpy(workloads.seg_values().view(np.int32)).to("cuda")
+    vh = workloads.seg_values()
+    v = torch.from_numpy(vh.view(np.int32)).to("cuda")
     o = torch.empty_like(v)
     for L in workloads.SEG_LENS:
         sums = torch.empty((v.numel() + L - 1) // L, dtype=torch.int32, device="cuda")
         row("segscan L=%d n=2^26" % L, v.numel(), 8 + 4.0 / L,
-            lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums), before=flush)
+            lambda: ps.segscan_u32(v, L, out=o, seg_sums=sums), before=flush,
+            cpu=("segmented scan", lambda: oracle_call("segscan_u32", vh, L)))
     # Irregular segments from head flags: value + flag read, output written
     # (12 B per element) and one 4-byte total per segment.
     f_means = (16, 1 << 20)
     for mean in f_means:
-        fl = torch.from_numpy(workloads.segment_heads(v.numel(), mean)).to("cuda")
+        flh = workloads.segment_heads(v.numel(), mean)
+        fl = torch.from_numpy(flh).to("cuda")
         nseg = int(fl.count_nonzero().item())
         sums = torch.empty(v.numel(), dtype=torch.int32, device="cuda")
         row("segscan flags mean=%d n=2^26" % mean, v.numel(), 12 + 4.0 * nseg / v.numel(),
             lambda: ps.segscan_flags_u32(v, fl, out=o, seg_sums=sums, want_nsegs=False),
-            before=flush)
+            before=flush,
+            cpu=("flag-segmented scan", lambda: oracle_call("segscan_flags_u32", vh, flh)))
         del fl, sums
     del v, o
     # Runs laid out by owner: the ends (8 B per owner), the -1 slots (4 B per
@@ -376,7 +457,8 @@ def suite(args, torch, ps):
     # queries (one binary search each; counted per query).
     for kind, gen in (("uniform", workloads.runs_counts_uniform),
                       ("sparse", workloads.runs_counts_sparse)):
-        c = torch.from_numpy(gen().view(np.int32)).to("cuda")
+        ch = gen()
+        c = torch.from_numpy(ch.view(np.int32)).to("cuda")
         ends = torch.empty_like(c)
         _, entries = ps.runs_layout_u32(c, ends=ends)
         total = int(ends[-1].item())
@@ -384,7 +466,8 @@ def suite(args, torch, ps):
             lambda: ps.runs_layout_u32(c, ends=ends, want_entries=False))
         own = torch.empty(total, dtype=torch.int32, device="cuda")
         row("runs owner_all %s n=2^24 entries=%d" % (kind, total), c.numel() + total, 4,
-            lambda: ps.runs_owner_all_u32(ends, total, owner=own))
+            lambda: ps.runs_owner_all_u32(ends, total, owner=own),
+            cpu=("owner of every entry", lambda: oracle_call("runs_owner_all", ch)))
         if kind == "uniform":
             slots = torch.empty(entries, dtype=torch.int32, device="cuda")
             row("runs slots entries=%d" % entries, entries, 4, lambda: ps.runs_slots_i32(slots))
@@ -396,10 +479,12 @@ def suite(args, torch, ps):
             del slots, q, qo
         del c, ends, own
     for kind, gen in (("uniform", workloads.radix_keys_uniform), ("256 distinct", workloads.radix_keys_distinct)):
-        k = torch.from_numpy(gen().view(np.int32)).to("cuda")
+        kh = gen()
+        k = torch.from_numpy(kh.view(np.int32)).to("cuda")
         perm = torch.empty_like(k)
         row("radix 1-bit x32 %s n=2^25" % kind, k.numel(), 508,
-            lambda: ps.radix_perm_u32(k, 1, perm=perm), reps=5, warm=1, before=flush)
+            lambda: ps.radix_perm_u32(k, 1, perm=perm), reps=5, warm=1, before=flush,
+            cpu=("std::stable_sort of the indices by key", lambda: oracle_call("stable_argsort_u32", kh)))
         row("radix 4-bit x8 %s n=2^25" % kind, k.numel(), 152,
             lambda: ps.radix_perm_u32(k, 4, perm=perm), reps=5, warm=1, before=flush)
         del k, perm
@@ -600,6 +685,7 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    vram = amd_smi_vram()                   # before anything here touches the GPU
     import torch
     import prefix_scan_amd as ps
     if not torch.cuda.is_available():
@@ -609,6 +695,7 @@ def main():
     if args.suite:
         suite(args, torch, ps)
     rec = headline(args, torch, ps)
+    rec["device"] = device_record(torch, vram)
     print(json.dumps(rec), flush=True)
 
 
