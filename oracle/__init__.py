@@ -1,7 +1,8 @@
 """CPU oracle for the prefix-scan primitives -- TEST INFRASTRUCTURE ONLY.
 
-Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
-``bench.py`` may import this package.  The HIP library never does, and this
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline legs of
+``bench.py`` (the headline's ``cpu_baseline`` and the suite rows' one-core
+times) may import this package.  The HIP library never does, and this
 package never imports the HIP library: the two share no code.
 
 Each function wraps one plain sequential C routine of ``oracle.c`` (see that
