@@ -176,6 +176,100 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict
         *total_out = carry;
 }
 
+// Pass 3 for blocks of many tiles: the same per-block scan, but a resident
+// grid walks the blocks round-robin and each workgroup runs a block's tiles
+// in the lockstep of the pipelined scan -- the next tile's loads issued, the
+// next tile reduced once they land, then the current tile finished and
+// stored -- with the carry kept in the workgroup: a block's first tile takes
+// the block's base, each later one the carry before it plus that tile's
+// sum.  No look-back: the bases are known.  Three cell buffers rotate, so a
+// tile's cells are written two steps after the buffer's previous tile was
+// last read, with barriers between.
+template <int BLOCK, int V, bool INCL>
+__global__ __launch_bounds__(BLOCK) void scan_blocks_pipelined_kernel(
+    uint32_t *__restrict__ abase, uint32_t head, uint64_t n, uint64_t bsize, uint64_t blocks,
+    const uint32_t *__restrict__ bases)
+{
+    using TS = TileScan<BLOCK, V>;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    __shared__ uint32_t s_cell[3][TS::NCELL];
+    __shared__ uint32_t s_agg;
+    u32x4 xa[V], xb[V];
+    int cb = 0;
+    for (uint64_t i = blockIdx.x; i < blocks; i += gridDim.x) {
+        const uint64_t lo = i * bsize < n ? i * bsize : n;
+        const uint64_t hi = lo + bsize < n ? lo + bsize : n;
+        if (lo >= hi)
+            continue;                           // the whole workgroup
+        const uint64_t vlo = lo + head, vhi = hi + head;
+        const uint64_t v0 = vlo & ~3ull;        // the block's first chunk
+        auto whole = [&](uint64_t vs) { return vs >= vlo && vs + T <= vhi; };
+        auto load = [&](u32x4 (&x)[V], uint64_t vs) {
+            if (whole(vs))
+                load_tile_full<BLOCK, V>(abase, vs, x);
+            else
+                load_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
+        };
+        // Phase 1 and 2 of the tile in x: its cells in s_cell[b], its sum
+        // returned (all threads, after the second barrier).
+        auto reduce = [&](u32x4 (&x)[V], int b) -> uint32_t {
+            uint32_t w[V];
+            TS::local(x, w, s_cell[b]);
+            __syncthreads();
+            if (threadIdx.x < kWave) {
+                const uint32_t agg = TS::cells(s_cell[b]);
+                if (threadIdx.x == 0)
+                    s_agg = agg;
+            }
+            __syncthreads();
+            return s_agg;
+        };
+        // Phase 3 with the carry, then the stores.
+        auto finish = [&](u32x4 (&x)[V], int b, uint64_t vs, uint32_t carry) {
+            uint32_t w[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                w[k] = wave_incl_add(x[k].w);
+            TS::template apply<INCL>(x, w, s_cell[b], carry);
+            if (whole(vs))
+                store_tile_full<BLOCK, V>(abase, vs, x);
+            else
+                store_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
+        };
+        uint32_t carry = bases[i];
+        uint64_t vs = v0;
+        load(xa, vs);
+        uint32_t sum = reduce(xa, cb);
+        // One step: X holds the tile at vs (reduced, cells in cb, sum in
+        // `sum`); Y receives the next.  Returns false after the last tile.
+        auto step = [&](u32x4 (&X)[V], u32x4 (&Y)[V]) -> bool {
+            const uint64_t vn = vs + T;
+            const bool more = vn < vhi;
+            const int nb = cb == 2 ? 0 : cb + 1;
+            uint32_t sum_next = 0;
+            if (more) {
+                load(Y, vn);
+                sum_next = reduce(Y, nb);
+            }
+            finish(X, cb, vs, carry);
+            carry += sum;
+            sum = sum_next;
+            vs = vn;
+            cb = nb;
+            return more;
+        };
+        for (;;) {
+            if (!step(xa, xb))
+                break;
+            if (!step(xb, xa))
+                break;
+        }
+        // The next block's first reduce writes s_agg and a cell buffer that
+        // this block's last finish may still read: wait for every thread.
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The streaming copy: the read + write ceiling beside the scan, and the
 // calibration of the HBM byte counters.
@@ -483,6 +577,26 @@ static void launch_scan_blocks(uint32_t *data, uint64_t n, uint64_t blocks, uint
                            dim3(kBlock), 0, stream, data - head, head, n, bsize, bases, total_out);
 }
 
+// Pass 3.  Blocks of at least two of its tiles take the pipelined kernel,
+// on one round of resident workgroups; smaller blocks keep one workgroup
+// each, tile after tile.
+constexpr int kTp3Block = 512;
+constexpr int kTp3Chunks = 16;
+
+static void launch_scan_blocks_pipelined(uint32_t *data, uint64_t n, uint64_t blocks,
+                                         uint64_t bsize, const uint32_t *bases, bool inclusive,
+                                         hipStream_t stream)
+{
+    const uint32_t head = head_of(data);
+    auto kern = inclusive ? scan_blocks_pipelined_kernel<kTp3Block, kTp3Chunks, true>
+                          : scan_blocks_pipelined_kernel<kTp3Block, kTp3Chunks, false>;
+    uint64_t grid = (uint64_t)resident_grid((const void *)kern, kTp3Block);
+    if (grid > blocks)
+        grid = blocks;
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kTp3Block), 0, stream, data - head, head,
+                       n, bsize, blocks, bases);
+}
+
 hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, unsigned d,
                                  const Scratch &s, uint32_t *total_out, hipStream_t stream)
 {
@@ -505,7 +619,10 @@ hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, uns
         launch_scan_blocks(sums, blocks, b2, bs2, sums2, nullptr, false, stream);
     }
     // Pass 3: each block rescanned in place from its base.
-    launch_scan_blocks(data, n, blocks, bsize, sums, nullptr, inclusive, stream);
+    if (bsize >= 2 * (uint64_t)kTp3Block * kTp3Chunks * 4)
+        launch_scan_blocks_pipelined(data, n, blocks, bsize, sums, inclusive, stream);
+    else
+        launch_scan_blocks(data, n, blocks, bsize, sums, nullptr, inclusive, stream);
     return hipGetLastError();
 }
 

@@ -71,6 +71,18 @@ def test_ragged_sizes(n):
         check(a, inclusive, algo="threepass", fork_depth=3)
 
 
+@pytest.mark.parametrize("n,b", [((1 << 22) - 3, 4), ((1 << 22) - 3, 5), ((1 << 22) - 3, 7),
+                                 ((1 << 24) - 100, 9), ((1 << 24) - 100, 10)])
+def test_threepass_blocks_of_whole_tiles(n, b):
+    # Pass-3 blocks of 8, 4 and 1 whole 32768-element tiles (b = 4, 5, 7 and
+    # 9) and of half a tile (b = 10): the pipelined and the one-tile-per-step
+    # rescans, each with a ragged last tile, aligned and one element off.
+    a = workloads.small_random_u32(n, 900 + b)
+    for inclusive in (False, True):
+        check(a, inclusive, algo="threepass", fork_depth=b)
+    check(a, True, algo="threepass", fork_depth=b, offset=1)
+
+
 @pytest.mark.parametrize("offset", [1, 2, 3])
 @pytest.mark.parametrize("n", [1, 3, 5, 4097, 65536 + 5, 1 << 20])
 def test_unaligned_pointers(n, offset):
