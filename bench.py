@@ -108,11 +108,21 @@ def timed_region(torch, fn, reps):
     return wall, e0.elapsed_time(e1)
 
 
+def under_profiler():
+    """True when a GPU profiler's library is preloaded into this process (and
+    so into every child it starts, where it may bring the GPU up first)."""
+    return (any(k.startswith("ROCPROF") for k in os.environ)
+            or "rocprof" in os.environ.get("LD_PRELOAD", ""))
+
+
 def amd_smi_vram():
     """The board's memory as amd-smi reports it (type, width, size ...), one
     line, or None; queried as a child process before this process touches
-    the GPU."""
+    the GPU.  Skipped under a profiler: there the child would start with the
+    GPU already initialised, and amd-smi's launcher then replaces itself."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["amd-smi", "static", "-g", "0", "--vram"], capture_output=True,
                            text=True, timeout=30)

@@ -138,7 +138,13 @@ int scan_inclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_
  * fork_depth   THREEPASS: -1 picks a depth for the GPU, b >= 0 uses
  *              d = min(b, floor(log2 n), 24) and 2^d blocks of ceil(n / 2^d)
  *              entries (the last blocks shorter or empty when 2^d does not
- *              divide n), one workgroup per block.  LOOKBACK: must be -1.
+ *              divide n).  Pass 3 runs blocks of exactly one 32768-entry
+ *              tile of a 16-byte aligned array as tiles drawn in turn by a
+ *              resident grid, blocks of two or more such tiles as a
+ *              resident grid's per-block pipelines, other blocks as one
+ *              workgroup each.  -1 takes blocks of one tile from n = 2^26 up
+ *              when a power of two gives them, else blocks of two to four
+ *              tiles; below 2^26 about 2048 blocks.  LOOKBACK: must be -1.
  * Other arguments as scan_exclusive_u32.  scratch must hold
  * scan_ex_scratch_bytes(n, algo, fork_depth) bytes.
  * Errors: as scan_exclusive_u32, plus ERR_ARG for an unknown algo, a

@@ -13,7 +13,8 @@
 //    "Driver"): block sums, a scan of the sums (one workgroup below 2^12
 //    sums, else the same scheme at half the depth), then each block rescanned
 //    from its base.  12 bytes per element; kept as the comparison scheme and
-//    for the fork-depth knob.
+//    for the fork-depth knob.  With blocks of one tile, pass 3 hands the
+//    tiles out from a ticket like the chained scan, minus the look-back.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
@@ -102,12 +103,15 @@ template <int BLOCK, int V>
 __global__ __launch_bounds__(BLOCK) void reduce_blocks_kernel(const uint32_t *__restrict__ abase,
                                                               uint32_t head, uint64_t n,
                                                               uint64_t bsize,
-                                                              uint32_t *__restrict__ sums)
+                                                              uint32_t *__restrict__ sums,
+                                                              uint32_t *__restrict__ clear)
 {
     constexpr int NW = BLOCK / kWave;
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     __shared__ uint32_t s_part[NW];
     const uint64_t i = blockIdx.x;
+    if (clear != nullptr && i == 0 && threadIdx.x == 0)
+        *clear = 0u;                            // a later pass's ticket
     const uint64_t lo = i * bsize < n ? i * bsize : n;
     const uint64_t hi = lo + bsize < n ? lo + bsize : n;
     const uint64_t vlo = lo + head, vhi = hi + head;
@@ -267,6 +271,92 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_pipelined_kernel(
         // The next block's first reduce writes s_agg and a cell buffer that
         // this block's last finish may still read: wait for every thread.
         __syncthreads();
+    }
+}
+
+// Pass 3 when every block is exactly one tile of an aligned array: each
+// tile's base is known, so the tiles need no order among themselves.  A
+// resident grid draws tile numbers from a ticket (pass 1 zeroed it), as the
+// look-back scan does, and runs them in the same lockstep -- the tile after
+// next drawn, the next tile loaded and reduced, then the current one
+// finished from its base and stored -- with no carry between tiles.
+template <int BLOCK, int V, bool INCL>
+__global__ __launch_bounds__(BLOCK) void scan_tiles_known_bases_kernel(
+    uint32_t *__restrict__ abase, uint64_t n, uint32_t ntiles, const uint32_t *__restrict__ bases,
+    uint32_t *ticket)
+{
+    using TS = TileScan<BLOCK, V>;
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    constexpr int kDrawer = BLOCK - kWave;      // lane 0 of the last wave
+    __shared__ uint32_t s_cell[3][TS::NCELL];
+    __shared__ uint32_t s_num[3];
+    auto draw = [&](uint32_t k) {
+        return __hip_atomic_fetch_add(ticket, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (threadIdx.x == kDrawer) {
+        const uint32_t first = draw(2u);
+        s_num[0] = first;
+        s_num[1] = first + 1u;
+    }
+    __syncthreads();
+    uint32_t cur = s_num[0], nxt = s_num[1];
+    if (cur >= ntiles)
+        return;                                 // the whole workgroup
+    auto load = [&](u32x4 (&x)[V], uint32_t tt) {
+        if ((uint64_t)tt * T + T <= n)
+            load_tile_full<BLOCK, V>(abase, (uint64_t)tt * T, x);
+        else
+            load_tile<BLOCK, V>(abase, (uint64_t)tt * T, 0, n, x);
+    };
+    // Phases 1 and 2: the tile's cells in s_cell[b] (its sum is not needed).
+    auto reduce = [&](u32x4 (&x)[V], int b) {
+        uint32_t w[V];
+        TS::local(x, w, s_cell[b]);
+        __syncthreads();
+        if (threadIdx.x < kWave)
+            (void)TS::cells(s_cell[b]);
+        __syncthreads();
+    };
+    auto finish = [&](u32x4 (&x)[V], int b, uint32_t tt) {
+        uint32_t w[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            w[k] = wave_incl_add(x[k].w);
+        TS::template apply<INCL>(x, w, s_cell[b], bases[tt]);
+        if ((uint64_t)tt * T + T <= n)
+            store_tile_full<BLOCK, V>(abase, (uint64_t)tt * T, x);
+        else
+            store_tile<BLOCK, V>(abase, (uint64_t)tt * T, 0, n, x);
+    };
+    u32x4 xa[V], xb[V];
+    int cb = 0;
+    load(xa, cur);
+    reduce(xa, cb);
+    // One step: X holds tile cur (cells in cb); Y receives nxt.  The number
+    // drawn for the tile after nxt goes through s_num[nb], read after the
+    // reduce's barriers and written again three steps later.
+    auto step = [&](u32x4 (&X)[V], u32x4 (&Y)[V]) -> bool {
+        const bool more = nxt < ntiles;
+        const int nb = cb == 2 ? 0 : cb + 1;
+        uint32_t nn = ntiles;
+        if (more) {
+            if (threadIdx.x == kDrawer)
+                s_num[nb] = draw(1u);
+            load(Y, nxt);
+            reduce(Y, nb);
+            nn = s_num[nb];
+        }
+        finish(X, cb, cur);
+        cur = nxt;
+        nxt = nn;
+        cb = nb;
+        return more;
+    };
+    for (;;) {
+        if (!step(xa, xb))
+            break;
+        if (!step(xb, xa))
+            break;
     }
 }
 
@@ -542,9 +632,26 @@ hipError_t launch_scan_table(uint32_t *data, uint64_t n, const Scratch &s, uint3
 // The three-pass scheme's own tile: 256 threads x 4 chunks.
 constexpr int kTpChunks = 4;
 
+// Pass 3's tile on a resident grid: 512 threads x 16 chunks of 4.
+constexpr int kTp3Block = 512;
+constexpr int kTp3Chunks = 16;
+
 unsigned threepass_auto_depth(uint64_t n)
 {
-    // About 2048 blocks (8 per CU), each at least one tile.
+    // From 2^26 elements (2048 tiles of pass 3) up: blocks of exactly one
+    // tile when a power of two of them fits n that way (pass 3 then draws
+    // the tiles from a ticket), else blocks of two to four tiles (pass 3
+    // pipelines each block).  Below: about 2048 blocks, each at least one
+    // tile of the one-workgroup-per-block rescan.
+    constexpr uint64_t T = (uint64_t)kTp3Block * kTp3Chunks * 4;
+    if (n >= (1ull << 26)) {
+        const uint64_t tiles = (n + T - 1) / T;
+        unsigned d = floor_log2(tiles);
+        if ((1ull << d) < tiles)
+            ++d;                                // 2^d >= tiles > 2^(d-1)
+        const uint64_t bsize = (n + (1ull << d) - 1) >> d;
+        return bsize == T ? d : d - 2;
+    }
     const unsigned lg = floor_log2(n);
     return lg > 12 ? (lg - 12 < 11 ? lg - 12 : 11) : 0;
 }
@@ -553,15 +660,15 @@ size_t scan_threepass_body_bytes(unsigned d)
 {
     const size_t s1 = round_up(((size_t)1 << d) * sizeof(uint32_t), kScratchAlign);
     const size_t s2 = round_up(((size_t)1 << (d / 2)) * sizeof(uint32_t), kScratchAlign);
-    return s1 + s2;
+    return s1 + s2 + kScratchAlign;             // + pass 3's ticket
 }
 
 static void launch_reduce(const uint32_t *data, uint64_t n, uint64_t blocks, uint64_t bsize,
-                          uint32_t *sums, hipStream_t stream)
+                          uint32_t *sums, hipStream_t stream, uint32_t *clear = nullptr)
 {
     const uint32_t head = head_of(data);
     hipLaunchKernelGGL((reduce_blocks_kernel<kBlock, kTpChunks>), dim3((uint32_t)blocks),
-                       dim3(kBlock), 0, stream, data - head, head, n, bsize, sums);
+                       dim3(kBlock), 0, stream, data - head, head, n, bsize, sums, clear);
 }
 
 static void launch_scan_blocks(uint32_t *data, uint64_t n, uint64_t blocks, uint64_t bsize,
@@ -577,17 +684,28 @@ static void launch_scan_blocks(uint32_t *data, uint64_t n, uint64_t blocks, uint
                            dim3(kBlock), 0, stream, data - head, head, n, bsize, bases, total_out);
 }
 
-// Pass 3.  Blocks of at least two of its tiles take the pipelined kernel,
-// on one round of resident workgroups; smaller blocks keep one workgroup
-// each, tile after tile.
-constexpr int kTp3Block = 512;
-constexpr int kTp3Chunks = 16;
+// Pass 3.  Blocks of exactly one of its tiles on an aligned array, and
+// blocks of at least two, take a resident grid (the tiles drawn from a
+// ticket, or each block pipelined); other blocks keep one workgroup each,
+// tile after tile.
 
 static void launch_scan_blocks_pipelined(uint32_t *data, uint64_t n, uint64_t blocks,
                                          uint64_t bsize, const uint32_t *bases, bool inclusive,
-                                         hipStream_t stream)
+                                         uint32_t *ticket, hipStream_t stream)
 {
     const uint32_t head = head_of(data);
+    if (ticket != nullptr) {
+        // One tile per block: tiles drawn from the ticket, each from its base.
+        auto kern = inclusive ? scan_tiles_known_bases_kernel<kTp3Block, kTp3Chunks, true>
+                              : scan_tiles_known_bases_kernel<kTp3Block, kTp3Chunks, false>;
+        const uint64_t ntiles = (n + bsize - 1) / bsize;
+        uint64_t grid = (uint64_t)resident_grid((const void *)kern, kTp3Block);
+        if (grid > ntiles)
+            grid = ntiles;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kTp3Block), 0, stream, data, n,
+                           (uint32_t)ntiles, bases, ticket);
+        return;
+    }
     auto kern = inclusive ? scan_blocks_pipelined_kernel<kTp3Block, kTp3Chunks, true>
                           : scan_blocks_pipelined_kernel<kTp3Block, kTp3Chunks, false>;
     uint64_t grid = (uint64_t)resident_grid((const void *)kern, kTp3Block);
@@ -603,11 +721,18 @@ hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, uns
     const uint64_t blocks = 1ull << d;
     const uint64_t bsize = (n + blocks - 1) / blocks;
     uint32_t *sums = reinterpret_cast<uint32_t *>(s.body());
-    uint32_t *sums2 = reinterpret_cast<uint32_t *>(
-        s.body() + round_up(blocks * sizeof(uint32_t), kScratchAlign));
+    const size_t s1 = round_up(blocks * sizeof(uint32_t), kScratchAlign);
+    uint32_t *sums2 = reinterpret_cast<uint32_t *>(s.body() + s1);
+    // Blocks of exactly one pass-3 tile, aligned: pass 3 draws the tiles
+    // from a ticket after the sums, which pass 1 zeroes.
+    const uint64_t tp3_tile = (uint64_t)kTp3Block * kTp3Chunks * 4;
+    uint32_t *ticket = nullptr;
+    if (bsize == tp3_tile && head_of(data) == 0)
+        ticket = reinterpret_cast<uint32_t *>(
+            s.body() + s1 + round_up(((size_t)1 << (d / 2)) * sizeof(uint32_t), kScratchAlign));
 
     // Pass 1: each block's sum.
-    launch_reduce(data, n, blocks, bsize, sums, stream);
+    launch_reduce(data, n, blocks, bsize, sums, stream, ticket);
     // Pass 2: the sums become their exclusive scan, and the total.
     if (d < 12) {
         launch_scan_blocks(sums, blocks, 1, blocks, nullptr, total_out, false, stream);
@@ -619,8 +744,8 @@ hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, uns
         launch_scan_blocks(sums, blocks, b2, bs2, sums2, nullptr, false, stream);
     }
     // Pass 3: each block rescanned in place from its base.
-    if (bsize >= 2 * (uint64_t)kTp3Block * kTp3Chunks * 4)
-        launch_scan_blocks_pipelined(data, n, blocks, bsize, sums, inclusive, stream);
+    if (bsize >= 2 * tp3_tile || ticket != nullptr)
+        launch_scan_blocks_pipelined(data, n, blocks, bsize, sums, inclusive, ticket, stream);
     else
         launch_scan_blocks(data, n, blocks, bsize, sums, nullptr, inclusive, stream);
     return hipGetLastError();

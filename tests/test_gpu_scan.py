@@ -74,9 +74,11 @@ def test_ragged_sizes(n):
 @pytest.mark.parametrize("n,b", [((1 << 22) - 3, 4), ((1 << 22) - 3, 5), ((1 << 22) - 3, 7),
                                  ((1 << 24) - 100, 9), ((1 << 24) - 100, 10)])
 def test_threepass_blocks_of_whole_tiles(n, b):
-    # Pass-3 blocks of 8, 4 and 1 whole 32768-element tiles (b = 4, 5, 7 and
-    # 9) and of half a tile (b = 10): the pipelined and the one-tile-per-step
-    # rescans, each with a ragged last tile, aligned and one element off.
+    # Pass-3 blocks of 8 and 4 whole 32768-element tiles (b = 4, 5: the
+    # pipelined rescan per block), of exactly one (b = 7, 9: the tiles
+    # round-robin from their bases) and of half a tile (b = 10: a workgroup
+    # per block), each with a ragged last tile; one element off alignment
+    # the one-tile blocks take a workgroup per block too.
     a = workloads.small_random_u32(n, 900 + b)
     for inclusive in (False, True):
         check(a, inclusive, algo="threepass", fork_depth=b)
@@ -128,6 +130,16 @@ def test_large_workload_uniform_exclusive_and_inclusive():
         assert first_mismatch(got, ref) is None
         assert int(to_host_u32(tot_dev)[0]) == tref
         del t
+
+
+@pytest.mark.parametrize("n", [(1 << 27) - 1000, 3 << 25, (1 << 26) + 1])
+def test_threepass_automatic_depth_large_ragged(n):
+    # Automatic depth from 2^26 up: blocks of one tile with a ragged last
+    # tile (2^27 - 1000), of three tiles (3 * 2^25), of two tiles and one
+    # entry (2^26 + 1).
+    a = workloads.small_random_u32(n, n % 1000)
+    check(a, False, algo="threepass")
+    check(a, True, algo="threepass")
 
 
 def test_large_workload_threepass():
