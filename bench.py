@@ -527,7 +527,7 @@ def algorithmic_bytes(name, grid):
     n28, n27, n26, n25 = 1 << 28, 1 << 27, 1 << 26, 1 << 25
     table = [
         ("scan_pipelined_kernel", 8 * n28), ("ceiling_copy_kernel", 8 * n28),
-        ("reduce_blocks_kernel", 4 * n28), ("compact_kernel", 8 * n26),
+        ("compact_kernel", 8 * n26),
         ("segscan_independent_kernel", 8 * n26 + 4 * (n26 // 16)),
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
         ("segscan_lanes_kernel", 8 * n26 + 4 * (n26 // 16)),
@@ -538,10 +538,13 @@ def algorithmic_bytes(name, grid):
     ]
     if "segflags_kernel" in name:
         return 12 * n26                # + 4 B per segment, under 2% at mean length 16
+    if "reduce_blocks_kernel" in name:
+        return 4 * n28 if big else None    # else pass 2's reduction of the block sums
     for key, b in table:
         if "::" + key + "<" in name:
             return b
-    if "scan_lookback_kernel" in name or "scan_blocks_kernel" in name:
+    if any(k in name for k in ("scan_lookback_kernel", "scan_blocks_kernel",
+                                "scan_blocks_pipelined_kernel", "scan_tiles_known_bases_kernel")):
         return 8 * n28 if big else None
     if "runs_owner_all_kernel" in name:
         # 4 B per merged item (run end or entry), 4096 items per 256-thread
