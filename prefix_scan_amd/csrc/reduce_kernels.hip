@@ -4,48 +4,42 @@
 // CAIRN "Concurrency", section "reduce and compact": a reduction folds the
 // values of all indices into one result under add_wrap, mul_wrap, &, |, ^,
 // min or max (here unsigned or signed); for these integer operators the
-// result does not depend on the order of the fold.  So a grid that fills the GPU walks the tiles round-robin, each
-// workgroup folds its tiles into one partial (a thread's chunks, the wave,
-// the workgroup), and one workgroup folds the partials.  4 bytes read per
-// element.
+// result does not depend on the order of the fold.  So each workgroup folds
+// one contiguous block of the array into one partial (a thread's chunks,
+// the wave, the workgroup), and one workgroup folds the partials.  4 bytes
+// read per element.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace libscan {
 
 constexpr int kRedBlock = 256;
-constexpr int kRedChunks = 16;          // 16384 values per tile
-constexpr uint32_t kMaxPartials = 4096;
+constexpr int kRedChunks = 4;           // 4096 values per step of a block
+constexpr uint64_t kRedMinBlock = 32768;
+constexpr uint32_t kMaxPartials = 16384;
 
+// Workgroup i folds the values of virtual indices [i * bsize, (i + 1) *
+// bsize) inside [vlo, vhi) into partials[i]; bsize is a whole number of
+// steps.  One workgroup per block, as many as the array needs, so the
+// hardware hands the blocks out in turn as workgroups finish.
 template <int BLOCK, int V, class M>
-__global__ __launch_bounds__(BLOCK) void reduce_partial_kernel(const uint32_t *__restrict__ abase,
-                                                               uint64_t vlo, uint64_t vhi,
-                                                               uint64_t ntiles,
-                                                               uint32_t *__restrict__ partials)
+__global__ __launch_bounds__(BLOCK) void reduce_block_kernel(const uint32_t *__restrict__ abase,
+                                                             uint64_t vlo, uint64_t vhi,
+                                                             uint64_t bsize,
+                                                             uint32_t *__restrict__ partials)
 {
     constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
     constexpr int NW = BLOCK / kWave;
     __shared__ uint32_t s_part[NW];
+    const uint64_t lo = (uint64_t)blockIdx.x * bsize;
+    const uint64_t hi = lo + bsize < vhi ? lo + bsize : vhi;
     uint32_t acc = M::identity;
-    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint64_t vstart = t * T;
+    for (uint64_t vs = lo; vs < hi; vs += T) {
         u32x4 x[V];
-        const bool whole = vstart >= vlo && vstart + T <= vhi;
-        if (whole) {
-            load_tile_full<BLOCK, V>(abase, vstart, x);
-        } else {
-            load_tile<BLOCK, V>(abase, vstart, vlo, vhi, x);
-            if constexpr (M::identity != 0u) {      // slots outside read as 0
-#pragma unroll
-                for (int k = 0; k < V; ++k) {
-                    const uint64_t v0 = vstart + (uint64_t)(k * BLOCK + threadIdx.x) * 4;
-                    if (!(v0 + 0 >= vlo && v0 + 0 < vhi)) x[k].x = M::identity;
-                    if (!(v0 + 1 >= vlo && v0 + 1 < vhi)) x[k].y = M::identity;
-                    if (!(v0 + 2 >= vlo && v0 + 2 < vhi)) x[k].z = M::identity;
-                    if (!(v0 + 3 >= vlo && v0 + 3 < vhi)) x[k].w = M::identity;
-                }
-            }
-        }
+        if (vs >= vlo && vs + T <= vhi)
+            load_tile_full<BLOCK, V>(abase, vs, x);
+        else
+            load_tile<BLOCK, V>(abase, vs, vlo, vhi, x, M::identity);
 #pragma unroll
         for (int k = 0; k < V; ++k)
             acc = M::apply(acc, M::apply(M::apply(x[k].x, x[k].y), M::apply(x[k].z, x[k].w)));
@@ -93,18 +87,19 @@ static hipError_t launch_reduce_m(const uint32_t *data, uint64_t n, const Scratc
 {
     constexpr uint64_t T = (uint64_t)kRedBlock * kRedChunks * 4;
     const uint32_t head = head_of(data);
-    const uint64_t ntiles = tiles_for(n, head, T);
-    auto kern = reduce_partial_kernel<kRedBlock, kRedChunks, M>;
-    uint64_t grid = (uint64_t)resident_grid((const void *)kern, kRedBlock);
-    if (grid > ntiles)
-        grid = ntiles;
-    if (grid > kMaxPartials)
-        grid = kMaxPartials;
+    const uint64_t vhi = n + head;
+    // Blocks of at least 32768 values, few enough for the partials buffer.
+    uint64_t bsize = (vhi + kMaxPartials - 1) / kMaxPartials;
+    bsize = (bsize + T - 1) / T * T;
+    if (bsize < kRedMinBlock)
+        bsize = kRedMinBlock;
+    const uint64_t blocks = (vhi + bsize - 1) / bsize;
     uint32_t *partials = reinterpret_cast<uint32_t *>(s.body());
-    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kRedBlock), 0, stream, data - head,
-                       (uint64_t)head, n + head, ntiles, partials);
-    hipLaunchKernelGGL((reduce_final_kernel<256, M>), dim3(1), dim3(256), 0, stream, partials,
-                       (uint32_t)grid, total_out);
+    hipLaunchKernelGGL((reduce_block_kernel<kRedBlock, kRedChunks, M>), dim3((uint32_t)blocks),
+                       dim3(kRedBlock), 0, stream, data - head, (uint64_t)head, vhi, bsize,
+                       partials);
+    hipLaunchKernelGGL((reduce_final_kernel<1024, M>), dim3(1), dim3(1024), 0, stream, partials,
+                       (uint32_t)blocks, total_out);
     return hipGetLastError();
 }
 

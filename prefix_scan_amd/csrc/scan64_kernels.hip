@@ -251,29 +251,34 @@ hipError_t launch_scan_op64(uint64_t *data, uint64_t n, int op, bool inclusive, 
 }
 
 // ---------------------------------------------------------------------------
-// Reduction: a grid that fills the GPU walks the tiles round-robin, each
-// workgroup folds its tiles into one partial, one workgroup folds those.
+// Reduction: each workgroup folds one contiguous block into one partial,
+// one workgroup folds those.
 // ---------------------------------------------------------------------------
 constexpr int kRed64Block = 256;
-constexpr int kRed64Chunks = 16;        // 8192 u64 per tile
-constexpr uint32_t kMaxPartials64 = 4096;
+constexpr int kRed64Chunks = 4;         // 2048 u64 per step of a block
+constexpr uint64_t kRed64MinBlock = 16384;
+constexpr uint32_t kMaxPartials64 = 16384;
 
+// Workgroup i folds the u64 values of virtual indices [i * bsize, (i + 1)
+// * bsize) inside [vlo, vhi) into partials[i]; bsize is a whole number of
+// steps.
 template <int BLOCK, int V, class M>
-__global__ __launch_bounds__(BLOCK) void reduce64_partial_kernel(
-    const uint64_t *__restrict__ abase, uint64_t vlo, uint64_t vhi, uint64_t ntiles,
+__global__ __launch_bounds__(BLOCK) void reduce64_block_kernel(
+    const uint64_t *__restrict__ abase, uint64_t vlo, uint64_t vhi, uint64_t bsize,
     uint64_t *__restrict__ partials)
 {
     constexpr uint64_t T = (uint64_t)BLOCK * V * 2;
     constexpr int NW = BLOCK / kWave;
     __shared__ uint64_t s_part[NW];
+    const uint64_t lo = (uint64_t)blockIdx.x * bsize;
+    const uint64_t hi = lo + bsize < vhi ? lo + bsize : vhi;
     uint64_t acc = M::identity;
-    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const uint64_t vstart = t * T;
+    for (uint64_t vs = lo; vs < hi; vs += T) {
         u32x4 x[V];
-        if (vstart >= vlo && vstart + T <= vhi) {
-            load_tile_full<BLOCK, V>(reinterpret_cast<const uint32_t *>(abase), vstart * 2, x);
+        if (vs >= vlo && vs + T <= vhi) {
+            load_tile_full<BLOCK, V>(reinterpret_cast<const uint32_t *>(abase), vs * 2, x);
         } else {
-            const uint64_t q0 = vstart / 2 + threadIdx.x;
+            const uint64_t q0 = vs / 2 + threadIdx.x;
 #pragma unroll
             for (int k = 0; k < V; ++k)
                 x[k] = load2_guarded64(abase, q0 + (uint64_t)k * BLOCK, vlo, vhi, M::identity);
@@ -325,18 +330,19 @@ static hipError_t reduce64_m(const uint64_t *data, uint64_t n, const Scratch &s,
 {
     constexpr uint64_t T = (uint64_t)kRed64Block * kRed64Chunks * 2;
     const uint32_t head = head_of64(data);
-    const uint64_t ntiles = tiles_for(n, head, T);
-    auto kern = reduce64_partial_kernel<kRed64Block, kRed64Chunks, M>;
-    uint64_t grid = (uint64_t)resident_grid((const void *)kern, kRed64Block);
-    if (grid > ntiles)
-        grid = ntiles;
-    if (grid > kMaxPartials64)
-        grid = kMaxPartials64;
+    const uint64_t vhi = n + head;
+    // Blocks of at least 16384 values (128 KiB), few enough for the partials.
+    uint64_t bsize = (vhi + kMaxPartials64 - 1) / kMaxPartials64;
+    bsize = (bsize + T - 1) / T * T;
+    if (bsize < kRed64MinBlock)
+        bsize = kRed64MinBlock;
+    const uint64_t blocks = (vhi + bsize - 1) / bsize;
     uint64_t *partials = reinterpret_cast<uint64_t *>(s.body());
-    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kRed64Block), 0, stream, data - head,
-                       (uint64_t)head, n + head, ntiles, partials);
-    hipLaunchKernelGGL((reduce64_final_kernel<256, M>), dim3(1), dim3(256), 0, stream, partials,
-                       (uint32_t)grid, total_out);
+    hipLaunchKernelGGL((reduce64_block_kernel<kRed64Block, kRed64Chunks, M>),
+                       dim3((uint32_t)blocks), dim3(kRed64Block), 0, stream, data - head,
+                       (uint64_t)head, vhi, bsize, partials);
+    hipLaunchKernelGGL((reduce64_final_kernel<1024, M>), dim3(1), dim3(1024), 0, stream, partials,
+                       (uint32_t)blocks, total_out);
     return hipGetLastError();
 }
 

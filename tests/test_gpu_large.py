@@ -210,3 +210,25 @@ def test_runs_at_int32_limit():
     last = 5 * ((total - 1) // 4) + (total - 1) % 4
     assert got == [0, 3, 5, last, -1, -1]
     _free(ends, q)
+
+
+def _xor_upto(m):
+    """0 ^ 1 ^ ... ^ m."""
+    return (m, 1, m + 1, 0)[m % 4]
+
+
+@pytest.mark.parametrize("bits,n,offset", [(32, (1 << 29) + 12345, 3), (64, (1 << 28) + 999, 1)])
+def test_reduce_blocks_past_their_minimum(bits, n, offset):
+    # Past 2^29 u32 (2^28 u64) values the reduction's blocks grow beyond
+    # their 128 KiB minimum so the partials still fit: an unaligned start and
+    # a ragged end there.  Value j at index j gives closed forms.
+    dt = torch.int32 if bits == 32 else torch.int64
+    buf = torch.arange(-offset, n + 4, dtype=dt, device="cuda")
+    t = buf[offset:offset + n]
+    f = ps.reduce_op_u32 if bits == 32 else ps.reduce_op_u64
+    mask = (1 << bits) - 1
+    assert f(t, "add") == (n * (n - 1) // 2) & mask
+    assert f(t, "max") == n - 1
+    assert f(t, "min") == 0
+    assert f(t, "xor") == _xor_upto(n - 1)
+    _free(buf, t)
