@@ -547,9 +547,9 @@ def algorithmic_bytes(name, grid):
                                 "scan_blocks_pipelined_kernel", "scan_tiles_known_bases_kernel")):
         return 8 * n28 if big else None
     if "runs_owner_all_kernel" in name:
-        # 4 B per merged item (run end or entry), 4096 items per 256-thread
-        # workgroup: within 16 KiB of 4 (n + total).
-        return 64 * grid
+        # 4 B per merged item (run end or entry), 8192 items per 256-thread
+        # workgroup: within 32 KiB of 4 (n + total).
+        return 128 * grid
     if "radix1_pass_kernel" in name or "digit_scatter_kernel" in name:
         first = ", true, false>" in name
         last = ", false, true>" in name

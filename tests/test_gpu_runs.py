@@ -132,3 +132,18 @@ def test_owner_all_one_long_run_and_many_empty_runs():
     want = oracle.runs_owner_all(c)
     got = ps.runs_owner_all_u32(to_dev(ends), want.size, owner=poisoned_index(want.size))
     assert first_mismatch(to_host_i32(got), want) is None
+
+
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+def test_owner_all_writes_nothing_outside_its_range(offset):
+    # Owners go out in 16-byte chunks aligned in memory; the chunks that hold
+    # the range's first and last entries must store only inside the range.
+    c = counts_of("uniform", 70001)
+    ends, _ = oracle.runs_u32(c)
+    want = oracle.runs_owner_all(c)
+    t = want.size - 5
+    buf = torch.full((t + offset + 8,), 12345, dtype=torch.int32, device="cuda")
+    ps.runs_owner_all_u32(to_dev(ends), t, owner=buf[offset:offset + t])
+    got = to_host_i32(buf)
+    assert first_mismatch(got[offset:offset + t], want[:t]) is None
+    assert (got[:offset] == 12345).all() and (got[offset + t:] == 12345).all()
