@@ -532,8 +532,8 @@ def algorithmic_bytes(name, grid):
         ("segscan_kernel", 8 * n26 + 4 * (n26 >> 20)), ("bit_ones_kernel", 4 * n25),
         ("segscan_lanes_kernel", 8 * n26 + 4 * (n26 // 16)),
         ("segscan_long_kernel", 8 * n26 + 4 * (n26 >> 20)),
-        ("digit_hist_kernel", 4 * n25), ("reduce_partial_kernel", 4 * n28),
-        ("scan64_pipelined_kernel", 16 * n27), ("reduce64_partial_kernel", 8 * n27),
+        ("digit_hist_kernel", 4 * n25), ("reduce_block_kernel", 4 * n28),
+        ("scan64_pipelined_kernel", 16 * n27), ("reduce64_block_kernel", 8 * n27),
         ("runs_ends_kernel", 8 * (1 << 24)),
     ]
     if "segflags_kernel" in name:
