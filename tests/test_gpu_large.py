@@ -72,6 +72,19 @@ def test_scan_beyond_2p32(algo, inclusive, offset):
     _free(buf, t)
 
 
+def test_threepass_one_tile_blocks_beyond_2p32():
+    # n = 2^33 - 12345: the automatic depth gives 2^18 blocks of exactly one
+    # 32768-entry tile, which pass 3 draws from a ticket; the last is ragged.
+    n = (1 << 33) - 12345
+    buf, t = _ones(n, 0)
+    assert ps.scan_u32_ex(t, inclusive=False, algo="threepass") == n & MASK32
+
+    def expected(start, stop):
+        return torch.arange(start, stop, dtype=torch.int64, device="cuda") & MASK32
+    _check_slices(t, expected, "threepass n=2^33-12345")
+    _free(buf, t)
+
+
 @pytest.mark.parametrize("L", [1 << 20, (1 << 31) + 7])
 def test_segscan_beyond_2p32(L):
     n = (1 << 32) + 777
