@@ -402,8 +402,11 @@ __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
     if (e1 < e0)
         e1 = e0;
     const uint32_t cnt = (uint32_t)(e1 - e0);            // entries to write
-    const uint32_t h = (uint32_t)(((uintptr_t)(owner + e0) >> 2) & 3u);
-    int32_t *obase = owner + e0 - h;                     // 16-byte aligned
+    const uintptr_t first = reinterpret_cast<uintptr_t>(owner + e0);
+    const uint32_t h = (uint32_t)((first >> 2) & 3u);
+    // 16-byte aligned, at or before the first entry (rounded as an address,
+    // so no pointer is formed before the array's start).
+    int32_t *obase = reinterpret_cast<int32_t *>(first & ~(uintptr_t)15);
     constexpr int kChunksPer = (int)((kMpTile + 3) / 4 + kMpBlock - 1) / kMpBlock + 1;
     const uint32_t nchunks = (cnt + h + 3) / 4;
     auto owner_at = [&](uint32_t x) -> int32_t {         // x: offset from e0
