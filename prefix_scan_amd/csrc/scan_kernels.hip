@@ -180,6 +180,41 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict
         *total_out = carry;
 }
 
+// Cache policies of the streaming stores: non-temporal loads; stores
+// non-temporal and device-scope, so a line leaves the L2 at once instead of
+// waiting there dirty for an eviction.  (The look-back scan keeps plain
+// non-temporal stores: with its device-scope descriptor reads in flight the
+// device-scope stores were slower.)
+constexpr int kCopyLoadAux = 2;          // nt
+constexpr int kCopyStoreAux = 2 | 16;    // nt, sc1
+
+template <int BLOCK, int V>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_tile_rsrc(const uint32_t *base,
+                                                                 uint32_t t, uint64_t n)
+{
+    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
+    const uint64_t start = (uint64_t)t * T;
+    const uint64_t left = n - start;
+    const uint32_t bytes = (uint32_t)((left < T ? left : T) * 4);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(base) + start, 0, bytes,
+                                             0x00020000);
+}
+
+// A whole tile's stores, device-scope and non-temporal, at virtual start vs
+// of a 16-byte aligned base (vs a multiple of 4).
+template <int BLOCK, int V>
+__device__ __forceinline__ void store_tile_stream(uint32_t *abase, uint64_t vs,
+                                                  const u32x4 (&x)[V])
+{
+    constexpr uint32_t kBytes = (uint32_t)BLOCK * V * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(abase + vs, 0, kBytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(x[k], rs, (k * BLOCK + threadIdx.x) * 16, 0,
+                                               kCopyStoreAux);
+}
+
 // Pass 3 for blocks of many tiles: the same per-block scan, but a resident
 // grid walks the blocks round-robin and each workgroup runs a block's tiles
 // in the lockstep of the pipelined scan -- the next tile's loads issued, the
@@ -236,7 +271,7 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_pipelined_kernel(
                 w[k] = wave_incl_add(x[k].w);
             TS::template apply<INCL>(x, w, s_cell[b], carry);
             if (whole(vs))
-                store_tile_full<BLOCK, V>(abase, vs, x);
+                store_tile_stream<BLOCK, V>(abase, vs, x);
             else
                 store_tile<BLOCK, V>(abase, vs, vlo, vhi, x);
         };
@@ -324,7 +359,7 @@ __global__ __launch_bounds__(BLOCK) void scan_tiles_known_bases_kernel(
             w[k] = wave_incl_add(x[k].w);
         TS::template apply<INCL>(x, w, s_cell[b], bases[tt]);
         if ((uint64_t)tt * T + T <= n)
-            store_tile_full<BLOCK, V>(abase, (uint64_t)tt * T, x);
+            store_tile_stream<BLOCK, V>(abase, (uint64_t)tt * T, x);
         else
             store_tile<BLOCK, V>(abase, (uint64_t)tt * T, 0, n, x);
     };
@@ -377,21 +412,6 @@ __global__ __launch_bounds__(BLOCK) void scan_tiles_known_bases_kernel(
 // plain copy); a tile past the end is cut by its buffer descriptor's size,
 // which drops loads and stores beyond it.  dst may equal src.
 // ---------------------------------------------------------------------------
-constexpr int kCopyLoadAux = 2;          // nt
-constexpr int kCopyStoreAux = 2 | 16;    // nt, sc1
-
-template <int BLOCK, int V>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_tile_rsrc(const uint32_t *base,
-                                                                 uint32_t t, uint64_t n)
-{
-    constexpr uint64_t T = (uint64_t)BLOCK * V * 4;
-    const uint64_t start = (uint64_t)t * T;
-    const uint64_t left = n - start;
-    const uint32_t bytes = (uint32_t)((left < T ? left : T) * 4);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(base) + start, 0, bytes,
-                                             0x00020000);
-}
-
 template <int BLOCK, int V>
 __global__ __launch_bounds__(BLOCK) void ceiling_copy_kernel(const uint32_t *src, uint32_t *dst,
                                                              uint64_t n, uint32_t ntiles,
