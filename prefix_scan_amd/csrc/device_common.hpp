@@ -607,6 +607,28 @@ __device__ __forceinline__ void store_tile(uint32_t *abase, uint64_t vstart, uin
     }
 }
 
+// Stores that stream past the caches: non-temporal and device-scope, so a
+// line leaves the L2 at once instead of waiting there dirty for an
+// eviction.  For kernels that read no look-back descriptors: with
+// device-scope descriptor reads in flight these stores were slower than
+// plain non-temporal ones.
+constexpr int kStreamStoreAux = 2 | 16;  // nt, sc1
+
+// A whole tile's stores, device-scope and non-temporal, at virtual start vs
+// of a 16-byte aligned base (vs a multiple of 4).
+template <int BLOCK, int V>
+__device__ __forceinline__ void store_tile_stream(uint32_t *abase, uint64_t vs,
+                                                  const u32x4 (&x)[V])
+{
+    constexpr uint32_t kBytes = (uint32_t)BLOCK * V * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(abase + vs, 0, kBytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(x[k], rs, (k * BLOCK + threadIdx.x) * 16, 0,
+                                               kStreamStoreAux);
+}
+
 // u64 arrays use the same 16-byte chunks, two elements each: the virtual
 // index is v = i + head with head = (address / 8) mod 2, so virtual chunk q
 // holds u64 elements 2q and 2q + 1 (lanes x, y and z, w of the u32x4).

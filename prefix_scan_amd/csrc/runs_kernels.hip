@@ -10,7 +10,8 @@
 //  * runs_ends_kernel: the out-of-place inclusive scan of the counts on the
 //    pipelined chained-carry driver (scan_op.hpp); its last tile writes
 //    entries = max(total, 1).  8 bytes per owner.
-//  * fill_value_kernel: the slots, -1 with 16-byte stores.  4 bytes per slot.
+//  * fill_value_kernel: the slots, -1 in 16-byte streaming stores.  4 bytes
+//    per slot.
 //  * runs_index_kernel + runs_owner_kernel: owner(e, ends) for a batch of
 //    entries, a search over an index of every 32nd end, then over one
 //    block of 32 ends.
@@ -120,21 +121,32 @@ hipError_t launch_runs_ends(const uint32_t *counts, uint32_t *ends, uint64_t n, 
 // ---------------------------------------------------------------------------
 // slots: every element of a u32 array set to one value.
 // ---------------------------------------------------------------------------
+// Tiles of 256 threads x 4 chunks; a whole tile goes out as streaming stores
+// (full lines, nothing read), the tiles at the ends element by element.
+constexpr int kFillChunks = 4;
+constexpr uint64_t kFillTile = (uint64_t)256 * kFillChunks * 4;
+
 __global__ __launch_bounds__(256) void fill_value_kernel(uint32_t *vbase, uint64_t vlo,
                                                          uint64_t vhi, uint32_t value)
 {
     const u32x4 v4 = {value, value, value, value};
-    const uint64_t q_hi = (vhi + 3) / 4;
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t q = vlo / 4 + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; q < q_hi;
-         q += stride) {
-        const uint64_t v0 = q * 4;
-        if (v0 >= vlo && v0 + 4 <= vhi) {
-            store4(vbase, q, v4);
+    const uint64_t ntiles = (vhi + kFillTile - 1) / kFillTile;
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t vs = t * kFillTile;
+        if (vs >= vlo && vs + kFillTile <= vhi) {
+            u32x4 x[kFillChunks];
+#pragma unroll
+            for (int k = 0; k < kFillChunks; ++k)
+                x[k] = v4;
+            store_tile_stream<256, kFillChunks>(vbase, vs, x);
         } else {
-            for (int j = 0; j < 4; ++j)
-                if (v0 + j >= vlo && v0 + j < vhi)
-                    vbase[v0 + j] = value;
+#pragma unroll
+            for (int k = 0; k < kFillChunks; ++k) {
+                const uint64_t v0 = vs + (uint64_t)(k * 256 + threadIdx.x) * 4;
+                for (int j = 0; j < 4; ++j)
+                    if (v0 + j >= vlo && v0 + j < vhi)
+                        vbase[v0 + j] = value;
+            }
         }
     }
 }
@@ -142,8 +154,7 @@ __global__ __launch_bounds__(256) void fill_value_kernel(uint32_t *vbase, uint64
 hipError_t launch_fill_value(uint32_t *p, uint64_t n, uint32_t value, hipStream_t stream)
 {
     const uint32_t head = head_of(p);
-    const uint64_t chunks = (n + head + 3) / 4;
-    uint64_t grid = (chunks + 255) / 256;
+    uint64_t grid = (n + head + kFillTile - 1) / kFillTile;
     if (grid > 8192)
         grid = 8192;
     hipLaunchKernelGGL(fill_value_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p - head,

@@ -180,13 +180,9 @@ __global__ __launch_bounds__(BLOCK) void scan_blocks_kernel(uint32_t *__restrict
         *total_out = carry;
 }
 
-// Cache policies of the streaming stores: non-temporal loads; stores
-// non-temporal and device-scope, so a line leaves the L2 at once instead of
-// waiting there dirty for an eviction.  (The look-back scan keeps plain
-// non-temporal stores: with its device-scope descriptor reads in flight the
-// device-scope stores were slower.)
+// The streaming copy's loads are non-temporal; its stores, like the
+// three-pass rescans', are the streaming stores of device_common.hpp.
 constexpr int kCopyLoadAux = 2;          // nt
-constexpr int kCopyStoreAux = 2 | 16;    // nt, sc1
 
 template <int BLOCK, int V>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_tile_rsrc(const uint32_t *base,
@@ -198,21 +194,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_tile_rsrc(const uint32_t 
     const uint32_t bytes = (uint32_t)((left < T ? left : T) * 4);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(base) + start, 0, bytes,
                                              0x00020000);
-}
-
-// A whole tile's stores, device-scope and non-temporal, at virtual start vs
-// of a 16-byte aligned base (vs a multiple of 4).
-template <int BLOCK, int V>
-__device__ __forceinline__ void store_tile_stream(uint32_t *abase, uint64_t vs,
-                                                  const u32x4 (&x)[V])
-{
-    constexpr uint32_t kBytes = (uint32_t)BLOCK * V * 16;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(abase + vs, 0, kBytes, 0x00020000);
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-        __builtin_amdgcn_raw_buffer_store_b128(x[k], rs, (k * BLOCK + threadIdx.x) * 16, 0,
-                                               kCopyStoreAux);
 }
 
 // Pass 3 for blocks of many tiles: the same per-block scan, but a resident
@@ -464,7 +445,7 @@ __global__ __launch_bounds__(BLOCK) void ceiling_copy_kernel(const uint32_t *src
 #pragma unroll
         for (int k = 0; k < V; ++k)
             __builtin_amdgcn_raw_buffer_store_b128(x[k], r, (k * BLOCK + threadIdx.x) * 16, 0,
-                                                   kCopyStoreAux);
+                                                   kStreamStoreAux);
     };
     load(a, cur);
     // One step: draw the next tile, load it and let it land, then store the

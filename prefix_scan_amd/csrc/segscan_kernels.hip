@@ -429,7 +429,7 @@ __global__ __launch_bounds__(BLOCK) void segscan_lanes_kernel(const uint32_t *__
         }
     }
     if (whole)
-        store_tile_full<BLOCK, V>(out, vstart, x);
+        store_tile_stream<BLOCK, V>(out, vstart, x);       // no descriptors read here
     else
         store_tile<BLOCK, V>(out, vstart, 0, n, x);
 }
