@@ -420,6 +420,9 @@ __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
     int32_t *obase = reinterpret_cast<int32_t *>(first & ~(uintptr_t)15);
     constexpr int kChunksPer = (int)((kMpTile + 3) / 4 + kMpBlock - 1) / kMpBlock + 1;
     const uint32_t nchunks = (cnt + h + 3) / 4;
+    // Whole chunks go out as streaming stores (full lines; nothing read).
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(obase, 0, nchunks * 16u, 0x00020000);
     auto owner_at = [&](uint32_t x) -> int32_t {         // x: offset from e0
         const uint64_t o = i0 + s_cnt[x];
         return o < n ? (int32_t)(uint32_t)o : -1;
@@ -434,8 +437,9 @@ __global__ __launch_bounds__(kMpBlock) void runs_owner_all_kernel(
             const uint32_t x = v0 - h;
             const int32_t a = owner_at(x), b2 = owner_at(x + 1), c2 = owner_at(x + 2),
                           d2 = owner_at(x + 3);
-            reinterpret_cast<u32x4 *>(obase)[c] =
-                u32x4{(uint32_t)a, (uint32_t)b2, (uint32_t)c2, (uint32_t)d2};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{(uint32_t)a, (uint32_t)b2, (uint32_t)c2, (uint32_t)d2}, rs, c * 16u, 0,
+                kStreamStoreAux);
         } else {
 #pragma unroll
             for (uint32_t i = 0; i < 4; ++i)
