@@ -129,9 +129,9 @@ int scan_inclusive_u32(uint32_t *data, uint64_t n, uint32_t *total_host, uint32_
  *   bendlib "scan.bend source", header comment: fork depth b cuts the array
  *   into 2^b equal blocks (b lowered to log2 n when larger) and every b gives
  *   the same bits; the three passes are (1) each block's sum, (2) the
- *   exclusive scan of the sums and the total -- one lane below 2^12 sums,
- *   else this same scan at half the depth -- and (3) each block rescanned from
- *   its base, in place.
+ *   exclusive scan of the sums and the total -- here one workgroup below
+ *   2^14 sums (the page's GPU switched at 2^12), else this same scan at half
+ *   the depth -- and (3) each block rescanned from its base, in place.
  *
  * inclusive    0 exclusive, 1 inclusive.
  * algo         LIBSCAN_ALGO_*.

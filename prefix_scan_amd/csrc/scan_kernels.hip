@@ -10,7 +10,7 @@
 //    with a look-back over published aggregates in place of strict turns.
 //  * reduce_blocks_kernel + scan_blocks_kernel: the three-pass scheme of
 //    bendlib "scan.bend source" (header comment, "Pass 1", "Pass 3",
-//    "Driver"): block sums, a scan of the sums (one workgroup below 2^12
+//    "Driver"): block sums, a scan of the sums (one workgroup below 2^14
 //    sums, else the same scheme at half the depth), then each block rescanned
 //    from its base.  12 bytes per element; kept as the comparison scheme and
 //    for the fork-depth knob.  With blocks of one tile, pass 3 hands the
@@ -734,8 +734,10 @@ hipError_t launch_scan_threepass(uint32_t *data, uint64_t n, bool inclusive, uns
 
     // Pass 1: each block's sum.
     launch_reduce(data, n, blocks, bsize, sums, stream, ticket);
-    // Pass 2: the sums become their exclusive scan, and the total.
-    if (d < 12) {
+    // Pass 2: the sums become their exclusive scan, and the total: one
+    // workgroup up to 2^13 sums (at 2^13 it beats the nested scan by ~9 us;
+    // at 2^14 they tie), else the same scheme at half the depth.
+    if (d < 14) {
         launch_scan_blocks(sums, blocks, 1, blocks, nullptr, total_out, false, stream);
     } else {
         const uint64_t b2 = 1ull << (d / 2);
