@@ -62,6 +62,23 @@ struct CompactOp {
             load_tile<BLOCK, V>(fbase, (uint64_t)t * T, vlo, vhi, r.x);   // outside: flag 0
     }
 
+    // Loads and reduces a tile in one call, so the driver reads the carry's
+    // first look-back window once the tile's flags have landed (2^26,
+    // p = 0.5: 112.3 -> 110.7 us).
+    static constexpr bool kLoadLocal = true;
+    template <class R>
+    __device__ __forceinline__ void load_local(Regs &r, Cells &c, uint32_t t, R &&ready) const
+    {
+        if (whole(t)) {
+            load_tile_full<BLOCK, V>(fbase, (uint64_t)t * T, r.x);
+            ready(r.x[V - 1].x);
+        } else {
+            load_tile<BLOCK, V>(fbase, (uint64_t)t * T, vlo, vhi, r.x);
+            ready(0u);
+        }
+        local(r, c, t);
+    }
+
     // Chunk k's keep bits, scanned inside the chunk.
     __device__ static __forceinline__ u32x4 kept_scanned(uint64_t kbits, int k)
     {

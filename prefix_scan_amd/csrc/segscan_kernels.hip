@@ -502,6 +502,23 @@ struct SegLongOp {
             load_tile<BLOCK, V>(ibase, (uint64_t)t * T, vlo, vhi, r.x);
     }
 
+    // Loads and reduces a tile in one call, so the driver reads the carry's
+    // first look-back window once the tile's loads have landed (2^26 with
+    // L = 2^20: 99.5 -> 95.9 us).
+    static constexpr bool kLoadLocal = true;
+    template <class R>
+    __device__ __forceinline__ void load_local(Regs &r, Cells &c, uint32_t t, R &&ready) const
+    {
+        if (whole(t)) {
+            load_tile_full<BLOCK, V>(ibase, (uint64_t)t * T, r.x);
+            ready(r.x[V - 1].x);
+        } else {
+            load_tile<BLOCK, V>(ibase, (uint64_t)t * T, vlo, vhi, r.x);
+            ready(0u);
+        }
+        local(r, c, t);
+    }
+
     __device__ __forceinline__ void local(Regs &r, Cells &c, uint32_t t) const
     {
         uint32_t w[V];
