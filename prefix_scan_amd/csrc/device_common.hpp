@@ -348,6 +348,74 @@ __device__ __forceinline__ void wave_incl64_add2(uint64_t &a, uint64_t &b)
 }
 #undef LIBSCAN_DPP64_STEP2
 
+// Two inclusive wave scans of u64 values under unsigned max, step by step.
+// A step compares each lane with its source lane by a DPP subtract-with-
+// borrow pair (source - own; the final borrow, in VCC, says own is larger)
+// and keeps own or takes the source's halves with two DPP selects: four
+// instructions a step, against five that first move the source's halves
+// into registers.  The subtraction's result is dropped.  Lanes whose source
+// lies outside the row, or in a masked row, are disabled for all four
+// instructions and keep their value.  The two scans' steps alternate, so
+// each DPP read follows the write of its register by four instructions.
+#define LIBSCAN_MAX64_STEP(LO, HI, CTRL, RMASK)                                                    \
+    "v_sub_co_u32_dpp %4, vcc, " LO ", " LO " " CTRL " row_mask:" RMASK " bank_mask:0xf\n"       \
+    "v_subb_co_u32_dpp %4, vcc, " HI ", " HI ", vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n" \
+    "v_cndmask_b32_dpp " LO ", " LO ", " LO ", vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n"  \
+    "v_cndmask_b32_dpp " HI ", " HI ", " HI ", vcc " CTRL " row_mask:" RMASK " bank_mask:0xf\n"
+#define LIBSCAN_MAX64_STEP2(CTRL, RMASK)                                                            \
+    LIBSCAN_MAX64_STEP("%0", "%1", CTRL, RMASK)                                                    \
+    LIBSCAN_MAX64_STEP("%2", "%3", CTRL, RMASK)
+__device__ __forceinline__ void wave_incl64_max2(uint64_t &a, uint64_t &b)
+{
+    uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32);
+    uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+    uint32_t t;
+    asm("s_nop 1\n"
+        LIBSCAN_MAX64_STEP2("row_shr:1", "0xf")
+        LIBSCAN_MAX64_STEP2("row_shr:2", "0xf")
+        LIBSCAN_MAX64_STEP2("row_shr:4", "0xf")
+        LIBSCAN_MAX64_STEP2("row_shr:8", "0xf")
+        LIBSCAN_MAX64_STEP2("row_bcast:15", "0xa")
+        LIBSCAN_MAX64_STEP2("row_bcast:31", "0xc")
+        "s_nop 1\n"
+        : "+v"(alo), "+v"(ahi), "+v"(blo), "+v"(bhi), "=&v"(t)
+        :
+        : "vcc");
+    a = ((uint64_t)ahi << 32) | alo;
+    b = ((uint64_t)bhi << 32) | blo;
+}
+#undef LIBSCAN_MAX64_STEP2
+#undef LIBSCAN_MAX64_STEP
+
+// The min / max family of u64 operators as unsigned max of flipped values:
+// x ^ mask reverses the order for min (all bits), maps the signed order to
+// the unsigned one for signed max (the sign bit), and does both for signed
+// min (all bits but the sign).
+template <class Op>
+struct MaxFlip64 {
+    static constexpr bool is = false;
+};
+template <>
+struct MaxFlip64<OpMax64> {
+    static constexpr bool is = true;
+    static constexpr uint64_t mask = 0ull;
+};
+template <>
+struct MaxFlip64<OpMin64> {
+    static constexpr bool is = true;
+    static constexpr uint64_t mask = ~0ull;
+};
+template <>
+struct MaxFlip64<OpMaxS64> {
+    static constexpr bool is = true;
+    static constexpr uint64_t mask = 0x8000000000000000ull;
+};
+template <>
+struct MaxFlip64<OpMinS64> {
+    static constexpr bool is = true;
+    static constexpr uint64_t mask = 0x7FFFFFFFFFFFFFFFull;
+};
+
 template <class Op>
 __device__ __forceinline__ uint64_t wave_incl64(uint64_t x)
 {
@@ -417,10 +485,18 @@ __device__ __forceinline__ void wave_incl64_n(const uint64_t (&e)[V], uint64_t (
 #pragma unroll
         for (int k = 0; k < V; k += 2) {
             uint64_t a = e[k], b = e[k + 1];
-            if constexpr (__is_same(Op, OpAdd64))
+            if constexpr (__is_same(Op, OpAdd64)) {
                 wave_incl64_add2(a, b);
-            else
+            } else if constexpr (MaxFlip64<Op>::is) {
+                constexpr uint64_t kFlip = MaxFlip64<Op>::mask;
+                a ^= kFlip;
+                b ^= kFlip;
+                wave_incl64_max2(a, b);
+                a ^= kFlip;
+                b ^= kFlip;
+            } else {
                 wave_incl64_pair<Op>(a, b);
+            }
             w[k] = a;
             w[k + 1] = b;
         }
