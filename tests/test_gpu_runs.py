@@ -87,6 +87,26 @@ def test_owner_queries(kind):
         assert int(to_host_i32(got)[j]) == oracle.runs_owner(ends, int(q[j]))
 
 
+@pytest.mark.parametrize("kind,n", [("uniform", 100), ("sparse", 32 * 32768 - 1),
+                                    ("sparse", 32 * 32768), ("sparse", 32 * 32768 + 33),
+                                    ("sparse", 64 * 32768 + 5)])
+def test_owner_queries_around_the_search_levels(kind, n):
+    """Owner counts around the sizes where the batch search's top level (at
+    most 32768 index entries, one per 32 ends) changes its block length;
+    queries at every run end and one before it (ties included: most sparse
+    runs are empty), and at both ends of the entry range."""
+    c = counts_of(kind, n)
+    ends, _ = oracle.runs_u32(c)
+    total = int(ends[-1])
+    assert total > 0
+    every = oracle.runs_owner_all(c)
+    e = ends.astype(np.int64)
+    q = np.concatenate([e, np.maximum(e - 1, 0), [0, total - 1, total, total + 5]]).astype(np.uint32)
+    want = np.where(q < total, every[np.minimum(q, total - 1)], -1).astype(np.int32)
+    got = ps.runs_owner_u32(to_dev(ends), to_dev(q, 1), owner=poisoned_index(q.size, 2))
+    assert first_mismatch(to_host_i32(got), want) is None
+
+
 def test_owner_queries_without_runs():
     q = torch.arange(100, dtype=torch.int32, device="cuda")
     got = ps.runs_owner_u32(torch.zeros(0, dtype=torch.int32, device="cuda"), q,
